@@ -1,0 +1,201 @@
+"""Benchmark of the dense fp16 NT GEMM C = A @ B.T on one MI355X.
+
+One step = one GEMM over the workload's inputs (the whole hot path: one
+kernel launch through the C ABI).  Inputs are seeded synthetic fp16 matrices
+(workloads.py), resident in HBM before the timed region starts.
+
+Protocol (after the pages' benchmark: CUDA-event timing of 30 launches after a
+3-second cooldown; page 6, Performance and the Warning after it): W warm-up
+launches, a cooldown, then exactly K launches between two events on the
+launch stream, each launch also bracketed by its own event pair for the
+per-launch kernel duration used in the roofline.
+
+Prints ONE JSON line.  Fields beyond the common contract:
+  roofline      the GEMM kernel against the MI355X dense fp16 MFMA peak
+  cpu_baseline  the CPU oracle timed on a bounded block of the same workload
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP16_TFLOPS = 2500.0      # MI355X published dense fp16 MFMA peak
+PEAK_HBM_GBS = 8000.0          # MI355X published HBM3E bandwidth
+PAGES_H100_TFLOPS = 756.0      # the pages' best kernel at 8192^3 on H100 SXM (context)
+SOURCE = os.path.join(ROOT, "dense_fp16_gemm_amd", "csrc", "gemm_f16_nt.hip")
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for path in (SOURCE, os.path.join(ROOT, "dense_fp16_gemm_amd", "csrc", "tile_schedule.h")):
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when there is none or the kernel source has changed since."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_digest") != source_digest():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, target_s: float):
+    """The oracle, as it is, on a bounded block of the workload: the first
+    m_s rows of A and n_s rows of B at the full K.  Scaled from a short probe
+    to take about target_s seconds."""
+    import numpy as np
+
+    import oracle
+    import workloads
+
+    threads = oracle.default_threads()
+    a, b = workloads.workload_inputs(w.name)
+    ms, ns = min(w.M, 64), min(w.N, 64)
+    t0 = time.perf_counter()
+    oracle.gemm(np.ascontiguousarray(a[:ms]), np.ascontiguousarray(b[:ns]), threads=threads)
+    probe = max(time.perf_counter() - t0, 1e-3)
+    scale = max(1.0, target_s / probe)
+    # grow the block along N first, then M, keeping it within the workload
+    ns2 = int(min(w.N, ns * scale))
+    ms2 = int(min(w.M, ms * max(1.0, scale * ns / ns2)))
+    t0 = time.perf_counter()
+    oracle.gemm(np.ascontiguousarray(a[:ms2]), np.ascontiguousarray(b[:ns2]), threads=threads)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * ms2 * ns2 * w.K
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"C[0:{ms2}, 0:{ns2}] of {w.name} at K={w.K} "
+                      f"({ms2 * ns2} of {w.M * w.N} outputs), {dt:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cooldown", type=float, default=3.0)
+    ap.add_argument("--workload", default=None, help="workload name (default: the 8192^3 one)")
+    ap.add_argument("--config", type=int, default=None, help="force a kernel configuration")
+    ap.add_argument("--swizzle", type=int, default=0)
+    ap.add_argument("--grid", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
+              "the GEMM shards into independent output tiles, see the design notes.",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import dense_fp16_gemm_amd as g
+    import workloads
+
+    g.load()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    name = args.workload or workloads.HEADLINE
+    w = workloads.WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    a_np, b_np = workloads.workload_inputs(name)
+    a = torch.from_numpy(a_np).to(dev)
+    b = torch.from_numpy(b_np).to(dev)
+    c = torch.empty((w.M, w.N), dtype=torch.float16, device=dev)
+    del a_np, b_np
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    plan = g.gemm_f16_nt_plan(w.M, w.N, w.K, cus).as_dict()
+    if args.config is not None:
+        info = g.gemm_f16_nt_config_info(args.config).as_dict()
+        plan.update({k: info[k] for k in ("config_id", "block_m", "block_n", "waves", "stages",
+                                          "lds_bytes")})
+
+    stream = torch.cuda.current_stream(dev)
+
+    def launch():
+        g.gemm_nt(a, b, out=c, config=args.config, swizzle=args.swizzle, grid=args.grid,
+                  stream=stream)
+
+    for _ in range(args.warmup):
+        launch()
+    torch.cuda.synchronize()
+    if args.cooldown > 0:
+        time.sleep(args.cooldown)
+
+    # timed region: exactly `steps` launches
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    win0 = torch.cuda.Event(enable_timing=True)
+    win1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    win0.record(stream)
+    for i in range(args.steps):
+        starts[i].record(stream)
+        launch()
+        ends[i].record(stream)
+    win1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = win0.elapsed_time(win1) / args.steps
+    kernel_ms = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    kernel_avg_ms = sum(kernel_ms) / len(kernel_ms)
+
+    tflops = w.flops / (ms_per_step * 1e-3) / 1e12
+    compute_bound = w.flops / w.algorithmic_bytes > (PEAK_FP16_TFLOPS * 1e12) / (PEAK_HBM_GBS * 1e9)
+    traffic = measured_traffic(name)
+    if compute_bound:
+        achieved = w.flops / (kernel_avg_ms * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP16_TFLOPS, 4),
+                    "traffic": traffic}
+    else:
+        achieved = w.algorithmic_bytes / (kernel_avg_ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                    "traffic": traffic}
+
+    out = {
+        "metric": "TFLOP/s and % of fp16 MFMA peak, fp16 NT GEMM M=N=K=8192, 1 GPU",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(tflops / PAGES_H100_TFLOPS, 3) if name == workloads.HEADLINE else None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": name, "M": w.M, "N": w.N, "K": w.K, "inputs": w.note,
+                   "seed": w.seed, "accumulate": "f32", "plan": plan,
+                   "kernel_ms_avg": round(kernel_avg_ms, 5),
+                   "kernel_ms_min": round(kernel_ms[0], 5),
+                   "kernel_ms_max": round(kernel_ms[-1], 5),
+                   "source_digest": source_digest()},
+        "roofline": roofline,
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_seconds),
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,160 @@
+"""MI355X (gfx950) dense fp16 NT GEMM: C = A @ B.T with fp32 accumulation.
+
+Thin ctypes binding over the C ABI of ``libgemm_f16.so`` (declared in
+``include/gemm_f16_nt.h``).  Every arithmetic step runs in the library's HIP
+kernels; this module only marshals arguments.  PyTorch is used for device
+memory and streams in :func:`gemm_nt`, nothing else.  There is no fallback:
+if the library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+from .build import LIB_PATH
+
+OK, INVALID_ARG, UNSUPPORTED, LAUNCH_FAILED = 0, 1, 2, 3
+
+_lock = threading.Lock()
+_lib = None
+
+
+class GemmError(RuntimeError):
+    """A non-zero status from the library."""
+
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_int32) for name in
+                ("config_id", "block_m", "block_n", "block_k", "waves", "stages",
+                 "swizzle", "tiles_m", "tiles_n", "grid")] + \
+               [("tiles", ctypes.c_int64), ("lds_bytes", ctypes.c_int32),
+                ("xcds", ctypes.c_int32)]
+
+    def as_dict(self) -> dict:
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+def library_path() -> str:
+    return LIB_PATH
+
+
+def load():
+    """Load libgemm_f16.so (built in-tree); raise if it is not there."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; "
+                "g.build()'` (hipcc, gfx950). There is no fallback path.")
+        lib = ctypes.CDLL(LIB_PATH)
+        i64, i32, p = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
+        lib.gemm_f16_nt.argtypes = [i64, i64, i64, p, p, p, p]
+        lib.gemm_f16_nt.restype = ctypes.c_int
+        lib.gemm_f16_nt_with_config.argtypes = [i64, i64, i64, p, p, p, p, i32, i32, i32]
+        lib.gemm_f16_nt_with_config.restype = ctypes.c_int
+        lib.gemm_f16_nt_status_string.argtypes = [ctypes.c_int]
+        lib.gemm_f16_nt_status_string.restype = ctypes.c_char_p
+        lib.gemm_f16_nt_validate.argtypes = [i64, i64, i64, p, p, p]
+        lib.gemm_f16_nt_validate.restype = ctypes.c_int
+        lib.gemm_f16_nt_plan.argtypes = [i64, i64, i64, i32, ctypes.POINTER(Plan)]
+        lib.gemm_f16_nt_plan.restype = ctypes.c_int
+        lib.gemm_f16_nt_num_configs.argtypes = []
+        lib.gemm_f16_nt_num_configs.restype = ctypes.c_int
+        lib.gemm_f16_nt_config_info.argtypes = [i32, ctypes.POINTER(Plan)]
+        lib.gemm_f16_nt_config_info.restype = ctypes.c_int
+        lib.gemm_f16_nt_tile_of_slot.argtypes = [ctypes.POINTER(Plan), i64,
+                                                 ctypes.POINTER(i32), ctypes.POINTER(i32)]
+        lib.gemm_f16_nt_tile_of_slot.restype = ctypes.c_int
+        _lib = lib
+        return lib
+
+
+def status_string(status: int) -> str:
+    return load().gemm_f16_nt_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != OK:
+        raise GemmError(status, where)
+
+
+# ---- C ABI, same names -----------------------------------------------------
+def gemm_f16_nt(M: int, N: int, K: int, A: int, B: int, C: int, stream: int = 0) -> None:
+    """C = A * B^T for device pointers A [M,K], B [N,K], C [M,N] (fp16)."""
+    _check(load().gemm_f16_nt(M, N, K, A, B, C, stream), "gemm_f16_nt")
+
+
+def gemm_f16_nt_with_config(M: int, N: int, K: int, A: int, B: int, C: int, stream: int,
+                            config_id: int, swizzle: int = 0, grid: int = 0) -> None:
+    _check(load().gemm_f16_nt_with_config(M, N, K, A, B, C, stream, config_id, swizzle, grid),
+           "gemm_f16_nt_with_config")
+
+
+def gemm_f16_nt_validate(M: int, N: int, K: int, A: int, B: int, C: int) -> int:
+    return load().gemm_f16_nt_validate(M, N, K, A, B, C)
+
+
+def gemm_f16_nt_plan(M: int, N: int, K: int, num_cus: int) -> Plan:
+    plan = Plan()
+    _check(load().gemm_f16_nt_plan(M, N, K, num_cus, ctypes.byref(plan)), "gemm_f16_nt_plan")
+    return plan
+
+
+def gemm_f16_nt_num_configs() -> int:
+    return load().gemm_f16_nt_num_configs()
+
+
+def gemm_f16_nt_config_info(config_id: int) -> Plan:
+    info = Plan()
+    _check(load().gemm_f16_nt_config_info(config_id, ctypes.byref(info)),
+           "gemm_f16_nt_config_info")
+    return info
+
+
+def gemm_f16_nt_tile_of_slot(plan: Plan, slot: int) -> tuple[int, int]:
+    tm, tn = ctypes.c_int32(), ctypes.c_int32()
+    _check(load().gemm_f16_nt_tile_of_slot(ctypes.byref(plan), slot, ctypes.byref(tm),
+                                           ctypes.byref(tn)), "gemm_f16_nt_tile_of_slot")
+    return tm.value, tn.value
+
+
+# ---- torch convenience -------------------------------------------------------
+def gemm_nt(a, b, out=None, config: int | None = None, swizzle: int = 0, grid: int = 0,
+            stream=None):
+    """C = a @ b.T for fp16 CUDA(HIP) tensors a [M,K] and b [N,K].
+
+    Checks dtype, contiguity, device and shapes, then calls the C ABI on the
+    current stream (or `stream`).  Returns the fp16 [M,N] output tensor.
+    """
+    import torch
+
+    if a.dtype != torch.float16 or b.dtype != torch.float16:
+        raise TypeError("a and b must be torch.float16")
+    if a.dim() != 2 or b.dim() != 2 or a.shape[1] != b.shape[1]:
+        raise ValueError(f"shape mismatch: a{tuple(a.shape)} b{tuple(b.shape)}")
+    if not (a.is_cuda and b.is_cuda) or a.device != b.device:
+        raise ValueError("a and b must be on the same GPU")
+    if not (a.is_contiguous() and b.is_contiguous()):
+        raise ValueError("a and b must be contiguous (row-major)")
+    m, k = a.shape
+    n = b.shape[0]
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float16, device=a.device)
+    elif (out.dtype != torch.float16 or tuple(out.shape) != (m, n) or not out.is_contiguous()
+          or out.device != a.device):
+        raise ValueError("out must be a contiguous float16 [M, N] tensor on a's device")
+    s = stream if stream is not None else torch.cuda.current_stream(a.device)
+    with torch.cuda.device(a.device):
+        if config is None:
+            gemm_f16_nt(m, n, k, a.data_ptr(), b.data_ptr(), out.data_ptr(), s.cuda_stream)
+        else:
+            gemm_f16_nt_with_config(m, n, k, a.data_ptr(), b.data_ptr(), out.data_ptr(),
+                                    s.cuda_stream, config, swizzle, grid)
+    return out

@@ -1,0 +1,562 @@
+// Dense fp16 NT GEMM for MI355X (gfx950): C[M,N] = fp16_rne(A[M,K] * B[N,K]^T),
+// fp32 accumulation (Tilus tutorial "Hopper matmul": page "2. Multi-Stage
+// Software Pipelining", The Full Kernel; page "6. Register Reallocation,
+// Multicast, and a Persistent Kernel", opening paragraphs).
+//
+// One kernel template, every workgroup doing every job (the pages' V2 shape,
+// which suits CDNA's in-order waves sharing one barrier):
+//
+//  * persistent tile loop: grid = min(tiles, CUs); workgroup wg walks slots
+//    wg, wg + grid, ... through the grouped, XCD-aware order of
+//    tile_schedule.h (page 4 "Tile Rasterization", page 6 "Persistent Tile
+//    Loop");
+//  * LDS ring of STAGES K-slices (page 2 "Software Pipelining", "Multi-Stage
+//    Shared Memory"), filled by gfx950 direct-to-LDS buffer loads
+//    (buffer_load_dwordx4 ... lds: 16 bytes per lane straight into LDS, no
+//    VGPR staging).  A DMA instruction writes 64 x 16 B contiguously, so the
+//    XOR swizzle that keeps the MFMA fragment reads free of bank conflicts is
+//    applied on the global side: the lane that fills physical 16-byte chunk p
+//    of row r fetches logical chunk p ^ swz(r);
+//  * stage bookkeeping without mbarriers: "full" = s_waitcnt vmcnt(n) on the
+//    wave's own DMA queue + s_barrier; "empty" = s_waitcnt lgkmcnt(0) before
+//    that same barrier, so one barrier per K-slice serves both roles (page 3
+//    "Producer-Consumer Barriers" describe the two roles); the loop is
+//    unrolled by STAGES so stage offsets are compile-time constants (page 2
+//    "Loop Unrolling and Stage Indices");
+//  * v_mfma_f32_32x32x16_f16 with fp32 accumulators held in AGPRs; the
+//    output tile is split over a WM x WN grid of waves that share A rows and
+//    B rows through LDS (page 4 "Two Consumer Warp Groups"); fragments for
+//    the next 16-deep K step are read while the current step's MFMAs run
+//    (the lesson of the pages' V5: never let the matrix pipe drain);
+//  * epilogue: round-to-nearest-even fp32 -> fp16 (v_cvt_f16_f32 under the
+//    default MODE), masked M/N tails, 8-byte stores where alignment allows.
+//
+// Operand roles: the MFMA's first operand (rows of its 32x32 result) takes a
+// 32-row slice of the B tile and the second operand (columns) a 32-row slice
+// of the A tile, so the result block is C^T and each lane ends up holding 4
+// consecutive N columns of one M row -- ready for packed fp16 stores.
+//
+// Tails: the buffer resource of a tile starts at its first row and covers
+// exactly its valid rows, so rows beyond M (or N) read as zero; a 16-byte
+// chunk beyond K is given an offset past the resource, which also reads as
+// zero (K is a multiple of 8, so chunks never straddle K).
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "gemm_f16_nt.h"
+#include "tile_schedule.h"
+
+namespace gemm_f16 {
+
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int BK = 64;                 // K elements per LDS stage
+constexpr int ROW_BYTES = BK * 2;      // one tile row of a stage: 128 B = 8 chunks
+constexpr uint32_t OOB_OFFSET = 0x80000000u;  // past every resource: reads 0
+constexpr int64_t MAX_K = int64_t(1) << 21;   // keeps BM * K * 2 < 2^31
+constexpr int LDS_LIMIT = 160 * 1024;  // gfx950 LDS per workgroup
+constexpr int DEFAULT_XCDS = 8;        // MI355X: 8 XCDs x 32 CUs
+
+// The 3-bit XOR applied to the 16-byte chunk index of tile row r.  It depends
+// only on r mod 32, so a 32-row MFMA fragment read sees the same pattern in
+// every block.  For the 32 lanes that read rows r0..r0+31 at one logical
+// chunk, any 8 consecutive rows hit 8 distinct chunks and any 16 consecutive
+// rows hit 16 distinct (row parity, chunk) pairs, i.e. all 64 banks of a
+// 256-byte LDS line.
+__host__ __device__ constexpr int chunk_swizzle(int r) { return (r & 7) ^ ((r >> 3) & 3); }
+
+template <int BM_, int BN_, int WM_, int WN_, int STAGES_>
+struct Cfg {
+    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, STAGES = STAGES_;
+    static constexpr int WAVES = WM * WN;
+    static constexpr int THREADS = 64 * WAVES;
+    static constexpr int TM = BM / WM;           // wave tile rows (M)
+    static constexpr int TN = BN / WN;           // wave tile columns (N)
+    static constexpr int FM = TM / 32;           // 32x32 MFMA blocks per wave along M
+    static constexpr int FN = TN / 32;           // ... along N
+    static constexpr int A_BYTES = BM * ROW_BYTES;
+    static constexpr int B_BYTES = BN * ROW_BYTES;
+    static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+    static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+    static constexpr int A_LOADS = BM / 8 / WAVES;   // DMA instructions per wave per stage
+    static constexpr int B_LOADS = BN / 8 / WAVES;   // (one instruction = 8 rows x 128 B)
+    static constexpr int LOADS = A_LOADS + B_LOADS;
+    static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be whole 32x32 blocks");
+    static_assert(BM % (8 * WAVES) == 0 && BN % (8 * WAVES) == 0, "DMA rows per wave");
+    static_assert(STAGES >= 2, "need at least a double buffer");
+    static_assert(LDS_BYTES <= LDS_LIMIT, "LDS ring exceeds 160 KB");
+    static_assert((STAGES - 2) * LOADS <= 63, "vmcnt counts at most 63 loads");
+};
+
+struct Params {
+    const uint16_t *A;
+    const uint16_t *B;
+    uint16_t *C;
+    int32_t M, N, K;
+    int32_t tiles_m, tiles_n, tiles;
+    int32_t swizzle, grid, xcds;
+    int32_t c_vec;   // 1: C rows allow 8-byte stores (C 8-byte aligned, N % 4 == 0)
+};
+
+// Buffer resource (V#) for raw byte addressing of `bytes` bytes at `base`:
+// stride 0, gfx9 data-format word; offsets >= bytes read as zero.
+__device__ __forceinline__ i32x4_t make_rsrc(const void *base, uint32_t bytes)
+{
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    i32x4_t r;
+    r.x = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(a & 0xffffffffu));
+    r.y = __builtin_amdgcn_readfirstlane(static_cast<int32_t>((a >> 32) & 0xffffu));
+    r.z = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(bytes));
+    r.w = 0x00020000;
+    return r;
+}
+
+// One direct-to-LDS load: lane l copies 16 bytes from rsrc + voff into LDS
+// byte address lds + 16 * l.  M0 carries the wave-uniform LDS base; the
+// s_nop covers the M0-write -> LDS-DMA hazard, which the compiler cannot see
+// inside an asm statement.
+__device__ __forceinline__ void dma16(i32x4_t rsrc, uint32_t voff, uint32_t lds)
+{
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(rsrc), "{m0}"(lds));
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+// All of this wave's LDS reads have returned, then workgroup barrier.  The
+// "memory" clobber also stops the compiler moving LDS reads across it.
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
+}
+
+template <class CF>
+__global__ __launch_bounds__(CF::THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_f16_nt_kernel(Params p)
+{
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[CF::LDS_BYTES];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wave_m = wave / CF::WN;
+    const int wave_n = wave - wave_m * CF::WN;
+    const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(smem));
+    const uint32_t row_pitch = static_cast<uint32_t>(p.K) * 2u;   // bytes per A/B row
+    const int KT = (p.K + BK - 1) / BK;
+
+    // ---- per-lane DMA geometry ---------------------------------------------
+    // Slot i of this wave fills tile rows R = (i * WAVES + wave) * 8 .. R + 7;
+    // lane l writes physical chunk l % 8 of row R + l / 8, which must hold
+    // logical chunk (l % 8) ^ swz(R + l / 8).  Since swz(r) = (r & 7) ^
+    // ((r >> 3) & 3), that is (l % 8) ^ (l / 8) ^ ((i * WAVES + wave) & 3):
+    // a per-lane constant XOR a wave-uniform one.
+    const uint32_t dma_lane_row = static_cast<uint32_t>(lane >> 3) * row_pitch;
+    const int dma_lane_x = (lane & 7) ^ (lane >> 3);
+
+    // ---- per-lane fragment read offsets ------------------------------------
+    // Fragment lane l reads row (l % 32) of a 32-row block, logical chunk
+    // 2 * kk + l / 32 (8 consecutive k), physically XOR-swizzled.
+    const int r32 = lane & 31;
+    const int khalf = lane >> 5;
+    uint32_t frag_off[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+        frag_off[kk] = r32 * ROW_BYTES + (((2 * kk + khalf) ^ chunk_swizzle(r32)) * 16);
+    const uint32_t a_frag_base = wave_m * CF::TM * ROW_BYTES;
+    const uint32_t b_frag_base = CF::A_BYTES + wave_n * CF::TN * ROW_BYTES;
+
+    for (int32_t slot = blockIdx.x; slot < p.tiles; slot += p.grid) {
+        int32_t tile_m, tile_n;
+        grouped_tile(slot_to_linear(slot, p.grid, p.tiles, p.xcds), p.tiles_m, p.tiles_n,
+                     p.swizzle, tile_m, tile_n);
+        const int32_t m0 = tile_m * CF::BM;
+        const int32_t n0 = tile_n * CF::BN;
+        const int32_t rows_a = min(CF::BM, p.M - m0);
+        const int32_t rows_b = min(CF::BN, p.N - n0);
+        const i32x4_t rsrc_a = make_rsrc(p.A + static_cast<int64_t>(m0) * p.K,
+                                         static_cast<uint32_t>(rows_a) * row_pitch);
+        const i32x4_t rsrc_b = make_rsrc(p.B + static_cast<int64_t>(n0) * p.K,
+                                         static_cast<uint32_t>(rows_b) * row_pitch);
+
+        // Issue the DMA of K-slice `kt` into ring stage `stage`.
+        auto issue = [&](int stage, int kt) {
+            const uint32_t k0 = static_cast<uint32_t>(kt) * BK;
+            const bool full = k0 + BK <= static_cast<uint32_t>(p.K);
+            const uint32_t base = lds0 + stage * CF::STAGE_BYTES;
+#pragma unroll
+            for (int i = 0; i < CF::LOADS; ++i) {
+                const bool is_a = i < CF::A_LOADS;
+                const int slot_i = is_a ? i : i - CF::A_LOADS;
+                const int rblk = slot_i * CF::WAVES + wave;          // 8-row block index
+                const int chunk = dma_lane_x ^ (rblk & 3);
+                uint32_t v = dma_lane_row + static_cast<uint32_t>(rblk * 8) * row_pitch +
+                             chunk * 16 + k0 * 2;
+                if (!full && k0 + chunk * 8 >= static_cast<uint32_t>(p.K)) v = OOB_OFFSET;
+                dma16(is_a ? rsrc_a : rsrc_b, v,
+                      base + (is_a ? 0 : CF::A_BYTES) + rblk * 8 * ROW_BYTES);
+            }
+        };
+
+        f32x16_t acc[CF::FM][CF::FN];
+#pragma unroll
+        for (int i = 0; i < CF::FM; ++i)
+#pragma unroll
+            for (int j = 0; j < CF::FN; ++j)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+        // Prefill: K-slices 0 .. STAGES-2 (fewer when K is short).
+#pragma unroll
+        for (int s = 0; s < CF::STAGES - 1; ++s)
+            if (s < KT) issue(s, s);
+
+        int rd_stage = 0;                 // stage holding slice kt
+        int wr_stage = CF::STAGES - 1;    // stage that receives slice kt + STAGES - 1
+        for (int kt = 0; kt < KT; ++kt) {
+            // "full": this wave's DMA for slice kt has landed (slices issued
+            // after it may stay in flight) ...
+            if (kt + CF::STAGES - 2 < KT)
+                wait_vmcnt<(CF::STAGES - 2) * CF::LOADS>();
+            else
+                wait_vmcnt<0>();
+            // ... and every wave's has; "empty": every wave has finished
+            // reading wr_stage (it held slice kt - 1).
+            lds_barrier();
+            if (kt + CF::STAGES - 1 < KT) issue(wr_stage, kt + CF::STAGES - 1);
+
+            const uint32_t st = rd_stage * CF::STAGE_BYTES;
+            half8_t af[2][CF::FM], bf[2][CF::FN];
+            auto load_frags = [&](int buf, int kk) {
+#pragma unroll
+                for (int i = 0; i < CF::FM; ++i)
+                    af[buf][i] = *reinterpret_cast<const half8_t *>(
+                        smem + st + a_frag_base + i * 32 * ROW_BYTES + frag_off[kk]);
+#pragma unroll
+                for (int j = 0; j < CF::FN; ++j)
+                    bf[buf][j] = *reinterpret_cast<const half8_t *>(
+                        smem + st + b_frag_base + j * 32 * ROW_BYTES + frag_off[kk]);
+            };
+            load_frags(0, 0);
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                if (kk < 3) load_frags((kk + 1) & 1, kk + 1);
+#pragma unroll
+                for (int i = 0; i < CF::FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < CF::FN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                            bf[kk & 1][j], af[kk & 1][i], acc[i][j], 0, 0, 0);
+            }
+            // Pin the issue order for the scheduler: the first step's reads,
+            // then for each 16-deep step its MFMAs with the next step's
+            // fragment reads slotted one after each MFMA, so the reads are in
+            // flight while the matrix pipe works.
+            constexpr int kReads = CF::FM + CF::FN;
+            constexpr int kMfma = CF::FM * CF::FN;
+            constexpr int kPaired = kReads < kMfma ? kReads : kMfma;
+            __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                if (kk < 3) {
+#pragma unroll
+                    for (int t = 0; t < kPaired; ++t) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    }
+                    if (kReads > kPaired) __builtin_amdgcn_sched_group_barrier(0x100, kReads - kPaired, 0);
+                    if (kMfma > kPaired) __builtin_amdgcn_sched_group_barrier(0x008, kMfma - kPaired, 0);
+                } else {
+                    __builtin_amdgcn_sched_group_barrier(0x008, kMfma, 0);
+                }
+            }
+            rd_stage = rd_stage + 1 == CF::STAGES ? 0 : rd_stage + 1;
+            wr_stage = wr_stage + 1 == CF::STAGES ? 0 : wr_stage + 1;
+        }
+
+        // ---- epilogue: RNE to fp16, masked stores --------------------------
+        // Lane l holds, for block (i, j) and group g, C[m][n .. n+3] with
+        // m = l % 32 and n = 8 g + 4 (l / 32) inside the block.
+#pragma unroll
+        for (int i = 0; i < CF::FM; ++i) {
+            const int32_t m = m0 + wave_m * CF::TM + i * 32 + r32;
+            if (m < p.M) {
+                uint16_t *crow = p.C + static_cast<int64_t>(m) * p.N;
+#pragma unroll
+                for (int j = 0; j < CF::FN; ++j) {
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const int32_t n = n0 + wave_n * CF::TN + j * 32 + g * 8 + khalf * 4;
+                        f32x4_t v;
+                        v.x = acc[i][j][4 * g + 0];
+                        v.y = acc[i][j][4 * g + 1];
+                        v.z = acc[i][j][4 * g + 2];
+                        v.w = acc[i][j][4 * g + 3];
+                        const half4_t h = __builtin_convertvector(v, half4_t);
+                        if (p.c_vec && n + 3 < p.N) {
+                            *reinterpret_cast<half4_t *>(crow + n) = h;
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                if (n + e < p.N)
+                                    reinterpret_cast<_Float16 *>(crow)[n + e] = h[e];
+                        }
+                    }
+                }
+            }
+        }
+        // Every wave is done with the ring before the next tile's prefill.
+        lds_barrier();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Kernel table
+// ---------------------------------------------------------------------------
+struct KernelEntry {
+    const void *fn;
+    int32_t block_m, block_n, waves, stages, lds_bytes, threads;
+    int32_t default_swizzle;
+    float rel_rate;   // relative MFMA rate per tile area, for the plan cost model
+};
+
+template <class CF>
+constexpr KernelEntry entry(int swizzle, float rate)
+{
+    return KernelEntry{reinterpret_cast<const void *>(&gemm_f16_nt_kernel<CF>),
+                       CF::BM, CF::BN, CF::WAVES, CF::STAGES, CF::LDS_BYTES, CF::THREADS,
+                       swizzle, rate};
+}
+
+static const KernelEntry kKernels[] = {
+    entry<Cfg<256, 256, 2, 2, 2>>(8, 1.00f),   // 0: 4 waves of 128x128
+    entry<Cfg<256, 256, 2, 4, 2>>(8, 0.95f),   // 1: 8 waves of 128x64
+    entry<Cfg<256, 128, 2, 2, 3>>(8, 0.90f),   // 2: 4 waves of 128x64, 3 stages
+    entry<Cfg<128, 128, 2, 2, 4>>(8, 0.80f),   // 3: 4 waves of 64x64, 4 stages
+    entry<Cfg<128, 64, 2, 1, 6>>(8, 0.60f),    // 4: 2 waves of 64x64, 6 stages
+};
+constexpr int kNumKernels = sizeof(kKernels) / sizeof(kKernels[0]);
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+static bool overlaps(const void *p, int64_t pbytes, const void *q, int64_t qbytes)
+{
+    if (pbytes <= 0 || qbytes <= 0) return false;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
+    return a < b + static_cast<uintptr_t>(qbytes) && b < a + static_cast<uintptr_t>(pbytes);
+}
+
+static int validate(int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *C)
+{
+    if (M < 0 || N < 0 || K < 0) return GEMM_F16_INVALID_ARG;
+    if (M > INT32_MAX || N > INT32_MAX) return GEMM_F16_UNSUPPORTED;
+    const int64_t a_bytes = M * K * 2, b_bytes = N * K * 2, c_bytes = M * N * 2;
+    if ((a_bytes > 0 && !A) || (b_bytes > 0 && !B) || (c_bytes > 0 && !C))
+        return GEMM_F16_INVALID_ARG;
+    if (overlaps(C, c_bytes, A, a_bytes) || overlaps(C, c_bytes, B, b_bytes))
+        return GEMM_F16_INVALID_ARG;
+    if (K % 8 != 0 || K > MAX_K) return GEMM_F16_UNSUPPORTED;
+    if ((a_bytes > 0 && reinterpret_cast<uintptr_t>(A) % 16 != 0) ||
+        (b_bytes > 0 && reinterpret_cast<uintptr_t>(B) % 16 != 0))
+        return GEMM_F16_UNSUPPORTED;
+    if (c_bytes > 0 && reinterpret_cast<uintptr_t>(C) % 2 != 0) return GEMM_F16_UNSUPPORTED;
+    // the smallest tile (128 x 64) must leave the tile count within int32
+    if (cdiv(M, 128) * cdiv(N, 64) > INT32_MAX) return GEMM_F16_UNSUPPORTED;
+    return GEMM_F16_OK;
+}
+
+static void fill_info(int id, gemm_f16_nt_plan_t *out)
+{
+    const KernelEntry &e = kKernels[id];
+    *out = gemm_f16_nt_plan_t{};
+    out->config_id = id;
+    out->block_m = e.block_m;
+    out->block_n = e.block_n;
+    out->block_k = BK;
+    out->waves = e.waves;
+    out->stages = e.stages;
+    out->swizzle = e.default_swizzle;
+    out->lds_bytes = e.lds_bytes;
+    out->xcds = DEFAULT_XCDS;
+}
+
+static void make_plan(int id, int64_t M, int64_t N, int32_t num_cus, int32_t swizzle,
+                      int32_t grid, gemm_f16_nt_plan_t *out)
+{
+    fill_info(id, out);
+    out->tiles_m = static_cast<int32_t>(cdiv(M, out->block_m));
+    out->tiles_n = static_cast<int32_t>(cdiv(N, out->block_n));
+    out->tiles = static_cast<int64_t>(out->tiles_m) * out->tiles_n;
+    if (swizzle > 0) out->swizzle = swizzle;
+    if (out->swizzle > out->tiles_n) out->swizzle = out->tiles_n > 0 ? out->tiles_n : 1;
+    const int64_t cap = grid > 0 ? grid : (num_cus > 0 ? num_cus : 1);
+    out->grid = static_cast<int32_t>(out->tiles < cap ? out->tiles : cap);
+}
+
+// Cost model: rounds of the persistent grid times the time one tile takes,
+// which scales with its area over the configuration's relative MFMA rate.
+static int choose_config(int64_t M, int64_t N, int32_t num_cus)
+{
+    int best = 0;
+    double best_cost = 0.0;
+    for (int id = 0; id < kNumKernels; ++id) {
+        const KernelEntry &e = kKernels[id];
+        if (id == 1) continue;   // kept for sweeps; never better than id 0 in the model
+        const int64_t tiles = cdiv(M, e.block_m) * cdiv(N, e.block_n);
+        const int64_t rounds = cdiv(tiles, num_cus > 0 ? num_cus : 1);
+        const double cost = static_cast<double>(rounds) * e.block_m * e.block_n / e.rel_rate;
+        if (id == 0 || cost < best_cost) {
+            best = id;
+            best_cost = cost;
+        }
+    }
+    return best;
+}
+
+struct DeviceInfo {
+    std::once_flag once;
+    int32_t cus = 0;
+    hipError_t err = hipSuccess;
+};
+constexpr int kMaxDevices = 64;
+static DeviceInfo g_devices[kMaxDevices];
+
+static int current_cus(int32_t *cus)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return GEMM_F16_LAUNCH_FAILED;
+    DeviceInfo &d = g_devices[dev];
+    std::call_once(d.once, [&] {
+        int v = 0;
+        d.err = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
+        d.cus = v;
+    });
+    if (d.err != hipSuccess || d.cus <= 0) return GEMM_F16_LAUNCH_FAILED;
+    *cus = d.cus;
+    return GEMM_F16_OK;
+}
+
+static int launch(const gemm_f16_nt_plan_t &plan, int64_t M, int64_t N, int64_t K,
+                  const void *A, const void *B, void *C, hipStream_t stream)
+{
+    Params p;
+    p.A = static_cast<const uint16_t *>(A);
+    p.B = static_cast<const uint16_t *>(B);
+    p.C = static_cast<uint16_t *>(C);
+    p.M = static_cast<int32_t>(M);
+    p.N = static_cast<int32_t>(N);
+    p.K = static_cast<int32_t>(K);
+    p.tiles_m = plan.tiles_m;
+    p.tiles_n = plan.tiles_n;
+    p.tiles = static_cast<int32_t>(plan.tiles);
+    p.swizzle = plan.swizzle;
+    p.grid = plan.grid;
+    p.xcds = plan.xcds;
+    p.c_vec = (N % 4 == 0 && reinterpret_cast<uintptr_t>(C) % 8 == 0) ? 1 : 0;
+    const KernelEntry &e = kKernels[plan.config_id];
+    void *args[] = {&p};
+    hipError_t err = hipLaunchKernel(e.fn, dim3(plan.grid), dim3(e.threads), args, 0, stream);
+    if (err != hipSuccess) return GEMM_F16_LAUNCH_FAILED;
+    if (hipGetLastError() != hipSuccess) return GEMM_F16_LAUNCH_FAILED;
+    return GEMM_F16_OK;
+}
+
+static int run(int64_t M, int64_t N, int64_t K, const void *A, const void *B, void *C,
+               hipStream_t stream, int32_t config_id, int32_t swizzle, int32_t grid)
+{
+    const int v = validate(M, N, K, A, B, C);
+    if (v != GEMM_F16_OK) return v;
+    if (config_id >= kNumKernels) return GEMM_F16_INVALID_ARG;
+    if (M == 0 || N == 0) return GEMM_F16_OK;
+    int32_t cus = 0;
+    const int s = current_cus(&cus);
+    if (s != GEMM_F16_OK) return s;
+    const int id = config_id >= 0 ? config_id : choose_config(M, N, cus);
+    gemm_f16_nt_plan_t plan;
+    make_plan(id, M, N, cus, swizzle, grid, &plan);
+    return launch(plan, M, N, K, A, B, C, stream);
+}
+
+}  // namespace gemm_f16
+
+using namespace gemm_f16;
+
+extern "C" int gemm_f16_nt(int64_t M, int64_t N, int64_t K, const void *A, const void *B,
+                           void *C, hipStream_t stream)
+{
+    return run(M, N, K, A, B, C, stream, -1, 0, 0);
+}
+
+extern "C" int gemm_f16_nt_with_config(int64_t M, int64_t N, int64_t K, const void *A,
+                                       const void *B, void *C, hipStream_t stream,
+                                       int32_t config_id, int32_t swizzle, int32_t grid)
+{
+    if (config_id < 0) return GEMM_F16_INVALID_ARG;
+    return run(M, N, K, A, B, C, stream, config_id, swizzle, grid);
+}
+
+extern "C" const char *gemm_f16_nt_status_string(int status)
+{
+    switch (status) {
+    case GEMM_F16_OK: return "ok";
+    case GEMM_F16_INVALID_ARG: return "invalid argument";
+    case GEMM_F16_UNSUPPORTED: return "unsupported argument";
+    case GEMM_F16_LAUNCH_FAILED: return "HIP launch failed";
+    default: return "unknown status";
+    }
+}
+
+extern "C" int gemm_f16_nt_validate(int64_t M, int64_t N, int64_t K, const void *A,
+                                    const void *B, const void *C)
+{
+    return validate(M, N, K, A, B, C);
+}
+
+extern "C" int gemm_f16_nt_plan(int64_t M, int64_t N, int64_t K, int32_t num_cus,
+                                gemm_f16_nt_plan_t *plan)
+{
+    if (!plan || M < 0 || N < 0 || K < 0 || num_cus <= 0) return GEMM_F16_INVALID_ARG;
+    if (M > INT32_MAX || N > INT32_MAX || cdiv(M, 128) * cdiv(N, 64) > INT32_MAX)
+        return GEMM_F16_UNSUPPORTED;
+    make_plan(choose_config(M, N, num_cus), M, N, num_cus, 0, 0, plan);
+    return GEMM_F16_OK;
+}
+
+extern "C" int gemm_f16_nt_num_configs(void) { return kNumKernels; }
+
+extern "C" int gemm_f16_nt_config_info(int32_t config_id, gemm_f16_nt_plan_t *info)
+{
+    if (!info || config_id < 0 || config_id >= kNumKernels) return GEMM_F16_INVALID_ARG;
+    fill_info(config_id, info);
+    return GEMM_F16_OK;
+}
+
+extern "C" int gemm_f16_nt_tile_of_slot(const gemm_f16_nt_plan_t *plan, int64_t slot,
+                                        int32_t *tile_m, int32_t *tile_n)
+{
+    if (!plan || !tile_m || !tile_n || slot < 0 || slot >= plan->tiles || plan->grid <= 0 ||
+        plan->swizzle <= 0)
+        return GEMM_F16_INVALID_ARG;
+    int32_t tm, tn;
+    grouped_tile(slot_to_linear(static_cast<int32_t>(slot), plan->grid,
+                                static_cast<int32_t>(plan->tiles), plan->xcds),
+                 plan->tiles_m, plan->tiles_n, plan->swizzle, tm, tn);
+    *tile_m = tm;
+    *tile_n = tn;
+    return GEMM_F16_OK;
+}

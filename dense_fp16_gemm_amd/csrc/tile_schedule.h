@@ -1,0 +1,63 @@
+// Tile order of the persistent GEMM kernel, shared verbatim by the device
+// code and by the host-side entry point the CPU tests call.
+//
+// Two layers:
+//  1. Grouped rasterization (Tilus tutorial "Hopper matmul", page
+//     "4. Pipeline Abstraction and Two Consumer Warp Groups", section Tile
+//     Rasterization): the N axis of the tile grid is cut into groups of
+//     `swizzle` tile columns; inside a group, linear ids walk the group's
+//     tiles row by row (m outer, n inner); when tiles_n is not a multiple of
+//     `swizzle` the last group is narrower, so the map stays a bijection.
+//     Tiles that run together then share a few B column strips and A row
+//     strips, which is what keeps B (and A) in cache.
+//  2. XCD-aware slot order (gfx950-specific, not on the pages): the
+//     persistent kernel's workgroup `wg` handles slots wg, wg + grid, ...
+//     (page "6. Register Reallocation, Multicast, and a Persistent Kernel",
+//     Persistent Tile Loop), and the dispatcher places workgroup `wg` on
+//     XCD `wg % xcds`.  Each XCD has its own L2, so within one round of
+//     `grid` slots we hand each XCD a contiguous run of grid / xcds linear
+//     ids; the raster group then makes that run a compact block of tiles.
+//     A partial last round keeps the plain order, so the map remains a
+//     bijection on [0, tiles).
+#ifndef GEMM_F16_TILE_SCHEDULE_H
+#define GEMM_F16_TILE_SCHEDULE_H
+
+#include <stdint.h>
+
+#if defined(__HIPCC__)
+#define GEMM_F16_HD __host__ __device__
+#else
+#define GEMM_F16_HD
+#endif
+
+namespace gemm_f16 {
+
+// Linear tile id -> (tile_m, tile_n) with raster groups `swizzle` columns wide.
+GEMM_F16_HD inline void grouped_tile(int32_t linear, int32_t tiles_m, int32_t tiles_n,
+                                     int32_t swizzle, int32_t &tile_m, int32_t &tile_n)
+{
+    const int32_t per_group = tiles_m * swizzle;
+    const int32_t group = linear / per_group;
+    const int32_t in_group = linear - group * per_group;
+    const int32_t first_n = group * swizzle;
+    const int32_t rest = tiles_n - first_n;
+    const int32_t width = rest < swizzle ? rest : swizzle;
+    tile_m = in_group / width;
+    tile_n = first_n + (in_group - tile_m * width);
+}
+
+// Persistent slot (round * grid + wg) -> linear tile id, XCD-contiguous.
+GEMM_F16_HD inline int32_t slot_to_linear(int32_t slot, int32_t grid, int32_t tiles,
+                                          int32_t xcds)
+{
+    const int32_t round = slot / grid;
+    const int32_t wg = slot - round * grid;
+    const int32_t base = round * grid;
+    if (xcds <= 1 || grid % xcds != 0 || base + grid > tiles) return slot;
+    const int32_t per_xcd = grid / xcds;
+    return base + (wg % xcds) * per_xcd + wg / xcds;
+}
+
+}  // namespace gemm_f16
+
+#endif  // GEMM_F16_TILE_SCHEDULE_H

@@ -1,0 +1,137 @@
+/*
+ * gemm_f16_nt.h -- C ABI of the MI355X (gfx950) dense fp16 NT GEMM library
+ * (libgemm_f16.so).
+ *
+ * The operation (Tilus tutorial "Hopper matmul", page "2. Multi-Stage
+ * Software Pipelining", The Full Kernel; page "6. Register Reallocation,
+ * Multicast, and a Persistent Kernel", opening paragraphs):
+ *
+ *     C[i][j] = fp16_rne( sum_k A[i][k] * B[j][k] )      (accumulated in fp32)
+ *
+ *   A  fp16 [M, K] row-major (leading dimension K)
+ *   B  fp16 [N, K] row-major (leading dimension K); the product uses B^T
+ *   C  fp16 [M, N] row-major (leading dimension N)
+ *
+ * The pages' kernels take (m_size, n_size, k_size, a_ptr, b_ptr, c_ptr): dense
+ * matrices, no leading-dimension, alpha or beta arguments.  This interface
+ * keeps that and adds the HIP stream to enqueue on.  fp16 data travel as raw
+ * 16-bit IEEE binary16 storage.  The fp32 accumulator is rounded once, to
+ * nearest with ties to even; results beyond the fp16 range become +-inf and
+ * fp16 subnormals are kept.  C is write-only (beta = 0): it is never read.
+ *
+ * Threading: every entry point may be called from any host thread.  The only
+ * global state is a lazily built, mutex-protected cache of per-device
+ * properties (compute-unit count).
+ */
+#ifndef GEMM_F16_NT_H
+#define GEMM_F16_NT_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+enum {
+    GEMM_F16_OK = 0,
+    /* a dimension < 0; a NULL pointer for a matrix with elements; C
+     * overlapping A or B; an unknown configuration id */
+    GEMM_F16_INVALID_ARG = 1,
+    /* valid but outside what the kernels handle: K not a multiple of 8, A or B
+     * not 16-byte aligned, C not 2-byte aligned, K > 2^21, or more than
+     * 2^31 - 1 output tiles */
+    GEMM_F16_UNSUPPORTED = 2,
+    /* the HIP runtime reported an error when launching (hipGetLastError) or
+     * when querying the current device */
+    GEMM_F16_LAUNCH_FAILED = 3
+};
+
+/*
+ * C = A * B^T on `stream` (0 = the null stream), on the current HIP device.
+ *
+ * A, B and C are device pointers owned by the caller; they must stay valid
+ * until the enqueued work has finished.  The library allocates nothing and
+ * uses no workspace.  The call returns once the kernel is enqueued; a fault
+ * inside the kernel surfaces at the caller's next synchronisation.
+ *
+ * M = 0 or N = 0: nothing to compute, returns GEMM_F16_OK without a launch.
+ * K = 0: C is filled with +0 (the empty sum).
+ * Results are deterministic: no atomics, and each element's K order depends
+ * only on K, never on the element's position or on the launch shape.
+ */
+int gemm_f16_nt(int64_t M, int64_t N, int64_t K,
+                const void *A, const void *B, void *C,
+                hipStream_t stream);
+
+/* A static, human-readable name for a status code. */
+const char *gemm_f16_nt_status_string(int status);
+
+/*
+ * Argument check used by every GEMM entry point; pure host function, touches
+ * no device and dereferences nothing.  Returns a status code.
+ */
+int gemm_f16_nt_validate(int64_t M, int64_t N, int64_t K,
+                         const void *A, const void *B, const void *C);
+
+/*
+ * The launch plan the library would use for (M, N, K) on a device with
+ * `num_cus` compute units.  Pure host function (no device access): used by
+ * tests and by the benchmark to report what runs.
+ */
+typedef struct {
+    int32_t config_id;   /* index into the compiled kernel table           */
+    int32_t block_m;     /* output tile rows (M)                           */
+    int32_t block_n;     /* output tile columns (N)                        */
+    int32_t block_k;     /* K depth of one LDS stage                        */
+    int32_t waves;       /* 64-lane wavefronts per workgroup               */
+    int32_t stages;      /* LDS ring depth                                 */
+    int32_t swizzle;     /* raster group width in N tiles (1 = plain rows) */
+    int32_t tiles_m;     /* ceil(M / block_m)                              */
+    int32_t tiles_n;     /* ceil(N / block_n)                              */
+    int32_t grid;        /* persistent workgroups launched                 */
+    int64_t tiles;       /* tiles_m * tiles_n                              */
+    int32_t lds_bytes;   /* LDS used by one workgroup                      */
+    int32_t xcds;        /* XCD count the tile order is arranged for       */
+} gemm_f16_nt_plan_t;
+
+int gemm_f16_nt_plan(int64_t M, int64_t N, int64_t K, int32_t num_cus,
+                     gemm_f16_nt_plan_t *plan);
+
+/* Number of kernel configurations compiled into the library, and the static
+ * description of configuration `config_id` (tiles_m, tiles_n, tiles and grid
+ * are left 0).  Pure host functions. */
+int gemm_f16_nt_num_configs(void);
+int gemm_f16_nt_config_info(int32_t config_id, gemm_f16_nt_plan_t *info);
+
+/*
+ * gemm_f16_nt with an explicit kernel configuration, raster group width and
+ * persistent grid size (grid <= 0: one workgroup per compute unit, capped by
+ * the tile count; swizzle <= 0: the configuration's default).  Same
+ * semantics, ownership and status codes as gemm_f16_nt; the result is
+ * identical for every configuration, swizzle and grid, because the K order of
+ * each element does not depend on them.  For tests and tuning sweeps.
+ */
+int gemm_f16_nt_with_config(int64_t M, int64_t N, int64_t K,
+                            const void *A, const void *B, void *C,
+                            hipStream_t stream, int32_t config_id,
+                            int32_t swizzle, int32_t grid);
+
+/*
+ * The tile order the kernel walks (Tilus tutorial "Hopper matmul", page
+ * "4. Pipeline Abstraction and Two Consumer Warp Groups", Tile
+ * Rasterization; page "6. ...", Persistent Tile Loop), exposed so that host
+ * tests run the very same function the device runs.  Pure host function.
+ * `slot` = round * grid + workgroup.  Writes the output tile (tile_m, tile_n)
+ * that this slot computes; returns GEMM_F16_INVALID_ARG when slot is out of
+ * [0, plan->tiles).
+ */
+int gemm_f16_nt_tile_of_slot(const gemm_f16_nt_plan_t *plan, int64_t slot,
+                             int32_t *tile_m, int32_t *tile_n);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMM_F16_NT_H */

@@ -1,0 +1,194 @@
+"""Host-side tests of libgemm_f16.so: no GPU needed, no compute calls.
+
+* every function declared in include/gemm_f16_nt.h is exported;
+* argument validation and status codes (pure host function);
+* the launch planner and the tile order (the very functions the kernel
+  runs, compiled for the host), pinned to the pages' raster and wave figures.
+"""
+import ctypes
+import json
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gemm_f16_nt.h")
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.fixture(scope="module")
+def g():
+    import dense_fp16_gemm_amd as lib
+
+    lib.load()
+    return lib
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gemm_f16_nt\w*)\s*\(", text)))
+
+
+def test_header_symbols_exported(g):
+    names = declared_functions()
+    assert "gemm_f16_nt" in names and "gemm_f16_nt_status_string" in names
+    lib = ctypes.CDLL(g.library_path())
+    for name in names:
+        assert hasattr(lib, name), f"{name} declared but not exported"
+
+
+def test_status_strings(g):
+    assert g.status_string(0) == "ok"
+    for s in (1, 2, 3):
+        assert g.status_string(s) not in ("ok", "unknown status")
+    assert g.status_string(99) == "unknown status"
+
+
+A0, B0, C0 = 0x10000, 0x20000000, 0x40000000   # fake, well-separated, aligned addresses
+
+
+@pytest.mark.parametrize("args,status", [
+    ((64, 64, 64, A0, B0, C0), 0),
+    ((-1, 64, 64, A0, B0, C0), 1),
+    ((64, -1, 64, A0, B0, C0), 1),
+    ((64, 64, -8, A0, B0, C0), 1),
+    ((64, 64, 64, 0, B0, C0), 1),              # NULL A with elements
+    ((64, 64, 64, A0, 0, C0), 1),
+    ((64, 64, 64, A0, B0, 0), 1),
+    ((0, 64, 64, 0, B0, 0), 0),                # empty A and C: NULL allowed
+    ((64, 64, 0, 0, 0, C0), 0),                # K = 0: A and B empty
+    ((64, 64, 64, A0, B0, A0 + 100), 1),       # C overlaps A
+    ((64, 64, 64, A0, B0, B0 + 8192 - 2), 1),  # C overlaps the end of B
+    ((64, 64, 64, A0, B0, B0 + 8192), 0),      # C right after B
+    ((64, 64, 60, A0, B0, C0), 2),             # K % 8 != 0
+    ((64, 64, 64, A0 + 8, B0, C0), 2),         # A not 16-byte aligned
+    ((64, 64, 64, A0, B0 + 2, C0), 2),
+    ((64, 64, 64, A0, B0, C0 + 1), 2),         # C not 2-byte aligned
+    ((64, 64, 64, A0, B0, C0 + 2), 0),         # C 2-byte aligned is fine
+    ((8, 8, (1 << 21) + 8, A0, B0 + (1 << 40), C0 + (1 << 41)), 2),   # K too large
+    ((1 << 31, 8, 8, A0, B0 + (1 << 40), C0 + (1 << 41)), 2),         # M beyond int32
+])
+def test_validate(g, args, status):
+    assert g.gemm_f16_nt_validate(*args) == status
+
+
+def test_config_table(g):
+    n = g.gemm_f16_nt_num_configs()
+    assert n >= 1
+    for cid in range(n):
+        info = g.gemm_f16_nt_config_info(cid)
+        assert info.config_id == cid
+        assert info.block_k == 64
+        # the LDS ring: stages * (BM + BN) * BK * 2 bytes within 160 KB
+        assert info.lds_bytes == info.stages * (info.block_m + info.block_n) * 64 * 2
+        assert info.lds_bytes <= 160 * 1024
+        assert info.block_m % 32 == 0 and info.block_n % 32 == 0
+    with pytest.raises(g.GemmError):
+        g.gemm_f16_nt_config_info(n)
+
+
+@pytest.mark.parametrize("shape", [(256, 256, 256), (4096, 4096, 4096), (8192, 8192, 8192),
+                                   (4999, 7001, 4160), (128, 16384, 16384), (1, 1, 8)])
+def test_plan_basics(g, shape):
+    m, n, k = shape
+    p = g.gemm_f16_nt_plan(m, n, k, 256)
+    assert p.tiles_m == -(-m // p.block_m) and p.tiles_n == -(-n // p.block_n)
+    assert p.tiles == p.tiles_m * p.tiles_n
+    assert 1 <= p.grid <= min(256, p.tiles)
+    assert 1 <= p.swizzle <= max(1, p.tiles_n)
+
+
+def test_plan_headline_and_skinny(g):
+    p = g.gemm_f16_nt_plan(8192, 8192, 8192, 256)
+    assert (p.block_m, p.block_n) == (256, 256)
+    assert p.tiles == 1024 and p.grid == 256          # exactly four full rounds
+    s = g.gemm_f16_nt_plan(128, 16384, 16384, 256)
+    assert s.block_m == 128 and s.tiles >= 256        # M = 128 must still fill the chip
+
+
+def _order(g, plan):
+    return [g.gemm_f16_nt_tile_of_slot(plan, s) for s in range(plan.tiles)]
+
+
+@pytest.mark.parametrize("mn", [(8, 8), (32, 32), (20, 28), (5, 7), (1, 64), (64, 1), (3, 3)])
+@pytest.mark.parametrize("swizzle", [1, 2, 3, 4, 8])
+@pytest.mark.parametrize("grid", [1, 7, 8, 16, 256])
+def test_tile_order_is_a_bijection(g, mn, swizzle, grid):
+    tm, tn = mn
+    plan = g.gemm_f16_nt_plan(tm * 256, tn * 256, 64, 256)
+    plan.tiles_m, plan.tiles_n, plan.tiles = tm, tn, tm * tn
+    plan.swizzle = min(swizzle, tn)
+    plan.grid = min(grid, plan.tiles)
+    order = _order(g, plan)
+    assert sorted(order) == [(i, j) for i in range(tm) for j in range(tn)]
+
+
+def test_tile_of_slot_rejects_out_of_range(g):
+    plan = g.gemm_f16_nt_plan(512, 512, 64, 256)
+    with pytest.raises(g.GemmError):
+        g.gemm_f16_nt_tile_of_slot(plan, plan.tiles)
+    with pytest.raises(g.GemmError):
+        g.gemm_f16_nt_tile_of_slot(plan, -1)
+
+
+def test_raster_working_set_matches_pages(g):
+    """Page 4, Tile Rasterization: on an 8x8 tile grid a wave of 16 blocks
+    touches 10 strips in the plain grid (M fastest) and 8 in 4x4 groups."""
+    fig = json.load(open(os.path.join(GOLDEN, "raster_and_waves.json")))["raster_working_set"]
+    tm, tn, active = fig["grid_m_tiles"], fig["grid_n_tiles"], fig["active_blocks"]
+    plan = g.gemm_f16_nt_plan(tm * 256, tn * 256, 64, 256)
+    plan.tiles_m, plan.tiles_n, plan.tiles = tm, tn, tm * tn
+    plan.grid, plan.xcds = active, 1
+    plan.swizzle = 4
+    first = [g.gemm_f16_nt_tile_of_slot(plan, s) for s in range(active)]
+    strips = len({m for m, _ in first}) + len({n for _, n in first})
+    assert strips == fig["strips_grouped_swizzle_4"]
+    # swizzle 1 is the pages' plain grid, M fastest: 8 A strips + 2 B strips
+    plan.swizzle = 1
+    plain = [g.gemm_f16_nt_tile_of_slot(plan, s) for s in range(active)]
+    assert plain == [(s % tm, s // tm) for s in range(active)]
+    strips = len({m for m, _ in plain}) + len({n for _, n in plain})
+    assert strips == fig["strips_plain_grid_m_fastest"]
+
+
+def test_raster_remainder_group(g):
+    """tiles_n not a multiple of the group width: the last group is narrower
+    (page 4, Tile Rasterization) and every tile still appears once."""
+    plan = g.gemm_f16_nt_plan(4999, 7001, 4160, 256)
+    plan.tiles_m, plan.tiles_n, plan.tiles = 20, 28, 560    # 256 x 256 tiles of the ragged shape
+    plan.grid, plan.xcds, plan.swizzle = 1, 1, 8            # 28 = 3 * 8 + 4
+    order = _order(g, plan)
+    last_group = order[3 * 20 * 8:]
+    assert {n for _, n in last_group} == {24, 25, 26, 27}
+    assert sorted(order) == [(i, j) for i in range(20) for j in range(28)]
+
+
+def test_xcd_order_gives_each_xcd_a_compact_block(g):
+    """8192^3 at 256x256: each XCD's 32 workgroups of a round get 32
+    consecutive linear ids, i.e. one compact 4 x 8 block of tiles."""
+    plan = g.gemm_f16_nt_plan(8192, 8192, 8192, 256)
+    assert plan.xcds == 8 and plan.grid == 256
+    for rnd in range(4):
+        for xcd in range(8):
+            wgs = [w for w in range(256) if w % 8 == xcd]
+            tiles = [g.gemm_f16_nt_tile_of_slot(plan, rnd * 256 + w) for w in wgs]
+            ms = {m for m, _ in tiles}
+            ns = {n for _, n in tiles}
+            assert len(ms) * len(ns) == 32 and len(ms) + len(ns) <= 12
+
+
+def test_wave_quantization_figure(g):
+    """Page 6, Performance: 128 x 320 tiles over 8192^2 give 1664 tiles, 12.6
+    rounds on 132 processors.  The same count rule (ceil per axis) applies
+    to our plans; and 256x256 on 256 CUs is exactly 4 rounds."""
+    fig = json.load(open(os.path.join(GOLDEN, "raster_and_waves.json")))["wave_quantization"]
+    tiles = -(-fig["M"] // fig["block_m"]) * -(-fig["N"] // fig["block_n"])
+    assert tiles == fig["tiles"]
+    assert round(tiles / fig["processors"], 1) == fig["rounds_one_decimal"]
+    rounds = round(tiles / fig["processors"], 1)            # 12.6, as printed
+    assert round((1 - (rounds - int(rounds))) * 100) == fig["idle_fraction_last_round_percent"]
+    p = g.gemm_f16_nt_plan(8192, 8192, 8192, 256)
+    assert p.tiles % p.grid == 0 and p.tiles // p.grid == 4

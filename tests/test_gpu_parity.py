@@ -1,0 +1,298 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+All inputs are seeded and synthetic (workloads.py).  Non-integer inputs are
+compared element by element within |C - C_ref| <= 2 ulp16(C_ref) + 1e-3;
+integer inputs, identity/permutation B, all-ones, scaling and the closed-form
+probes must be bit-exact.  Shapes span several tiles with ragged tails; the
+five workload shapes run at full size in the launch configuration the
+benchmark times, checked on sampled elements (whole boundary rows/columns
+plus random positions) and through size-independent properties.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import workloads
+from parity import assert_bit_exact, assert_within_tolerance, tolerance_report
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def g():
+    import torch
+
+    import dense_fp16_gemm_amd as lib
+
+    lib.load()
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return lib
+
+
+def _say(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def run_gpu(g, a, b, config=None, swizzle=0, grid=0):
+    import torch
+
+    _say(f"  gpu gemm {a.shape[0]}x{b.shape[0]}x{a.shape[1]} config={config} "
+         f"swizzle={swizzle} grid={grid}")
+    dev = torch.device("cuda:0")
+    ta = torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    tb = torch.from_numpy(np.ascontiguousarray(b)).to(dev)
+    # poison C so that an element the kernel never writes cannot pass
+    out = torch.full((a.shape[0], b.shape[0]), float("nan"), dtype=torch.float16, device=dev)
+    g.gemm_nt(ta, tb, out=out, config=config, swizzle=swizzle, grid=grid)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def num_configs(g):
+    return g.gemm_f16_nt_num_configs()
+
+
+# ---------------------------------------------------------------------------
+# small and medium shapes against the full oracle
+# ---------------------------------------------------------------------------
+SHAPES = [
+    (256, 256, 256),      # one 256x256 tile
+    (300, 260, 200),      # ragged M/N/K, two tiles each way
+    (513, 385, 136),      # three tiles of 256 along M, K tail of 8
+    (1, 1, 8),            # degenerate
+    (33, 31, 24),         # smaller than one MFMA block
+    (640, 96, 1000),      # K tail of 40, tall-skinny
+    (96, 700, 72),        # N tail, K = one full slice + 8
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+def test_parity_default_plan(g, oracle_mod, shape):
+    m, n, k = shape
+    a, b = workloads.make_inputs(m, n, k, "uniform", 1.0 / np.sqrt(k), seed=m * 7 + n + k)
+    got = run_gpu(g, a, b)
+    ref = oracle_mod.gemm(a, b)
+    assert_within_tolerance(got, ref, f"{shape}")
+
+
+@pytest.mark.parametrize("shape", [(300, 260, 200), (513, 385, 136), (33, 31, 24),
+                                   (129, 65, 520)])
+def test_parity_every_config(g, oracle_mod, shape):
+    """Every compiled configuration, including ones the planner does not pick
+    for this shape; all must agree with the oracle and be bit-identical to
+    each other (the K order of an element never depends on the tiling)."""
+    m, n, k = shape
+    a, b = workloads.make_inputs(m, n, k, "normal", 1.0 / np.sqrt(k), seed=m + 3 * n + k)
+    ref = oracle_mod.gemm(a, b)
+    first = None
+    for cid in range(num_configs(g)):
+        got = run_gpu(g, a, b, config=cid)
+        assert_within_tolerance(got, ref, f"{shape} config {cid}")
+        if first is None:
+            first = got
+        else:
+            assert_bit_exact(got, first, f"{shape} config {cid} vs config 0")
+
+
+@pytest.mark.parametrize("cid", [0, 2, 3, 4])
+@pytest.mark.parametrize("k", [8, 24, 64, 72, 128, 136, 192, 200, 256, 264])
+def test_short_and_ragged_k(g, oracle_mod, cid, k):
+    """K with fewer slices than stages, exactly the stages, one more, and
+    tails of 8..56 beyond a whole slice."""
+    a, b = workloads.make_inputs(130, 70, k, "uniform", 1.0, seed=k)
+    got = run_gpu(g, a, b, config=cid)
+    assert_within_tolerance(got, oracle_mod.gemm(a, b), f"k={k} config {cid}")
+
+
+@pytest.mark.parametrize("cid", [0, 3, 4])
+def test_edge_m_n(g, oracle_mod, cid):
+    info = g.gemm_f16_nt_config_info(cid)
+    bm, bn = info.block_m, info.block_n
+    for m in (1, 31, 32, 33, bm - 1, bm + 1):
+        for n in (1, 33, bn - 1, bn + 1):
+            a, b = workloads.make_inputs(m, n, 72, "normal", 0.1, seed=m * 1000 + n)
+            got = run_gpu(g, a, b, config=cid)
+            assert_within_tolerance(got, oracle_mod.gemm(a, b), f"{m}x{n}x72 config {cid}")
+
+
+def test_k_zero_writes_positive_zero(g):
+    a = np.zeros((70, 0), np.float16)
+    b = np.zeros((90, 0), np.float16)
+    got = run_gpu(g, a, b)
+    assert np.all(got.view(np.uint16) == 0)
+
+
+def test_m_or_n_zero_is_a_no_op(g):
+    import torch
+
+    z = torch.zeros((0, 64), dtype=torch.float16, device="cuda:0")
+    b = torch.zeros((16, 64), dtype=torch.float16, device="cuda:0")
+    assert tuple(g.gemm_nt(z, b).shape) == (0, 16)
+    assert tuple(g.gemm_nt(b, z).shape) == (16, 0)
+
+
+# ---------------------------------------------------------------------------
+# bit-exact cases
+# ---------------------------------------------------------------------------
+def test_integer_inputs_bit_exact(g, oracle_mod):
+    a, b = workloads.make_inputs(700, 500, 1032, "int2", 1.0, seed=31)
+    got = run_gpu(g, a, b)
+    assert_bit_exact(got, oracle_mod.gemm(a, b), "int2 700x500x1032")
+
+
+def test_identity_and_permutation_b(g):
+    rng = np.random.default_rng(2)
+    a, _ = workloads.make_inputs(300, 1, 264, "normal", 1.0, seed=5)
+    eye = np.eye(264, dtype=np.float16)
+    assert_bit_exact(run_gpu(g, a, eye), a, "B = I")
+    perm = rng.permutation(264)
+    bp = np.zeros((264, 264), np.float16)
+    bp[np.arange(264), perm] = 1.0
+    assert_bit_exact(run_gpu(g, a, bp), a[:, perm], "B = permutation")
+
+
+@pytest.mark.parametrize("k,expect", [(256, 256.0), (4096, 4096.0), (4160, 4160.0),
+                                      (8192, 8192.0), (2056, 2056.0), (5000, 5000.0)])
+def test_all_ones(g, k, expect):
+    a = np.ones((260, k), np.float16)
+    b = np.ones((70, k), np.float16)
+    got = run_gpu(g, a, b).astype(np.float64)
+    assert np.all(got == expect)
+
+
+def test_rne_tie_probes(g):
+    # K padded to 8 with zeros; sums 1 + 3*2^-11 (tie -> 1 + 2^-9) and
+    # 1 + 0.75*2^-10 (-> 1 + 2^-10).  A truncating convert gives 1 + 2^-10 and 1.
+    a = np.zeros((2, 8), np.float16)
+    a[0, :2] = [1.0, 3 * 2.0 ** -11]
+    a[1, :2] = [1.0, 0.75 * 2.0 ** -10]
+    b = np.zeros((1, 8), np.float16)
+    b[0, :2] = 1.0
+    got = run_gpu(g, a, b).astype(np.float64).ravel()
+    assert got[0] == 1 + 2.0 ** -9
+    assert got[1] == 1 + 2.0 ** -10
+
+
+def test_overflow_probe(g):
+    a = np.full((3, 256), 16.0, np.float16)
+    got = run_gpu(g, a, a).astype(np.float64)
+    assert np.all(np.isposinf(got))
+    a2 = np.zeros((3, 256), np.float16)
+    a2[:, :255] = 16.0
+    got2 = run_gpu(g, a2, a2).astype(np.float64)
+    assert np.all(got2 == 65280.0)
+
+
+def test_subnormal_probe(g):
+    j = np.arange(0, 1024, dtype=np.float64)          # 0 and every subnormal j * 2^-24
+    a = (j * 2.0 ** -24).astype(np.float16).reshape(32, 32)
+    assert np.all(a.view(np.uint16) < 0x0400)
+    eye = np.zeros((32, 32), np.float16)
+    eye[np.arange(32), np.arange(32)] = 1.0
+    assert_bit_exact(run_gpu(g, a, eye), a, "subnormal A, B = I")
+
+
+def test_power_of_two_scaling_bit_exact(g):
+    a, b = workloads.make_inputs(300, 270, 520, "uniform", 1.0 / 16, seed=41)
+    c = run_gpu(g, a, b).astype(np.float64)
+    c4 = run_gpu(g, (a.astype(np.float64) * 4).astype(np.float16), b).astype(np.float64)
+    normal = (np.abs(c) >= 2.0 ** -14) & (np.abs(c) * 4 <= 65504)
+    assert normal.mean() > 0.9
+    assert np.array_equal(c4[normal], 4 * c[normal])
+
+
+def test_swap_invariant_integer(g):
+    a, b = workloads.make_inputs(333, 290, 264, "int2", 1.0, seed=43)
+    assert_bit_exact(run_gpu(g, b, a), run_gpu(g, a, b).T, "swap")
+
+
+def test_determinism_and_launch_shape_independence(g):
+    a, b = workloads.make_inputs(1100, 900, 1000, "normal", 0.03, seed=47)
+    first = run_gpu(g, a, b)
+    for _ in range(3):
+        assert_bit_exact(run_gpu(g, a, b), first, "rerun")
+    for swz in (1, 3, 5):
+        assert_bit_exact(run_gpu(g, a, b, config=0, swizzle=swz), first, f"swizzle {swz}")
+    for grid in (1, 7, 64):
+        assert_bit_exact(run_gpu(g, a, b, config=0, grid=grid), first, f"grid {grid}")
+
+
+def test_page_mae_statistic(g):
+    """K = 8192 with unit-variance outputs: the mean |error| against the exact
+    sum must sit at the pages' fp32-accumulation figure, 0.00014 (page 6,
+    note in "Shared-Memory Epilogue"), not near the fp16-accumulation 0.0023."""
+    import json
+    import os
+
+    with open(os.path.join(os.path.dirname(__file__), "golden", "page_accuracy_k8192.json")) as f:
+        fig = json.load(f)
+    rng = np.random.default_rng(23)
+    k = fig["K"]
+    a = rng.standard_normal((256, k)).astype(np.float16)
+    b = (rng.standard_normal((256, k)) / np.sqrt(k)).astype(np.float16)
+    import oracle
+
+    ref, exact = oracle.gemm(a, b, return_sum=True)
+    got = run_gpu(g, a, b)
+    ok, stats = tolerance_report(got, ref, exact_sum=exact)
+    assert ok, stats
+    assert 0.000135 <= stats["mae_vs_exact"] <= 0.000145, stats
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads, in the launch configuration the benchmark times
+# ---------------------------------------------------------------------------
+def _sample_positions(m, n, rng, count=4096):
+    rows = [rng.integers(0, m, count)]
+    cols = [rng.integers(0, n, count)]
+    # whole last row and column (the tails) and whole first row
+    for r in {0, m - 1}:
+        rows.append(np.full(n, r))
+        cols.append(np.arange(n))
+    rows.append(np.arange(m))
+    cols.append(np.full(m, n - 1))
+    return np.concatenate(rows), np.concatenate(cols)
+
+
+@pytest.mark.parametrize("name", list(workloads.WORKLOADS))
+def test_full_size_workload(g, oracle_mod, name):
+    w = workloads.WORKLOADS[name]
+    _say(f"  workload {name}: {w.M}x{w.N}x{w.K} {w.dist} seed={w.seed}")
+    a, b = workloads.workload_inputs(name)
+    got = run_gpu(g, a, b)
+    assert not np.isnan(got).any(), "unwritten (NaN-poisoned) output elements"
+    rng = np.random.default_rng(w.seed)
+    r, c = _sample_positions(w.M, w.N, rng)
+    ref = oracle_mod.gemm_sampled(a, b, r, c)
+    if w.dist == "int2":
+        assert_bit_exact(got[r, c], ref, name)
+    else:
+        assert_within_tolerance(got[r, c], ref, name)
+
+
+def test_tail_equals_padded_interior(g):
+    """Ragged 4999 x 7001 x 4160: the same inputs zero-padded to whole tiles
+    give bit-identical values on the original rows and columns, since each
+    element's K order does not depend on its position."""
+    a, b = workloads.workload_inputs("ragged4999x7001x4160")
+    got = run_gpu(g, a, b)
+    ap = np.zeros((5120, 4160), np.float16)
+    ap[:4999] = a
+    bp = np.zeros((7168, 4160), np.float16)
+    bp[:7001] = b
+    padded = run_gpu(g, ap, bp)
+    assert_bit_exact(got, padded[:4999, :7001], "tail vs padded")
+    assert np.all(padded[4999:].view(np.uint16) == 0)
+    assert np.all(padded[:, 7001:].view(np.uint16) == 0)
+
+
+def test_integer_workload_full_matrix(g):
+    """4096^3 with entries in {-2..2}: every partial sum is an integer below
+    2^24, so the whole output must equal the exactly computed integer product
+    (numpy fp64 matmul is exact here)."""
+    a, b = workloads.workload_inputs("square4096_int")
+    got = run_gpu(g, a, b)
+    exact = (a.astype(np.float64) @ b.astype(np.float64).T).astype(np.float16)
+    assert_bit_exact(got, exact, "4096^3 int2 full matrix")
