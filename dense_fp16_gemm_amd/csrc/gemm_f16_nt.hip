@@ -57,42 +57,61 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int BK = 64;                 // K elements per LDS stage
-constexpr int ROW_BYTES = BK * 2;      // one tile row of a stage: 128 B = 8 chunks
 constexpr uint32_t OOB_OFFSET = 0x80000000u;  // past every resource: reads 0
 constexpr int64_t MAX_K = int64_t(1) << 21;   // keeps BM * K * 2 < 2^31
 constexpr int LDS_LIMIT = 160 * 1024;  // gfx950 LDS per workgroup
 constexpr int DEFAULT_XCDS = 8;        // MI355X: 8 XCDs x 32 CUs
+constexpr int DMA_BYTES = 64 * 16;     // one direct-to-LDS instruction: 64 lanes x 16 B
 
-// The 3-bit XOR applied to the 16-byte chunk index of tile row r.  It depends
-// only on r mod 32, so a 32-row MFMA fragment read sees the same pattern in
-// every block.  For the 32 lanes that read rows r0..r0+31 at one logical
-// chunk, any 8 consecutive rows hit 8 distinct chunks and any 16 consecutive
-// rows hit 16 distinct (row parity, chunk) pairs, i.e. all 64 banks of a
-// 256-byte LDS line.
-__host__ __device__ constexpr int chunk_swizzle(int r) { return (r & 7) ^ ((r >> 3) & 3); }
+// XOR applied to the 16-byte chunk index of LDS tile row r (rows are BK * 2
+// bytes = CHUNKS chunks).  An MFMA fragment read has 32 lanes reading rows
+// r0 .. r0 + 31 (r0 a multiple of 32) at one logical chunk.  The swizzle
+// depends on r mod 32 only and makes any 8 consecutive rows of such a read
+// cover 128 distinct bytes of bank space and any 16 consecutive rows 256
+// distinct bytes, i.e. conflict-free whether a ds_read_b128 is served 8 or 16
+// lanes at a time from 32 or 64 banks.
+//   8 chunks (128 B rows): row parity picks the 128-byte half of a 256-byte
+//   bank line, so the chunk XOR must differ across 8 consecutive rows and
+//   across the 8 even (odd) rows of 16: (r & 7) ^ ((r >> 3) & 3).
+//   4 chunks (64 B rows): r mod 4 picks the 64-byte quarter; the XOR must
+//   differ across the 4 rows of one quarter within 16 rows and across the
+//   even (odd) rows of 8: ((r >> 1) & 3) ^ ((r >> 3) & 1).
+template <int CHUNKS>
+__host__ __device__ constexpr int chunk_swizzle(int r)
+{
+    return CHUNKS == 8 ? ((r & 7) ^ ((r >> 3) & 3)) : (((r >> 1) & 3) ^ ((r >> 3) & 1));
+}
 
-template <int BM_, int BN_, int WM_, int WN_, int STAGES_>
+template <int BM_, int BN_, int BK_, int WM_, int WN_, int STAGES_>
 struct Cfg {
-    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, STAGES = STAGES_;
+    static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, STAGES = STAGES_;
     static constexpr int WAVES = WM * WN;
     static constexpr int THREADS = 64 * WAVES;
+    // one workgroup per CU (the LDS ring takes most of the 160 KB)
+    static constexpr int WAVES_PER_SIMD = WAVES <= 4 ? 1 : WAVES / 4;
     static constexpr int TM = BM / WM;           // wave tile rows (M)
     static constexpr int TN = BN / WN;           // wave tile columns (N)
     static constexpr int FM = TM / 32;           // 32x32 MFMA blocks per wave along M
     static constexpr int FN = TN / 32;           // ... along N
+    static constexpr int KK = BK / 16;           // 16-deep MFMA steps per K-slice
+    static constexpr int ROW_BYTES = BK * 2;     // one LDS tile row
+    static constexpr int CHUNKS = BK / 8;        // 16-byte chunks per row
+    static constexpr int DMA_ROWS = DMA_BYTES / ROW_BYTES;   // rows per DMA instruction
     static constexpr int A_BYTES = BM * ROW_BYTES;
     static constexpr int B_BYTES = BN * ROW_BYTES;
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
     static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
-    static constexpr int A_LOADS = BM / 8 / WAVES;   // DMA instructions per wave per stage
-    static constexpr int B_LOADS = BN / 8 / WAVES;   // (one instruction = 8 rows x 128 B)
+    static constexpr int A_LOADS = BM / DMA_ROWS / WAVES;    // DMA instructions per wave per stage
+    static constexpr int B_LOADS = BN / DMA_ROWS / WAVES;
     static constexpr int LOADS = A_LOADS + B_LOADS;
+    static_assert(BK == 32 || BK == 64, "BK is 32 or 64");
+    static_assert(KK % 2 == 0, "fragment double buffer alternates within a slice");
     static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be whole 32x32 blocks");
-    static_assert(BM % (8 * WAVES) == 0 && BN % (8 * WAVES) == 0, "DMA rows per wave");
+    static_assert(BM % (DMA_ROWS * WAVES) == 0 && BN % (DMA_ROWS * WAVES) == 0,
+                  "every wave issues the same number of DMA instructions");
     static_assert(STAGES >= 2, "need at least a double buffer");
     static_assert(LDS_BYTES <= LDS_LIMIT, "LDS ring exceeds 160 KB");
-    static_assert((STAGES - 2) * LOADS <= 63, "vmcnt counts at most 63 loads");
+    static_assert((STAGES - 1) * LOADS <= 63, "vmcnt counts at most 63 loads");
 };
 
 struct Params {
@@ -142,11 +161,119 @@ __device__ __forceinline__ void lds_barrier()
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
 }
 
+// Coordinates and buffer resources of one output tile.
+struct Tile {
+    int32_t m0, n0;
+    i32x4_t rsrc_a, rsrc_b;
+};
+
 template <class CF>
-__global__ __launch_bounds__(CF::THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__device__ __forceinline__ Tile make_tile(const Params &p, int32_t slot, uint32_t row_pitch)
+{
+    int32_t tile_m, tile_n;
+    grouped_tile(slot_to_linear(slot, p.grid, p.tiles, p.xcds), p.tiles_m, p.tiles_n,
+                 p.swizzle, tile_m, tile_n);
+    Tile t;
+    t.m0 = tile_m * CF::BM;
+    t.n0 = tile_n * CF::BN;
+    // the resource covers exactly the tile's valid rows: rows past M (N) read 0
+    const int32_t rows_a = min(CF::BM, p.M - t.m0);
+    const int32_t rows_b = min(CF::BN, p.N - t.n0);
+    t.rsrc_a = make_rsrc(p.A + static_cast<int64_t>(t.m0) * p.K,
+                         static_cast<uint32_t>(rows_a) * row_pitch);
+    t.rsrc_b = make_rsrc(p.B + static_cast<int64_t>(t.n0) * p.K,
+                         static_cast<uint32_t>(rows_b) * row_pitch);
+    return t;
+}
+
+// One of this wave's DMA instructions for K-slice `kt` of tile `t`, into ring
+// stage `stage`.  Instruction i fills rows R = (i' * WAVES + wave) * DMA_ROWS
+// .. R + DMA_ROWS - 1 of the A tile (i < A_LOADS, i' = i) or of the B tile
+// (i' = i - A_LOADS); lane l writes physical chunk l % CHUNKS of row
+// R + l / CHUNKS, so it fetches logical chunk (l % CHUNKS) ^ swz(row).  A
+// chunk at or past K gets an offset beyond the resource and lands as zeros.
+template <class CF>
+__device__ __forceinline__ void dma_one(const Params &p, const Tile &t, int stage, int kt, int i,
+                                        uint32_t lds0, int wave, int lane, uint32_t row_pitch)
+{
+    const uint32_t k0 = static_cast<uint32_t>(kt) * CF::BK;
+    const bool is_a = i < CF::A_LOADS;
+    const int rblk = (is_a ? i : i - CF::A_LOADS) * CF::WAVES + wave;
+    const int row = rblk * CF::DMA_ROWS + lane / CF::CHUNKS;
+    const int chunk = (lane % CF::CHUNKS) ^ chunk_swizzle<CF::CHUNKS>(row);
+    uint32_t v = static_cast<uint32_t>(row) * row_pitch + chunk * 16 + k0 * 2;
+    if (k0 + chunk * 8 >= static_cast<uint32_t>(p.K)) v = OOB_OFFSET;
+    dma16(is_a ? t.rsrc_a : t.rsrc_b, v,
+          lds0 + stage * CF::STAGE_BYTES + (is_a ? 0 : CF::A_BYTES) +
+              rblk * CF::DMA_ROWS * CF::ROW_BYTES);
+}
+
+// All DMA instructions of one slice, back to back (prefill only).
+template <class CF>
+__device__ __forceinline__ void dma_slice(const Params &p, const Tile &t, int stage, int kt,
+                                          uint32_t lds0, int wave, int lane, uint32_t row_pitch)
+{
+#pragma unroll
+    for (int i = 0; i < CF::LOADS; ++i) dma_one<CF>(p, t, stage, kt, i, lds0, wave, lane, row_pitch);
+}
+
+// Work of one 16-deep K step, in a fixed issue order.  The wave owns one
+// SIMD's matrix pipe, so its instruction stream must keep an MFMA issuing
+// every 32 cycles: after MFMA t it issues its share of
+//   * the next step's fragment reads (spread over the first half of the
+//     step, so they have the second half to return), and
+//   * `dma_count` DMA instructions refilling the stage freed at the last
+//     barrier (spread over the whole step, so the vector-memory queue drains
+//     between them instead of stalling the wave).
+// sched_barrier(0) after each group keeps the compiler from regrouping them.
+template <class CF, bool READS, int DMA_PER_STEP>
+struct Step {
+    template <class ReadFn, class DmaFn>
+    __device__ __forceinline__ static void run(f32x16_t (&acc)[CF::FM][CF::FN],
+                                               const half8_t (&af)[CF::FM],
+                                               const half8_t (&bf)[CF::FN], ReadFn read,
+                                               DmaFn dma)
+    {
+        constexpr int NM = CF::FM * CF::FN;
+        constexpr int NR = CF::FM + CF::FN;
+        constexpr int RSPAN = NM / 2 > 0 ? NM / 2 : 1;
+#pragma unroll
+        for (int t = 0; t < NM; ++t) {
+            const int i = t / CF::FN, j = t % CF::FN;
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[j], af[i], acc[i][j], 0, 0, 0);
+            if constexpr (READS) {
+                const int r0 = t < RSPAN ? (t * NR) / RSPAN : NR;
+                const int r1 = t < RSPAN ? ((t + 1) * NR) / RSPAN : NR;
+#pragma unroll
+                for (int r = r0; r < r1; ++r) read(r);
+            }
+            if constexpr (DMA_PER_STEP > 0) {
+                const int d0 = (t * DMA_PER_STEP) / NM;
+                const int d1 = ((t + 1) * DMA_PER_STEP) / NM;
+#pragma unroll
+                for (int d = d0; d < d1; ++d) dma(d);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+};
+
+template <class CF>
+__global__ __launch_bounds__(CF::THREADS)
+__attribute__((amdgpu_waves_per_eu(CF::WAVES_PER_SIMD, CF::WAVES_PER_SIMD)))
 void gemm_f16_nt_kernel(Params p)
 {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[CF::LDS_BYTES];
+    constexpr int S = CF::STAGES;
+    constexpr int KK = CF::KK;
+    constexpr int L = CF::LOADS;
+    constexpr int DPS = L / KK;                 // DMA instructions per 16-deep step
+    static_assert(L % KK == 0, "a slice's DMA splits evenly over its steps");
+    static_assert(S >= 3, "a refill streams over a whole slice: needs 3+ stages");
+    // outstanding DMA allowed when slice kt + 1 must have landed at the end of
+    // slice kt: slices kt+2 .. kt+S-2 and the first KK-1 parts of kt+S-1
+    constexpr int VM_STEADY = (S - 3) * L + (KK - 1) * DPS;
+    static_assert((S - 1) * L <= 63, "vmcnt counts at most 63 loads");
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -154,61 +281,43 @@ void gemm_f16_nt_kernel(Params p)
     const int wave_n = wave - wave_m * CF::WN;
     const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(smem));
     const uint32_t row_pitch = static_cast<uint32_t>(p.K) * 2u;   // bytes per A/B row
-    const int KT = (p.K + BK - 1) / BK;
+    const int KT = (p.K + CF::BK - 1) / CF::BK;
 
-    // ---- per-lane DMA geometry ---------------------------------------------
-    // Slot i of this wave fills tile rows R = (i * WAVES + wave) * 8 .. R + 7;
-    // lane l writes physical chunk l % 8 of row R + l / 8, which must hold
-    // logical chunk (l % 8) ^ swz(R + l / 8).  Since swz(r) = (r & 7) ^
-    // ((r >> 3) & 3), that is (l % 8) ^ (l / 8) ^ ((i * WAVES + wave) & 3):
-    // a per-lane constant XOR a wave-uniform one.
-    const uint32_t dma_lane_row = static_cast<uint32_t>(lane >> 3) * row_pitch;
-    const int dma_lane_x = (lane & 7) ^ (lane >> 3);
-
-    // ---- per-lane fragment read offsets ------------------------------------
     // Fragment lane l reads row (l % 32) of a 32-row block, logical chunk
     // 2 * kk + l / 32 (8 consecutive k), physically XOR-swizzled.
     const int r32 = lane & 31;
     const int khalf = lane >> 5;
-    uint32_t frag_off[4];
+    uint32_t frag_off[KK];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-        frag_off[kk] = r32 * ROW_BYTES + (((2 * kk + khalf) ^ chunk_swizzle(r32)) * 16);
-    const uint32_t a_frag_base = wave_m * CF::TM * ROW_BYTES;
-    const uint32_t b_frag_base = CF::A_BYTES + wave_n * CF::TN * ROW_BYTES;
+    for (int kk = 0; kk < KK; ++kk)
+        frag_off[kk] = r32 * CF::ROW_BYTES +
+                       (((2 * kk + khalf) ^ chunk_swizzle<CF::CHUNKS>(r32)) * 16);
+    const uint32_t a_frag_base = wave_m * CF::TM * CF::ROW_BYTES;
+    const uint32_t b_frag_base = CF::A_BYTES + wave_n * CF::TN * CF::ROW_BYTES;
 
-    for (int32_t slot = blockIdx.x; slot < p.tiles; slot += p.grid) {
-        int32_t tile_m, tile_n;
-        grouped_tile(slot_to_linear(slot, p.grid, p.tiles, p.xcds), p.tiles_m, p.tiles_n,
-                     p.swizzle, tile_m, tile_n);
-        const int32_t m0 = tile_m * CF::BM;
-        const int32_t n0 = tile_n * CF::BN;
-        const int32_t rows_a = min(CF::BM, p.M - m0);
-        const int32_t rows_b = min(CF::BN, p.N - n0);
-        const i32x4_t rsrc_a = make_rsrc(p.A + static_cast<int64_t>(m0) * p.K,
-                                         static_cast<uint32_t>(rows_a) * row_pitch);
-        const i32x4_t rsrc_b = make_rsrc(p.B + static_cast<int64_t>(n0) * p.K,
-                                         static_cast<uint32_t>(rows_b) * row_pitch);
+    half8_t af[2][CF::FM], bf[2][CF::FN];
+    // read r of step kk of `stage` into buffer `buf`: r < FM -> A block r, else B block r - FM
+    auto read_frag = [&](int buf, int stage, int kk, int r) {
+        const uint32_t st = stage * CF::STAGE_BYTES + frag_off[kk];
+        if (r < CF::FM)
+            af[buf][r] = *reinterpret_cast<const half8_t *>(smem + st + a_frag_base +
+                                                             r * 32 * CF::ROW_BYTES);
+        else
+            bf[buf][r - CF::FM] = *reinterpret_cast<const half8_t *>(
+                smem + st + b_frag_base + (r - CF::FM) * 32 * CF::ROW_BYTES);
+    };
+    auto no_dma = [](int) {};
 
-        // Issue the DMA of K-slice `kt` into ring stage `stage`.
-        auto issue = [&](int stage, int kt) {
-            const uint32_t k0 = static_cast<uint32_t>(kt) * BK;
-            const bool full = k0 + BK <= static_cast<uint32_t>(p.K);
-            const uint32_t base = lds0 + stage * CF::STAGE_BYTES;
+    int32_t slot = blockIdx.x;
+    if (slot >= p.tiles) return;
+    Tile cur = make_tile<CF>(p, slot, row_pitch);
+    // Prefill: slices 0 .. S-2 into stages 0 .. S-2; stage S-1 is refilled
+    // while slice 0 is computed.  Issued even when K has fewer slices (those
+    // move no data), so every wait below counts the same instructions.
 #pragma unroll
-            for (int i = 0; i < CF::LOADS; ++i) {
-                const bool is_a = i < CF::A_LOADS;
-                const int slot_i = is_a ? i : i - CF::A_LOADS;
-                const int rblk = slot_i * CF::WAVES + wave;          // 8-row block index
-                const int chunk = dma_lane_x ^ (rblk & 3);
-                uint32_t v = dma_lane_row + static_cast<uint32_t>(rblk * 8) * row_pitch +
-                             chunk * 16 + k0 * 2;
-                if (!full && k0 + chunk * 8 >= static_cast<uint32_t>(p.K)) v = OOB_OFFSET;
-                dma16(is_a ? rsrc_a : rsrc_b, v,
-                      base + (is_a ? 0 : CF::A_BYTES) + rblk * 8 * ROW_BYTES);
-            }
-        };
+    for (int s = 0; s < S - 1; ++s) dma_slice<CF>(p, cur, s, s, lds0, wave, lane, row_pitch);
 
+    while (true) {
         f32x16_t acc[CF::FM][CF::FN];
 #pragma unroll
         for (int i = 0; i < CF::FM; ++i)
@@ -217,72 +326,59 @@ void gemm_f16_nt_kernel(Params p)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-        // Prefill: K-slices 0 .. STAGES-2 (fewer when K is short).
-#pragma unroll
-        for (int s = 0; s < CF::STAGES - 1; ++s)
-            if (s < KT) issue(s, s);
-
-        int rd_stage = 0;                 // stage holding slice kt
-        int wr_stage = CF::STAGES - 1;    // stage that receives slice kt + STAGES - 1
-        for (int kt = 0; kt < KT; ++kt) {
-            // "full": this wave's DMA for slice kt has landed (slices issued
-            // after it may stay in flight) ...
-            if (kt + CF::STAGES - 2 < KT)
-                wait_vmcnt<(CF::STAGES - 2) * CF::LOADS>();
-            else
-                wait_vmcnt<0>();
-            // ... and every wave's has; "empty": every wave has finished
-            // reading wr_stage (it held slice kt - 1).
+        if (KT > 0) {
+            // slice 0 landed (slices 1 .. S-2 may still be in flight)
+            wait_vmcnt<(S - 2) * L>();
             lds_barrier();
-            if (kt + CF::STAGES - 1 < KT) issue(wr_stage, kt + CF::STAGES - 1);
+#pragma unroll
+            for (int r = 0; r < CF::FM + CF::FN; ++r) read_frag(0, 0, 0, r);
+        }
 
-            const uint32_t st = rd_stage * CF::STAGE_BYTES;
-            half8_t af[2][CF::FM], bf[2][CF::FN];
-            auto load_frags = [&](int buf, int kk) {
+        // One branch-free loop over the slices.  Slice kt streams in the refill
+        // of slice kt + S - 1 (into the stage freed before slice kt); past the
+        // end of K those refills carry out-of-range offsets, so they move no
+        // data and only write zeros into stages this tile no longer reads.
+        // Their accounting is therefore identical to the real ones.
+        int rd = 0;        // stage holding slice kt
+        int pst = S - 1;   // stage receiving slice kt + S - 1, freed before slice kt
+        for (int kt = 0; kt < KT; ++kt) {
+            const int rd_next = rd + 1 == S ? 0 : rd + 1;
+            const int pkt = kt + S - 1;
 #pragma unroll
-                for (int i = 0; i < CF::FM; ++i)
-                    af[buf][i] = *reinterpret_cast<const half8_t *>(
-                        smem + st + a_frag_base + i * 32 * ROW_BYTES + frag_off[kk]);
-#pragma unroll
-                for (int j = 0; j < CF::FN; ++j)
-                    bf[buf][j] = *reinterpret_cast<const half8_t *>(
-                        smem + st + b_frag_base + j * 32 * ROW_BYTES + frag_off[kk]);
-            };
-            load_frags(0, 0);
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                if (kk < 3) load_frags((kk + 1) & 1, kk + 1);
-#pragma unroll
-                for (int i = 0; i < CF::FM; ++i)
-#pragma unroll
-                    for (int j = 0; j < CF::FN; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                            bf[kk & 1][j], af[kk & 1][i], acc[i][j], 0, 0, 0);
-            }
-            // Pin the issue order for the scheduler: the first step's reads,
-            // then for each 16-deep step its MFMAs with the next step's
-            // fragment reads slotted one after each MFMA, so the reads are in
-            // flight while the matrix pipe works.
-            constexpr int kReads = CF::FM + CF::FN;
-            constexpr int kMfma = CF::FM * CF::FN;
-            constexpr int kPaired = kReads < kMfma ? kReads : kMfma;
-            __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                if (kk < 3) {
-#pragma unroll
-                    for (int t = 0; t < kPaired; ++t) {
-                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                    }
-                    if (kReads > kPaired) __builtin_amdgcn_sched_group_barrier(0x100, kReads - kPaired, 0);
-                    if (kMfma > kPaired) __builtin_amdgcn_sched_group_barrier(0x008, kMfma - kPaired, 0);
+            for (int kk = 0; kk < KK; ++kk) {
+                auto dma = [&](int d) {
+                    dma_one<CF>(p, cur, pst, pkt, kk * DPS + d, lds0, wave, lane, row_pitch);
+                };
+                if (kk + 1 < KK) {
+                    auto rf = [&](int r) { read_frag((kk + 1) & 1, rd, kk + 1, r); };
+                    Step<CF, true, DPS>::run(acc, af[kk & 1], bf[kk & 1], rf, dma);
                 } else {
-                    __builtin_amdgcn_sched_group_barrier(0x008, kMfma, 0);
+                    // End of the slice (the last step's fragments are in
+                    // registers).  "full": slice kt + 1 has landed for this
+                    // wave, and after the barrier for every wave; "empty":
+                    // every wave has read all of stage rd, which receives
+                    // slice kt + S during the next slice.  After the last
+                    // slice the reads below fetch unused data (in bounds).
+                    wait_vmcnt<VM_STEADY>();
+                    lds_barrier();
+                    auto rf = [&](int r) { read_frag(0, rd_next, 0, r); };
+                    Step<CF, true, DPS>::run(acc, af[kk & 1], bf[kk & 1], rf, dma);
                 }
             }
-            rd_stage = rd_stage + 1 == CF::STAGES ? 0 : rd_stage + 1;
-            wr_stage = wr_stage + 1 == CF::STAGES ? 0 : wr_stage + 1;
+            pst = rd;
+            rd = rd_next;
+        }
+
+        // Every wave is done with the ring (and every DMA has landed): the next
+        // tile's prefill may start, and it flies while this tile is stored.
+        wait_vmcnt<0>();
+        lds_barrier();
+        const int32_t next = slot + p.grid;
+        Tile nxt;
+        if (next < p.tiles) {
+            nxt = make_tile<CF>(p, next, row_pitch);
+#pragma unroll
+            for (int s = 0; s < S - 1; ++s) dma_slice<CF>(p, nxt, s, s, lds0, wave, lane, row_pitch);
         }
 
         // ---- epilogue: RNE to fp16, masked stores --------------------------
@@ -290,14 +386,14 @@ void gemm_f16_nt_kernel(Params p)
         // m = l % 32 and n = 8 g + 4 (l / 32) inside the block.
 #pragma unroll
         for (int i = 0; i < CF::FM; ++i) {
-            const int32_t m = m0 + wave_m * CF::TM + i * 32 + r32;
+            const int32_t m = cur.m0 + wave_m * CF::TM + i * 32 + r32;
             if (m < p.M) {
                 uint16_t *crow = p.C + static_cast<int64_t>(m) * p.N;
 #pragma unroll
                 for (int j = 0; j < CF::FN; ++j) {
 #pragma unroll
                     for (int g = 0; g < 4; ++g) {
-                        const int32_t n = n0 + wave_n * CF::TN + j * 32 + g * 8 + khalf * 4;
+                        const int32_t n = cur.n0 + wave_n * CF::TN + j * 32 + g * 8 + khalf * 4;
                         f32x4_t v;
                         v.x = acc[i][j][4 * g + 0];
                         v.y = acc[i][j][4 * g + 1];
@@ -316,8 +412,9 @@ void gemm_f16_nt_kernel(Params p)
                 }
             }
         }
-        // Every wave is done with the ring before the next tile's prefill.
-        lds_barrier();
+        if (next >= p.tiles) break;
+        slot = next;
+        cur = nxt;
     }
 }
 
@@ -326,7 +423,7 @@ void gemm_f16_nt_kernel(Params p)
 // ---------------------------------------------------------------------------
 struct KernelEntry {
     const void *fn;
-    int32_t block_m, block_n, waves, stages, lds_bytes, threads;
+    int32_t block_m, block_n, block_k, waves, stages, lds_bytes, threads;
     int32_t default_swizzle;
     float rel_rate;   // relative MFMA rate per tile area, for the plan cost model
 };
@@ -335,16 +432,20 @@ template <class CF>
 constexpr KernelEntry entry(int swizzle, float rate)
 {
     return KernelEntry{reinterpret_cast<const void *>(&gemm_f16_nt_kernel<CF>),
-                       CF::BM, CF::BN, CF::WAVES, CF::STAGES, CF::LDS_BYTES, CF::THREADS,
+                       CF::BM, CF::BN, CF::BK, CF::WAVES, CF::STAGES, CF::LDS_BYTES, CF::THREADS,
                        swizzle, rate};
 }
 
 static const KernelEntry kKernels[] = {
-    entry<Cfg<256, 256, 2, 2, 2>>(8, 1.00f),   // 0: 4 waves of 128x128
-    entry<Cfg<256, 256, 2, 4, 2>>(8, 0.95f),   // 1: 8 waves of 128x64
-    entry<Cfg<256, 128, 2, 2, 3>>(8, 0.90f),   // 2: 4 waves of 128x64, 3 stages
-    entry<Cfg<128, 128, 2, 2, 4>>(8, 0.80f),   // 3: 4 waves of 64x64, 4 stages
-    entry<Cfg<128, 64, 2, 1, 6>>(8, 0.60f),    // 4: 2 waves of 64x64, 6 stages
+    entry<Cfg<256, 256, 32, 2, 2, 4>>(8, 1.00f),   // 0: 4 waves of 128x128, 4 stages of K 32
+    entry<Cfg<256, 256, 32, 2, 2, 5>>(8, 0.00f),   // 1: the same, 5 stages
+    entry<Cfg<256, 128, 64, 2, 2, 3>>(8, 0.90f),   // 2: 4 waves of 128x64, 3 stages of K 64
+    entry<Cfg<256, 128, 32, 2, 2, 6>>(8, 0.00f),   // 3: the same tile, 6 stages of K 32
+    entry<Cfg<128, 128, 64, 2, 2, 4>>(8, 0.80f),   // 4: 4 waves of 64x64, 4 stages
+    entry<Cfg<128, 64, 64, 2, 1, 6>>(8, 0.60f),    // 5: 2 waves of 64x64, 6 stages
+    entry<Cfg<256, 256, 32, 2, 4, 4>>(8, 0.00f),   // 6: 8 waves of 128x64, 4 stages of K 32
+    entry<Cfg<256, 256, 32, 4, 2, 4>>(8, 0.00f),   // 7: 8 waves of 64x128, 4 stages of K 32
+    entry<Cfg<256, 256, 32, 2, 4, 5>>(8, 0.00f),   // 8: 8 waves of 128x64, 5 stages of K 32
 };
 constexpr int kNumKernels = sizeof(kKernels) / sizeof(kKernels[0]);
 
@@ -386,7 +487,7 @@ static void fill_info(int id, gemm_f16_nt_plan_t *out)
     out->config_id = id;
     out->block_m = e.block_m;
     out->block_n = e.block_n;
-    out->block_k = BK;
+    out->block_k = e.block_k;
     out->waves = e.waves;
     out->stages = e.stages;
     out->swizzle = e.default_swizzle;
@@ -409,17 +510,18 @@ static void make_plan(int id, int64_t M, int64_t N, int32_t num_cus, int32_t swi
 
 // Cost model: rounds of the persistent grid times the time one tile takes,
 // which scales with its area over the configuration's relative MFMA rate.
+// Entries with rel_rate 0 are compiled for sweeps but never planned.
 static int choose_config(int64_t M, int64_t N, int32_t num_cus)
 {
-    int best = 0;
+    int best = -1;
     double best_cost = 0.0;
     for (int id = 0; id < kNumKernels; ++id) {
         const KernelEntry &e = kKernels[id];
-        if (id == 1) continue;   // kept for sweeps; never better than id 0 in the model
+        if (e.rel_rate <= 0.0f) continue;
         const int64_t tiles = cdiv(M, e.block_m) * cdiv(N, e.block_n);
         const int64_t rounds = cdiv(tiles, num_cus > 0 ? num_cus : 1);
         const double cost = static_cast<double>(rounds) * e.block_m * e.block_n / e.rel_rate;
-        if (id == 0 || cost < best_cost) {
+        if (best < 0 || cost < best_cost) {
             best = id;
             best_cost = cost;
         }

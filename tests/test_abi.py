@@ -81,9 +81,9 @@ def test_config_table(g):
     for cid in range(n):
         info = g.gemm_f16_nt_config_info(cid)
         assert info.config_id == cid
-        assert info.block_k == 64
+        assert info.block_k in (32, 64)
         # the LDS ring: stages * (BM + BN) * BK * 2 bytes within 160 KB
-        assert info.lds_bytes == info.stages * (info.block_m + info.block_n) * 64 * 2
+        assert info.lds_bytes == info.stages * (info.block_m + info.block_n) * info.block_k * 2
         assert info.lds_bytes <= 160 * 1024
         assert info.block_m % 32 == 0 and info.block_n % 32 == 0
     with pytest.raises(g.GemmError):
