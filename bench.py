@@ -41,22 +41,30 @@ def source_digest() -> str:
 
 
 def measured_traffic(workload: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or
-    None when there is none or the kernel source has changed since."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    """HBM-side bytes per launch from the committed rocprofv3 counter summary
+    (profiles/traffic_<workload>.txt, "key = value" lines), or None when there
+    is none or the kernel source has changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
     if not os.path.exists(path):
         return None
+    fields = {}
     with open(path) as f:
-        t = json.load(f)
-    if t.get("source_digest") != source_digest():
+        for line in f:
+            if " = " in line:
+                key, _, val = line.partition(" = ")
+                fields[key.strip()] = val.strip()
+    if fields.get("source_digest") != source_digest():
         return None
-    return t.get("hbm_bytes_per_launch")
+    try:
+        return int(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(w, target_s: float):
     """The oracle, as it is, on a bounded block of the workload: the first
-    m_s rows of A and n_s rows of B at the full K.  Scaled from a short probe
-    to take about target_s seconds."""
+    m_s rows of A against all of B at the full K (a block of C), grown until
+    one evaluation takes about target_s seconds."""
     import numpy as np
 
     import oracle
@@ -64,21 +72,19 @@ def cpu_baseline(w, target_s: float):
 
     threads = oracle.default_threads()
     a, b = workloads.workload_inputs(w.name)
-    ms, ns = min(w.M, 64), min(w.N, 64)
-    t0 = time.perf_counter()
-    oracle.gemm(np.ascontiguousarray(a[:ms]), np.ascontiguousarray(b[:ns]), threads=threads)
-    probe = max(time.perf_counter() - t0, 1e-3)
-    scale = max(1.0, target_s / probe)
-    # grow the block along N first, then M, keeping it within the workload
-    ns2 = int(min(w.N, ns * scale))
-    ms2 = int(min(w.M, ms * max(1.0, scale * ns / ns2)))
-    t0 = time.perf_counter()
-    oracle.gemm(np.ascontiguousarray(a[:ms2]), np.ascontiguousarray(b[:ns2]), threads=threads)
-    dt = time.perf_counter() - t0
-    flops = 2.0 * ms2 * ns2 * w.K
+    ns = w.N
+    ms = max(1, min(w.M, threads))
+    while True:
+        t0 = time.perf_counter()
+        oracle.gemm(np.ascontiguousarray(a[:ms]), np.ascontiguousarray(b[:ns]), threads=threads)
+        dt = time.perf_counter() - t0
+        if dt >= 0.5 * target_s or ms >= w.M:
+            break
+        ms = min(w.M, max(ms + threads, int(ms * min(8.0, 1.2 * target_s / max(dt, 1e-3)))))
+    flops = 2.0 * ms * ns * w.K
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"C[0:{ms2}, 0:{ns2}] of {w.name} at K={w.K} "
-                      f"({ms2 * ns2} of {w.M * w.N} outputs), {dt:.1f} s"}
+            "sample": f"C[0:{ms}, 0:{ns}] of {w.name} at K={w.K} "
+                      f"({ms * ns} of {w.M * w.N} outputs), {dt:.1f} s"}
 
 
 def copy_probe(args) -> int:
