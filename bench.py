@@ -113,6 +113,8 @@ def main() -> int:
     ap.add_argument("--config", type=int, default=None, help="force a kernel configuration")
     ap.add_argument("--swizzle", type=int, default=0)
     ap.add_argument("--grid", type=int, default=0)
+    ap.add_argument("--epilogue", type=int, default=-1,
+                    help="-1: library choice, 0: direct stores, 1: staged through LDS")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -154,12 +156,14 @@ def main() -> int:
         info = g.gemm_f16_nt_config_info(args.config).as_dict()
         plan.update({k: info[k] for k in ("config_id", "block_m", "block_n", "block_k", "waves",
                                           "stages", "lds_bytes")})
+    if args.epilogue >= 0:
+        plan["epilogue"] = args.epilogue
 
     stream = torch.cuda.current_stream(dev)
 
     def launch():
         g.gemm_nt(a, b, out=c, config=args.config, swizzle=args.swizzle, grid=args.grid,
-                  stream=stream)
+                  stream=stream, epilogue=args.epilogue)
 
     # cooldown first (the pages' protocol), then the warm-up launches bring
     # the clock back up from idle before the timed window opens

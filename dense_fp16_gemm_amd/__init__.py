@@ -33,7 +33,7 @@ class Plan(ctypes.Structure):
                 ("config_id", "block_m", "block_n", "block_k", "waves", "stages",
                  "swizzle", "tiles_m", "tiles_n", "grid")] + \
                [("tiles", ctypes.c_int64), ("lds_bytes", ctypes.c_int32),
-                ("xcds", ctypes.c_int32)]
+                ("xcds", ctypes.c_int32), ("epilogue", ctypes.c_int32)]
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -57,7 +57,7 @@ def load():
         i64, i32, p = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
         lib.gemm_f16_nt.argtypes = [i64, i64, i64, p, p, p, p]
         lib.gemm_f16_nt.restype = ctypes.c_int
-        lib.gemm_f16_nt_with_config.argtypes = [i64, i64, i64, p, p, p, p, i32, i32, i32]
+        lib.gemm_f16_nt_with_config.argtypes = [i64, i64, i64, p, p, p, p, i32, i32, i32, i32]
         lib.gemm_f16_nt_with_config.restype = ctypes.c_int
         lib.gemm_f16_nt_status_string.argtypes = [ctypes.c_int]
         lib.gemm_f16_nt_status_string.restype = ctypes.c_char_p
@@ -92,8 +92,10 @@ def gemm_f16_nt(M: int, N: int, K: int, A: int, B: int, C: int, stream: int = 0)
 
 
 def gemm_f16_nt_with_config(M: int, N: int, K: int, A: int, B: int, C: int, stream: int,
-                            config_id: int, swizzle: int = 0, grid: int = 0) -> None:
-    _check(load().gemm_f16_nt_with_config(M, N, K, A, B, C, stream, config_id, swizzle, grid),
+                            config_id: int, swizzle: int = 0, grid: int = 0,
+                            epilogue: int = -1) -> None:
+    _check(load().gemm_f16_nt_with_config(M, N, K, A, B, C, stream, config_id, swizzle, grid,
+                                          epilogue),
            "gemm_f16_nt_with_config")
 
 
@@ -127,7 +129,7 @@ def gemm_f16_nt_tile_of_slot(plan: Plan, slot: int) -> tuple[int, int]:
 
 # ---- torch convenience -------------------------------------------------------
 def gemm_nt(a, b, out=None, config: int | None = None, swizzle: int = 0, grid: int = 0,
-            stream=None):
+            stream=None, epilogue: int = -1):
     """C = a @ b.T for fp16 CUDA(HIP) tensors a [M,K] and b [N,K].
 
     Checks dtype, contiguity, device and shapes, then calls the C ABI on the
@@ -152,9 +154,10 @@ def gemm_nt(a, b, out=None, config: int | None = None, swizzle: int = 0, grid: i
         raise ValueError("out must be a contiguous float16 [M, N] tensor on a's device")
     s = stream if stream is not None else torch.cuda.current_stream(a.device)
     with torch.cuda.device(a.device):
-        if config is None:
+        if config is None and epilogue < 0:
             gemm_f16_nt(m, n, k, a.data_ptr(), b.data_ptr(), out.data_ptr(), s.cuda_stream)
         else:
             gemm_f16_nt_with_config(m, n, k, a.data_ptr(), b.data_ptr(), out.data_ptr(),
-                                    s.cuda_stream, config, swizzle, grid)
+                                    s.cuda_stream, -1 if config is None else config, swizzle,
+                                    grid, epilogue)
     return out

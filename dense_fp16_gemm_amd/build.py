@@ -25,6 +25,10 @@ def compile_command(out: str) -> list[str]:
     return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
             # packed fp32 VALU ops stay off (only the device pass knows the feature)
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # the MFMA step loops must unroll fully: accumulators are indexed
+            # by the loop counters, and a rolled loop would demote them to
+            # scratch memory
+            "-mllvm", "-pragma-unroll-threshold=1000000",
             "-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG_DIR, "csrc"),
             "-o", out] + SOURCES
 

@@ -43,6 +43,7 @@
 #include <hip/hip_runtime.h>
 
 #include <mutex>
+#include <type_traits>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -56,6 +57,13 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
+
+template <int N>
+struct AccVec;
+template <>
+struct AccVec<16> { typedef f32x16_t type; };
+template <>
+struct AccVec<4> { typedef f32x4_t type; };
 
 constexpr uint32_t OOB_OFFSET = 0x80000000u;  // past every resource: reads 0
 constexpr int64_t MAX_K = int64_t(1) << 21;   // keeps BM * K * 2 < 2^31
@@ -82,18 +90,29 @@ __host__ __device__ constexpr int chunk_swizzle(int r)
     return CHUNKS == 8 ? ((r & 7) ^ ((r >> 3) & 3)) : (((r >> 1) & 3) ^ ((r >> 3) & 1));
 }
 
-template <int BM_, int BN_, int BK_, int WM_, int WN_, int STAGES_>
+// MI_ picks the MFMA: 32 -> v_mfma_f32_32x32x16_f16 (16 accumulators per lane
+// per block), 16 -> v_mfma_f32_16x16x32_f16 (4 per block: half the
+// accumulator register traffic per flop).
+template <int BM_, int BN_, int BK_, int WM_, int WN_, int STAGES_, int MI_ = 32,
+          int DSTEPS_ = 0>
 struct Cfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, STAGES = STAGES_;
+    static constexpr int MI = MI_;               // MFMA block edge (M and N)
+    static constexpr int MK = 512 / MI;          // K per MFMA: 16 or 32
+    static constexpr int ACC_N = MI * MI / 64;   // accumulators per lane per block
+    // steps of a slice that carry refill DMA (0: every step with 3+ stages,
+    // the first half with 2)
+    static constexpr int DSTEPS = DSTEPS_;
+    typedef typename AccVec<ACC_N>::type Acc;
     static constexpr int WAVES = WM * WN;
     static constexpr int THREADS = 64 * WAVES;
     // one workgroup per CU (the LDS ring takes most of the 160 KB)
     static constexpr int WAVES_PER_SIMD = WAVES <= 4 ? 1 : WAVES / 4;
     static constexpr int TM = BM / WM;           // wave tile rows (M)
     static constexpr int TN = BN / WN;           // wave tile columns (N)
-    static constexpr int FM = TM / 32;           // 32x32 MFMA blocks per wave along M
-    static constexpr int FN = TN / 32;           // ... along N
-    static constexpr int KK = BK / 16;           // 16-deep MFMA steps per K-slice
+    static constexpr int FM = TM / MI;           // MFMA blocks per wave along M
+    static constexpr int FN = TN / MI;           // ... along N
+    static constexpr int KK = BK / MK;           // MFMA K steps per K-slice
     static constexpr int ROW_BYTES = BK * 2;     // one LDS tile row
     static constexpr int CHUNKS = BK / 8;        // 16-byte chunks per row
     static constexpr int DMA_ROWS = DMA_BYTES / ROW_BYTES;   // rows per DMA instruction
@@ -104,9 +123,13 @@ struct Cfg {
     static constexpr int A_LOADS = BM / DMA_ROWS / WAVES;    // DMA instructions per wave per stage
     static constexpr int B_LOADS = BN / DMA_ROWS / WAVES;
     static constexpr int LOADS = A_LOADS + B_LOADS;
+    // the LDS-staged epilogue writes one block row of every wave (WM * MI tile
+    // rows of BN halves, rows padded by 16 bytes) into one ring stage
+    static constexpr bool STAGED_OK = WM * MI * (BN * 2 + 16) <= STAGE_BYTES;
     static_assert(BK == 32 || BK == 64, "BK is 32 or 64");
     static_assert(KK % 2 == 0, "fragment double buffer alternates within a slice");
-    static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be whole 32x32 blocks");
+    static_assert(MI == 32 || MI == 16, "MFMA is 32x32x16 or 16x16x32");
+    static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be whole 32-row blocks");
     static_assert(BM % (DMA_ROWS * WAVES) == 0 && BN % (DMA_ROWS * WAVES) == 0,
                   "every wave issues the same number of DMA instructions");
     static_assert(STAGES >= 2, "need at least a double buffer");
@@ -122,6 +145,8 @@ struct Params {
     int32_t tiles_m, tiles_n, tiles;
     int32_t swizzle, grid, xcds;
     int32_t c_vec;   // 1: C rows allow 8-byte stores (C 8-byte aligned, N % 4 == 0)
+    int32_t c_vec16; // 1: C rows allow 16-byte stores (C 16-byte aligned, N % 8 == 0)
+    int32_t staged;  // 1: stage C through LDS for row-contiguous stores
 };
 
 // Buffer resource (V#) for raw byte addressing of `bytes` bytes at `base`:
@@ -164,7 +189,8 @@ __device__ __forceinline__ void lds_barrier()
 // Coordinates and buffer resources of one output tile.
 struct Tile {
     int32_t m0, n0;
-    i32x4_t rsrc_a, rsrc_b;
+    i32x4_t rsrc_a, rsrc_b;              // for the DMA asm
+    __amdgpu_buffer_rsrc_t ra, rb;       // the same ranges, for register loads
 };
 
 template <class CF>
@@ -183,6 +209,12 @@ __device__ __forceinline__ Tile make_tile(const Params &p, int32_t slot, uint32_
                          static_cast<uint32_t>(rows_a) * row_pitch);
     t.rsrc_b = make_rsrc(p.B + static_cast<int64_t>(t.n0) * p.K,
                          static_cast<uint32_t>(rows_b) * row_pitch);
+    t.ra = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(p.A + static_cast<int64_t>(t.m0) * p.K), static_cast<short>(0),
+        static_cast<int32_t>(static_cast<uint32_t>(rows_a) * row_pitch), 0x00020000);
+    t.rb = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(p.B + static_cast<int64_t>(t.n0) * p.K), static_cast<short>(0),
+        static_cast<int32_t>(static_cast<uint32_t>(rows_b) * row_pitch), 0x00020000);
     return t;
 }
 
@@ -217,47 +249,238 @@ __device__ __forceinline__ void dma_slice(const Params &p, const Tile &t, int st
     for (int i = 0; i < CF::LOADS; ++i) dma_one<CF>(p, t, stage, kt, i, lds0, wave, lane, row_pitch);
 }
 
-// Work of one 16-deep K step, in a fixed issue order.  The wave owns one
-// SIMD's matrix pipe, so its instruction stream must keep an MFMA issuing
-// every 32 cycles: after MFMA t it issues its share of
-//   * the next step's fragment reads (spread over the first half of the
-//     step, so they have the second half to return), and
-//   * `dma_count` DMA instructions refilling the stage freed at the last
-//     barrier (spread over the whole step, so the vector-memory queue drains
-//     between them instead of stalling the wave).
-// sched_barrier(0) after each group keeps the compiler from regrouping them.
-template <class CF, bool READS, int DMA_PER_STEP>
+// Work of one MFMA K step, in a fixed issue order.  The wave owns one SIMD's
+// matrix pipe, so its instruction stream must keep an MFMA issuing back to
+// back.  The FM x FN blocks run row by row in boustrophedon order (each MFMA
+// shares an operand with the previous one), and other work rides between the
+// MFMAs, each item after a fixed MFMA:
+//   * the next step's B fragments (double-buffered) over the first half of
+//     the step, so they have the second half to return;
+//   * the next step's A fragment i (single-buffered) right after the last
+//     MFMA of row i, the earliest point its register is free;
+//   * NLD global DMA instructions over the whole step, so the vector-memory
+//     queue drains between them instead of stalling the wave.
+// sched_barrier(0) after each MFMA group keeps the compiler from regrouping.
+template <class CF, int NLD>
 struct Step {
-    template <class ReadFn, class DmaFn>
-    __device__ __forceinline__ static void run(f32x16_t (&acc)[CF::FM][CF::FN],
+    template <class RdA, class RdB, class Ld>
+    __device__ __forceinline__ static void run(typename CF::Acc (&acc)[CF::FM][CF::FN],
                                                const half8_t (&af)[CF::FM],
-                                               const half8_t (&bf)[CF::FN], ReadFn read,
-                                               DmaFn dma)
+                                               const half8_t (&bf)[CF::FN], RdA rda, RdB rdb,
+                                               Ld ld)
     {
         constexpr int NM = CF::FM * CF::FN;
-        constexpr int NR = CF::FM + CF::FN;
         constexpr int RSPAN = NM / 2 > 0 ? NM / 2 : 1;
 #pragma unroll
         for (int t = 0; t < NM; ++t) {
-            const int i = t / CF::FN, j = t % CF::FN;
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[j], af[i], acc[i][j], 0, 0, 0);
-            if constexpr (READS) {
-                const int r0 = t < RSPAN ? (t * NR) / RSPAN : NR;
-                const int r1 = t < RSPAN ? ((t + 1) * NR) / RSPAN : NR;
+            const int i = t / CF::FN;
+            const int j = (i & 1) ? CF::FN - 1 - t % CF::FN : t % CF::FN;
+            if constexpr (CF::MI == 32)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[j], af[i], acc[i][j], 0, 0, 0);
+            else
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bf[j], af[i], acc[i][j], 0, 0, 0);
 #pragma unroll
-                for (int r = r0; r < r1; ++r) read(r);
-            }
-            if constexpr (DMA_PER_STEP > 0) {
-                const int d0 = (t * DMA_PER_STEP) / NM;
-                const int d1 = ((t + 1) * DMA_PER_STEP) / NM;
+            for (int w = 0; w < CF::FN; ++w)
+                if ((w * RSPAN) / CF::FN == t) rdb(w);
+            if (t % CF::FN == CF::FN - 1) rda(i);
+            if constexpr (NLD > 0) {
 #pragma unroll
-                for (int d = d0; d < d1; ++d) dma(d);
+                for (int w = 0; w < NLD; ++w)
+                    if ((w * NM) / NLD == t) ld(w);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
     }
 };
 
+// Epilogue: RNE to fp16 and masked stores.  The MFMA's first operand holds B
+// rows, so a result block is a block of C^T: lane l holds, for block (i, j),
+// C[m][n .. n+3] with m = l % MI and, per group g of four accumulators,
+//   32x32: n = 8 g + 4 (l / 32)  (g = 0..3),   16x16: n = 4 (l / 16).
+template <class CF>
+__device__ __forceinline__ void store_tile(const Params &p, const Tile &t,
+                                           const typename CF::Acc (&acc)[CF::FM][CF::FN],
+                                           int wave_m, int wave_n, int lane)
+{
+    const int lrow = lane % CF::MI;
+    const int lq = lane / CF::MI;
+#pragma unroll
+    for (int i = 0; i < CF::FM; ++i) {
+        const int32_t m = t.m0 + wave_m * CF::TM + i * CF::MI + lrow;
+        if (m < p.M) {
+            uint16_t *crow = p.C + static_cast<int64_t>(m) * p.N;
+#pragma unroll
+            for (int j = 0; j < CF::FN; ++j) {
+#pragma unroll
+                for (int g = 0; g < CF::ACC_N / 4; ++g) {
+                    const int32_t n = t.n0 + wave_n * CF::TN + j * CF::MI +
+                                      (CF::MI == 32 ? g * 8 + lq * 4 : lq * 4);
+                    f32x4_t v;
+                    v.x = acc[i][j][4 * g + 0];
+                    v.y = acc[i][j][4 * g + 1];
+                    v.z = acc[i][j][4 * g + 2];
+                    v.w = acc[i][j][4 * g + 3];
+                    const half4_t h = __builtin_convertvector(v, half4_t);
+                    if (p.c_vec && n + 3 < p.N) {
+                        *reinterpret_cast<half4_t *>(crow + n) = h;
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (n + e < p.N) reinterpret_cast<_Float16 *>(crow)[n + e] = h[e];
+                    }
+                }
+            }
+        }
+    }
+}
+
+// Epilogue staged through LDS (the stage the next tile's prefill leaves
+// free).  Block row i of every wave -- WM * MI tile rows -- is written to LDS
+// as fp16, rows padded by 16 bytes so that the 32 rows one write instruction
+// touches fall in distinct banks; after a barrier every thread stores whole
+// row segments: 16 bytes per lane when C rows are 16-byte aligned, else one
+// half per lane with a wave covering 64 consecutive columns.  Masked at M and
+// N.  A barrier ends each block row before the buffer is reused.
+template <class CF>
+__device__ __forceinline__ void store_tile_staged(const Params &p, const Tile &t,
+                                                  const typename CF::Acc (&acc)[CF::FM][CF::FN],
+                                                  int wave_m, int wave_n, int lane, uint8_t *smem)
+{
+    constexpr int PITCH = CF::BN * 2 + 16;     // bytes per staged row
+    constexpr int CROWS = CF::WM * CF::MI;     // tile rows per block row
+    static_assert(CF::STAGED_OK, "staged block row fits one stage");
+    uint8_t *buf = smem + (CF::STAGES - 1) * CF::STAGE_BYTES;
+    const int lrow = lane % CF::MI;
+    const int lq = lane / CF::MI;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < CF::FM; ++i) {
+        const int srow = wave_m * CF::MI + lrow;   // staged row of this lane
+#pragma unroll
+        for (int j = 0; j < CF::FN; ++j) {
+#pragma unroll
+            for (int g = 0; g < CF::ACC_N / 4; ++g) {
+                const int ncol = wave_n * CF::TN + j * CF::MI + (CF::MI == 32 ? g * 8 + lq * 4 : lq * 4);
+                f32x4_t v;
+                v.x = acc[i][j][4 * g + 0];
+                v.y = acc[i][j][4 * g + 1];
+                v.z = acc[i][j][4 * g + 2];
+                v.w = acc[i][j][4 * g + 3];
+                *reinterpret_cast<half4_t *>(buf + srow * PITCH + ncol * 2) =
+                    __builtin_convertvector(v, half4_t);
+            }
+        }
+        lds_barrier();
+        if (p.c_vec16) {
+            constexpr int SEGS = CF::BN / 8;           // 16-byte segments per row
+            constexpr int ITEMS = CROWS * SEGS;
+#pragma unroll
+            for (int it = 0; it < (ITEMS + CF::THREADS - 1) / CF::THREADS; ++it) {
+                const int c = it * CF::THREADS + tid;
+                if (c < ITEMS) {
+                    const int sr = c / SEGS, sc = c % SEGS;
+                    const int32_t m = t.m0 + (sr / CF::MI) * CF::TM + i * CF::MI + sr % CF::MI;
+                    const int32_t n = t.n0 + sc * 8;
+                    if (m < p.M && n < p.N) {
+                        const half8_t h = *reinterpret_cast<const half8_t *>(buf + sr * PITCH + sc * 16);
+                        _Float16 *dst = reinterpret_cast<_Float16 *>(p.C) + static_cast<int64_t>(m) * p.N + n;
+                        if (n + 8 <= p.N) {
+                            *reinterpret_cast<half8_t *>(dst) = h;
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < 8; ++e)
+                                if (n + e < p.N) dst[e] = h[e];
+                        }
+                    }
+                }
+            }
+        } else {
+            // Rows are 2-byte aligned at best: store 4-byte pairs starting at
+            // the row's first 4-byte aligned column (lead = 0 or 1); a row
+            // with lead 1 also stores its column 0 alone (item BN / 2).
+            constexpr int ITEMS_ROW = CF::BN / 2 + 1;
+            constexpr int ITEMS = CROWS * ITEMS_ROW;
+            const uint32_t c_half = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p.C) >> 1);
+#pragma unroll 4
+            for (int it = 0; it < (ITEMS + CF::THREADS - 1) / CF::THREADS; ++it) {
+                const int c = it * CF::THREADS + tid;
+                if (c < ITEMS) {
+                    const int sr = c / ITEMS_ROW, q = c % ITEMS_ROW;
+                    const int32_t m = t.m0 + (sr / CF::MI) * CF::TM + i * CF::MI + sr % CF::MI;
+                    if (m < p.M) {
+                        const int64_t row0 = static_cast<int64_t>(m) * p.N + t.n0;   // element index of column 0
+                        const int lead = static_cast<int>((c_half + static_cast<uint32_t>(row0)) & 1u);
+                        const int col = q < CF::BN / 2 ? lead + 2 * q : 0;
+                        const bool pair = q < CF::BN / 2 && col + 1 < CF::BN && t.n0 + col + 1 < p.N;
+                        const bool single = !pair && (q < CF::BN / 2 ? (col < CF::BN && t.n0 + col < p.N)
+                                                                    : (lead == 1 && t.n0 < p.N));
+                        _Float16 *dst = reinterpret_cast<_Float16 *>(p.C) + row0 + col;
+                        const _Float16 *src = reinterpret_cast<const _Float16 *>(buf + sr * PITCH + col * 2);
+                        if (pair) {
+                            typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+                            half2_t h2;
+                            h2.x = src[0];
+                            h2.y = src[1];
+                            *reinterpret_cast<half2_t *>(dst) = h2;
+                        } else if (single) {
+                            dst[0] = src[0];
+                        }
+                    }
+                }
+            }
+        }
+        lds_barrier();
+    }
+}
+
+// Per-wave constants.
+template <class CF>
+struct WaveCtx {
+    int lane, wave, wave_m, wave_n;
+    uint32_t row_pitch, a_frag_base, b_frag_base;
+    // Fragment lane l reads row l % MI of an MI-row block, logical chunk
+    // kk * (MK / 8) + l / MI (8 consecutive k), physically XOR-swizzled.  The
+    // swizzle depends on the row mod 32, so a 16-row block at an odd multiple
+    // of 16 (parity 1) sees a different pattern.
+    uint32_t frag_off[2][CF::KK];
+
+    __device__ __forceinline__ WaveCtx(const Params &p)
+    {
+        lane = threadIdx.x & 63;
+        wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        wave_m = wave / CF::WN;
+        wave_n = wave - wave_m * CF::WN;
+        row_pitch = static_cast<uint32_t>(p.K) * 2u;
+        const int lrow = lane % CF::MI;
+        const int lq = lane / CF::MI;
+#pragma unroll
+        for (int par = 0; par < 2; ++par)
+#pragma unroll
+            for (int kk = 0; kk < CF::KK; ++kk) {
+                const int row32 = par * 16 + lrow;
+                const int chunk = kk * (CF::MK / 8) + lq;
+                frag_off[par][kk] = lrow * CF::ROW_BYTES +
+                                    ((chunk ^ chunk_swizzle<CF::CHUNKS>(CF::MI == 16 ? row32 : lrow)) * 16);
+            }
+        a_frag_base = wave_m * CF::TM * CF::ROW_BYTES;
+        b_frag_base = CF::A_BYTES + wave_n * CF::TN * CF::ROW_BYTES;
+    }
+};
+
+template <class CF>
+__device__ __forceinline__ void zero_acc(typename CF::Acc (&acc)[CF::FM][CF::FN])
+{
+#pragma unroll
+    for (int i = 0; i < CF::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < CF::FN; ++j)
+#pragma unroll
+            for (int e = 0; e < CF::ACC_N; ++e) acc[i][j][e] = 0.0f;
+}
+
+// ---------------------------------------------------------------------------
+// Kernel, direct-to-LDS fill
+// ---------------------------------------------------------------------------
 template <class CF>
 __global__ __launch_bounds__(CF::THREADS)
 __attribute__((amdgpu_waves_per_eu(CF::WAVES_PER_SIMD, CF::WAVES_PER_SIMD)))
@@ -267,71 +490,60 @@ void gemm_f16_nt_kernel(Params p)
     constexpr int S = CF::STAGES;
     constexpr int KK = CF::KK;
     constexpr int L = CF::LOADS;
-    constexpr int DPS = L / KK;                 // DMA instructions per 16-deep step
-    static_assert(L % KK == 0, "a slice's DMA splits evenly over its steps");
-    static_assert(S >= 3, "a refill streams over a whole slice: needs 3+ stages");
+    // The refill of slice kt + S - 1 streams over slice kt.  With 3+ stages it
+    // spreads over every step; with 2 the refilled slice is the very next one,
+    // so it must land before the barrier that ends slice kt: it goes into the
+    // first half of the slice's steps, leaving the rest for its latency.
+    static_assert(S >= 2, "double buffer at least");
+    static_assert(S >= 3 || KK >= 2, "two stages need a slice of 2+ steps");
+    constexpr int DSTEPS = CF::DSTEPS > 0 ? CF::DSTEPS : (S >= 3 ? KK : KK / 2);
+    static_assert(DSTEPS <= KK && (S >= 3 || DSTEPS < KK), "refill steps");
+    constexpr int DPS = (L + DSTEPS - 1) / DSTEPS;  // DMA instructions per such step (the last may have fewer)
     // outstanding DMA allowed when slice kt + 1 must have landed at the end of
-    // slice kt: slices kt+2 .. kt+S-2 and the first KK-1 parts of kt+S-1
-    constexpr int VM_STEADY = (S - 3) * L + (KK - 1) * DPS;
-    static_assert((S - 1) * L <= 63, "vmcnt counts at most 63 loads");
+    // slice kt: slices kt+2 .. kt+S-2 and the parts of kt+S-1 issued so far
+    // (none of which is slice kt + 1 when S >= 3; with S = 2 it is).
+    constexpr int ISSUED_BEFORE_BARRIER = (KK - 1) * DPS < L ? (KK - 1) * DPS : L;
+    constexpr int VM_STEADY = S >= 3 ? (S - 3) * L + ISSUED_BEFORE_BARRIER : 0;
+    static_assert((S - 1) * L <= 63 && VM_STEADY <= 63, "vmcnt counts at most 63 loads");
 
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wave_m = wave / CF::WN;
-    const int wave_n = wave - wave_m * CF::WN;
+    const WaveCtx<CF> w(p);
     const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(smem));
-    const uint32_t row_pitch = static_cast<uint32_t>(p.K) * 2u;   // bytes per A/B row
     const int KT = (p.K + CF::BK - 1) / CF::BK;
 
-    // Fragment lane l reads row (l % 32) of a 32-row block, logical chunk
-    // 2 * kk + l / 32 (8 consecutive k), physically XOR-swizzled.
-    const int r32 = lane & 31;
-    const int khalf = lane >> 5;
-    uint32_t frag_off[KK];
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-        frag_off[kk] = r32 * CF::ROW_BYTES +
-                       (((2 * kk + khalf) ^ chunk_swizzle<CF::CHUNKS>(r32)) * 16);
-    const uint32_t a_frag_base = wave_m * CF::TM * CF::ROW_BYTES;
-    const uint32_t b_frag_base = CF::A_BYTES + wave_n * CF::TN * CF::ROW_BYTES;
-
-    half8_t af[2][CF::FM], bf[2][CF::FN];
-    // read r of step kk of `stage` into buffer `buf`: r < FM -> A block r, else B block r - FM
-    auto read_frag = [&](int buf, int stage, int kk, int r) {
-        const uint32_t st = stage * CF::STAGE_BYTES + frag_off[kk];
-        if (r < CF::FM)
-            af[buf][r] = *reinterpret_cast<const half8_t *>(smem + st + a_frag_base +
-                                                             r * 32 * CF::ROW_BYTES);
-        else
-            bf[buf][r - CF::FM] = *reinterpret_cast<const half8_t *>(
-                smem + st + b_frag_base + (r - CF::FM) * 32 * CF::ROW_BYTES);
+    half8_t af[CF::FM], bf[2][CF::FN];
+    // A fragment i / B fragment j of step kk of `stage`
+    auto read_a = [&](int stage, int kk, int i) {
+        af[i] = *reinterpret_cast<const half8_t *>(smem + stage * CF::STAGE_BYTES +
+                                                    w.frag_off[i & 1][kk] + w.a_frag_base +
+                                                    i * CF::MI * CF::ROW_BYTES);
     };
-    auto no_dma = [](int) {};
+    auto read_b = [&](int buf, int stage, int kk, int j) {
+        bf[buf][j] = *reinterpret_cast<const half8_t *>(smem + stage * CF::STAGE_BYTES +
+                                                         w.frag_off[j & 1][kk] + w.b_frag_base +
+                                                         j * CF::MI * CF::ROW_BYTES);
+    };
+    auto none = [](int) {};
 
     int32_t slot = blockIdx.x;
     if (slot >= p.tiles) return;
-    Tile cur = make_tile<CF>(p, slot, row_pitch);
+    Tile cur = make_tile<CF>(p, slot, w.row_pitch);
     // Prefill: slices 0 .. S-2 into stages 0 .. S-2; stage S-1 is refilled
     // while slice 0 is computed.  Issued even when K has fewer slices (those
     // move no data), so every wait below counts the same instructions.
 #pragma unroll
-    for (int s = 0; s < S - 1; ++s) dma_slice<CF>(p, cur, s, s, lds0, wave, lane, row_pitch);
+    for (int s = 0; s < S - 1; ++s) dma_slice<CF>(p, cur, s, s, lds0, w.wave, w.lane, w.row_pitch);
 
     while (true) {
-        f32x16_t acc[CF::FM][CF::FN];
-#pragma unroll
-        for (int i = 0; i < CF::FM; ++i)
-#pragma unroll
-            for (int j = 0; j < CF::FN; ++j)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-
+        typename CF::Acc acc[CF::FM][CF::FN];
+        zero_acc<CF>(acc);
         if (KT > 0) {
             // slice 0 landed (slices 1 .. S-2 may still be in flight)
             wait_vmcnt<(S - 2) * L>();
             lds_barrier();
 #pragma unroll
-            for (int r = 0; r < CF::FM + CF::FN; ++r) read_frag(0, 0, 0, r);
+            for (int i = 0; i < CF::FM; ++i) read_a(0, 0, i);
+#pragma unroll
+            for (int j = 0; j < CF::FN; ++j) read_b(0, 0, 0, j);
         }
 
         // One branch-free loop over the slices.  Slice kt streams in the refill
@@ -347,22 +559,33 @@ void gemm_f16_nt_kernel(Params p)
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) {
                 auto dma = [&](int d) {
-                    dma_one<CF>(p, cur, pst, pkt, kk * DPS + d, lds0, wave, lane, row_pitch);
+                    if (kk * DPS + d < L)
+                        dma_one<CF>(p, cur, pst, pkt, kk * DPS + d, lds0, w.wave, w.lane, w.row_pitch);
                 };
                 if (kk + 1 < KK) {
-                    auto rf = [&](int r) { read_frag((kk + 1) & 1, rd, kk + 1, r); };
-                    Step<CF, true, DPS>::run(acc, af[kk & 1], bf[kk & 1], rf, dma);
+                    auto ra = [&](int i) { read_a(rd, kk + 1, i); };
+                    auto rb = [&](int j) { read_b((kk + 1) & 1, rd, kk + 1, j); };
+                    if (kk < DSTEPS)
+                        Step<CF, DPS>::run(acc, af, bf[kk & 1], ra, rb, dma);
+                    else
+                        Step<CF, 0>::run(acc, af, bf[kk & 1], ra, rb, none);
                 } else {
-                    // End of the slice (the last step's fragments are in
-                    // registers).  "full": slice kt + 1 has landed for this
-                    // wave, and after the barrier for every wave; "empty":
-                    // every wave has read all of stage rd, which receives
-                    // slice kt + S during the next slice.  After the last
-                    // slice the reads below fetch unused data (in bounds).
+                    // End of the slice (the last step's B fragments are in
+                    // registers; its A fragments were all read before any
+                    // of them is overwritten).  "full": slice kt + 1 has
+                    // landed for this wave, and after the barrier for every
+                    // wave; "empty": every wave has read all of stage rd,
+                    // which receives slice kt + S during the next slice.
+                    // After the last slice the reads below fetch unused data
+                    // (in bounds).
                     wait_vmcnt<VM_STEADY>();
                     lds_barrier();
-                    auto rf = [&](int r) { read_frag(0, rd_next, 0, r); };
-                    Step<CF, true, DPS>::run(acc, af[kk & 1], bf[kk & 1], rf, dma);
+                    auto ra = [&](int i) { read_a(rd_next, 0, i); };
+                    auto rb = [&](int j) { read_b(0, rd_next, 0, j); };
+                    if (kk < DSTEPS)
+                        Step<CF, DPS>::run(acc, af, bf[kk & 1], ra, rb, dma);
+                    else
+                        Step<CF, 0>::run(acc, af, bf[kk & 1], ra, rb, none);
                 }
             }
             pst = rd;
@@ -376,41 +599,18 @@ void gemm_f16_nt_kernel(Params p)
         const int32_t next = slot + p.grid;
         Tile nxt;
         if (next < p.tiles) {
-            nxt = make_tile<CF>(p, next, row_pitch);
+            nxt = make_tile<CF>(p, next, w.row_pitch);
 #pragma unroll
-            for (int s = 0; s < S - 1; ++s) dma_slice<CF>(p, nxt, s, s, lds0, wave, lane, row_pitch);
+            for (int s = 0; s < S - 1; ++s)
+                dma_slice<CF>(p, nxt, s, s, lds0, w.wave, w.lane, w.row_pitch);
         }
-
-        // ---- epilogue: RNE to fp16, masked stores --------------------------
-        // Lane l holds, for block (i, j) and group g, C[m][n .. n+3] with
-        // m = l % 32 and n = 8 g + 4 (l / 32) inside the block.
-#pragma unroll
-        for (int i = 0; i < CF::FM; ++i) {
-            const int32_t m = cur.m0 + wave_m * CF::TM + i * 32 + r32;
-            if (m < p.M) {
-                uint16_t *crow = p.C + static_cast<int64_t>(m) * p.N;
-#pragma unroll
-                for (int j = 0; j < CF::FN; ++j) {
-#pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const int32_t n = cur.n0 + wave_n * CF::TN + j * 32 + g * 8 + khalf * 4;
-                        f32x4_t v;
-                        v.x = acc[i][j][4 * g + 0];
-                        v.y = acc[i][j][4 * g + 1];
-                        v.z = acc[i][j][4 * g + 2];
-                        v.w = acc[i][j][4 * g + 3];
-                        const half4_t h = __builtin_convertvector(v, half4_t);
-                        if (p.c_vec && n + 3 < p.N) {
-                            *reinterpret_cast<half4_t *>(crow + n) = h;
-                        } else {
-#pragma unroll
-                            for (int e = 0; e < 4; ++e)
-                                if (n + e < p.N)
-                                    reinterpret_cast<_Float16 *>(crow)[n + e] = h[e];
-                        }
-                    }
-                }
-            }
+        if constexpr (CF::STAGED_OK) {
+            if (p.staged)
+                store_tile_staged<CF>(p, cur, acc, w.wave_m, w.wave_n, w.lane, smem);
+            else
+                store_tile<CF>(p, cur, acc, w.wave_m, w.wave_n, w.lane);
+        } else {
+            store_tile<CF>(p, cur, acc, w.wave_m, w.wave_n, w.lane);
         }
         if (next >= p.tiles) break;
         slot = next;
@@ -426,6 +626,7 @@ struct KernelEntry {
     int32_t block_m, block_n, block_k, waves, stages, lds_bytes, threads;
     int32_t default_swizzle;
     float rel_rate;   // relative MFMA rate per tile area, for the plan cost model
+    int32_t staged_ok;
 };
 
 template <class CF>
@@ -433,19 +634,27 @@ constexpr KernelEntry entry(int swizzle, float rate)
 {
     return KernelEntry{reinterpret_cast<const void *>(&gemm_f16_nt_kernel<CF>),
                        CF::BM, CF::BN, CF::BK, CF::WAVES, CF::STAGES, CF::LDS_BYTES, CF::THREADS,
-                       swizzle, rate};
+                       swizzle, rate, CF::STAGED_OK ? 1 : 0};
 }
 
 static const KernelEntry kKernels[] = {
-    entry<Cfg<256, 256, 32, 2, 2, 4>>(8, 1.00f),   // 0: 4 waves of 128x128, 4 stages of K 32
+    entry<Cfg<256, 256, 32, 2, 2, 4>>(8, 0.00f),   // 0: 4 waves of 128x128, 4 stages of K 32
     entry<Cfg<256, 256, 32, 2, 2, 5>>(8, 0.00f),   // 1: the same, 5 stages
-    entry<Cfg<256, 128, 64, 2, 2, 3>>(8, 0.90f),   // 2: 4 waves of 128x64, 3 stages of K 64
+    entry<Cfg<256, 128, 64, 2, 2, 3>>(8, 0.85f),   // 2: 4 waves of 128x64, 3 stages of K 64
     entry<Cfg<256, 128, 32, 2, 2, 6>>(8, 0.00f),   // 3: the same tile, 6 stages of K 32
-    entry<Cfg<128, 128, 64, 2, 2, 4>>(8, 0.80f),   // 4: 4 waves of 64x64, 4 stages
+    entry<Cfg<128, 128, 64, 2, 2, 4>>(8, 0.75f),   // 4: 4 waves of 64x64, 4 stages
     entry<Cfg<128, 64, 64, 2, 1, 6>>(8, 0.60f),    // 5: 2 waves of 64x64, 6 stages
     entry<Cfg<256, 256, 32, 2, 4, 4>>(8, 0.00f),   // 6: 8 waves of 128x64, 4 stages of K 32
     entry<Cfg<256, 256, 32, 4, 2, 4>>(8, 0.00f),   // 7: 8 waves of 64x128, 4 stages of K 32
     entry<Cfg<256, 256, 32, 2, 4, 5>>(8, 0.00f),   // 8: 8 waves of 128x64, 5 stages of K 32
+    entry<Cfg<256, 256, 64, 2, 2, 2>>(8, 1.00f),   // 9: 4 waves of 128x128, 2 stages of K 64
+    entry<Cfg<256, 256, 64, 2, 4, 2>>(8, 0.00f),   // 10: 8 waves of 128x64, 2 stages of K 64
+    entry<Cfg<256, 256, 64, 2, 2, 2, 16>>(8, 0.00f),   // 11: as 9 with 16x16x32 MFMAs
+    entry<Cfg<256, 128, 64, 2, 2, 3, 16>>(8, 0.00f),   // 12: as 2 with 16x16x32 MFMAs
+    entry<Cfg<192, 256, 64, 2, 2, 2>>(8, 0.80f),   // 13: 4 waves of 96x128, 2 stages of K 64
+    entry<Cfg<256, 192, 64, 2, 2, 2>>(8, 0.82f),   // 14: 4 waves of 128x96, 2 stages of K 64
+    entry<Cfg<192, 256, 32, 2, 2, 5>>(8, 0.00f),   // 15: 4 waves of 96x128, 5 stages of K 32
+    entry<Cfg<256, 192, 32, 2, 2, 5>>(8, 0.00f),   // 16: 4 waves of 128x96, 5 stages of K 32
 };
 constexpr int kNumKernels = sizeof(kKernels) / sizeof(kKernels[0]);
 
@@ -495,10 +704,21 @@ static void fill_info(int id, gemm_f16_nt_plan_t *out)
     out->xcds = DEFAULT_XCDS;
 }
 
+// Epilogue policy: stage C through LDS whenever the configuration has room
+// for it (row-contiguous stores measured faster than direct stores from the
+// MFMA layout for aligned and unaligned C alike).
+static int32_t choose_epilogue(int id, int64_t N, bool c_aligned8)
+{
+    (void)N;
+    (void)c_aligned8;
+    return kKernels[id].staged_ok ? 1 : 0;
+}
+
 static void make_plan(int id, int64_t M, int64_t N, int32_t num_cus, int32_t swizzle,
                       int32_t grid, gemm_f16_nt_plan_t *out)
 {
     fill_info(id, out);
+    out->epilogue = choose_epilogue(id, N, true);
     out->tiles_m = static_cast<int32_t>(cdiv(M, out->block_m));
     out->tiles_n = static_cast<int32_t>(cdiv(N, out->block_n));
     out->tiles = static_cast<int64_t>(out->tiles_m) * out->tiles_n;
@@ -570,6 +790,8 @@ static int launch(const gemm_f16_nt_plan_t &plan, int64_t M, int64_t N, int64_t 
     p.grid = plan.grid;
     p.xcds = plan.xcds;
     p.c_vec = (N % 4 == 0 && reinterpret_cast<uintptr_t>(C) % 8 == 0) ? 1 : 0;
+    p.c_vec16 = (N % 8 == 0 && reinterpret_cast<uintptr_t>(C) % 16 == 0) ? 1 : 0;
+    p.staged = plan.epilogue;
     const KernelEntry &e = kKernels[plan.config_id];
     void *args[] = {&p};
     hipError_t err = hipLaunchKernel(e.fn, dim3(plan.grid), dim3(e.threads), args, 0, stream);
@@ -579,7 +801,8 @@ static int launch(const gemm_f16_nt_plan_t &plan, int64_t M, int64_t N, int64_t 
 }
 
 static int run(int64_t M, int64_t N, int64_t K, const void *A, const void *B, void *C,
-               hipStream_t stream, int32_t config_id, int32_t swizzle, int32_t grid)
+               hipStream_t stream, int32_t config_id, int32_t swizzle, int32_t grid,
+               int32_t epilogue)
 {
     const int v = validate(M, N, K, A, B, C);
     if (v != GEMM_F16_OK) return v;
@@ -591,6 +814,12 @@ static int run(int64_t M, int64_t N, int64_t K, const void *A, const void *B, vo
     const int id = config_id >= 0 ? config_id : choose_config(M, N, cus);
     gemm_f16_nt_plan_t plan;
     make_plan(id, M, N, cus, swizzle, grid, &plan);
+    if (epilogue < 0) {
+        plan.epilogue = choose_epilogue(id, N, reinterpret_cast<uintptr_t>(C) % 8 == 0);
+    } else {
+        if (epilogue > 1 || (epilogue == 1 && !kKernels[id].staged_ok)) return GEMM_F16_UNSUPPORTED;
+        plan.epilogue = epilogue;
+    }
     return launch(plan, M, N, K, A, B, C, stream);
 }
 
@@ -601,15 +830,16 @@ using namespace gemm_f16;
 extern "C" int gemm_f16_nt(int64_t M, int64_t N, int64_t K, const void *A, const void *B,
                            void *C, hipStream_t stream)
 {
-    return run(M, N, K, A, B, C, stream, -1, 0, 0);
+    return run(M, N, K, A, B, C, stream, -1, 0, 0, -1);
 }
 
 extern "C" int gemm_f16_nt_with_config(int64_t M, int64_t N, int64_t K, const void *A,
                                        const void *B, void *C, hipStream_t stream,
-                                       int32_t config_id, int32_t swizzle, int32_t grid)
+                                       int32_t config_id, int32_t swizzle, int32_t grid,
+                                       int32_t epilogue)
 {
-    if (config_id < 0) return GEMM_F16_INVALID_ARG;
-    return run(M, N, K, A, B, C, stream, config_id, swizzle, grid);
+    return run(M, N, K, A, B, C, stream, config_id < 0 ? -1 : config_id, swizzle, grid,
+               epilogue);
 }
 
 extern "C" const char *gemm_f16_nt_status_string(int status)

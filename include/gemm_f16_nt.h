@@ -94,6 +94,8 @@ typedef struct {
     int64_t tiles;       /* tiles_m * tiles_n                              */
     int32_t lds_bytes;   /* LDS used by one workgroup                      */
     int32_t xcds;        /* XCD count the tile order is arranged for       */
+    int32_t epilogue;    /* 0: stores straight from the MFMA registers;
+                            1: C staged through LDS for row-contiguous stores */
 } gemm_f16_nt_plan_t;
 
 int gemm_f16_nt_plan(int64_t M, int64_t N, int64_t K, int32_t num_cus,
@@ -106,17 +108,21 @@ int gemm_f16_nt_num_configs(void);
 int gemm_f16_nt_config_info(int32_t config_id, gemm_f16_nt_plan_t *info);
 
 /*
- * gemm_f16_nt with an explicit kernel configuration, raster group width and
- * persistent grid size (grid <= 0: one workgroup per compute unit, capped by
- * the tile count; swizzle <= 0: the configuration's default).  Same
+ * gemm_f16_nt with an explicit kernel configuration, raster group width,
+ * persistent grid size and epilogue (config_id < 0: the planner's choice;
+ * grid <= 0: one workgroup per compute unit, capped by the tile count;
+ * swizzle <= 0: the configuration's default;
+ * epilogue < 0: the library's choice, 0: direct stores, 1: staged through
+ * LDS -- GEMM_F16_UNSUPPORTED if the configuration has no room for it).  Same
  * semantics, ownership and status codes as gemm_f16_nt; the result is
- * identical for every configuration, swizzle and grid, because the K order of
- * each element does not depend on them.  For tests and tuning sweeps.
+ * identical for every configuration, swizzle, grid and epilogue, because the
+ * K order of each element does not depend on them.  For tests and tuning
+ * sweeps.
  */
 int gemm_f16_nt_with_config(int64_t M, int64_t N, int64_t K,
                             const void *A, const void *B, void *C,
                             hipStream_t stream, int32_t config_id,
-                            int32_t swizzle, int32_t grid);
+                            int32_t swizzle, int32_t grid, int32_t epilogue);
 
 /*
  * The tile order the kernel walks (Tilus tutorial "Hopper matmul", page

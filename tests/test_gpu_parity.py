@@ -35,19 +35,27 @@ def _say(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def run_gpu(g, a, b, config=None, swizzle=0, grid=0):
+def run_gpu(g, a, b, config=None, swizzle=0, grid=0, epilogue=-1, c_offset=0):
+    """C = a @ b.T on the GPU through the C ABI.  c_offset shifts C by that
+    many fp16 elements inside a larger buffer (to test C alignment)."""
     import torch
 
     _say(f"  gpu gemm {a.shape[0]}x{b.shape[0]}x{a.shape[1]} config={config} "
-         f"swizzle={swizzle} grid={grid}")
+         f"swizzle={swizzle} grid={grid} epilogue={epilogue} c_offset={c_offset}")
     dev = torch.device("cuda:0")
     ta = torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     tb = torch.from_numpy(np.ascontiguousarray(b)).to(dev)
+    m, n = a.shape[0], b.shape[0]
     # poison C so that an element the kernel never writes cannot pass
-    out = torch.full((a.shape[0], b.shape[0]), float("nan"), dtype=torch.float16, device=dev)
-    g.gemm_nt(ta, tb, out=out, config=config, swizzle=swizzle, grid=grid)
+    flat = torch.full((m * n + c_offset + 8,), float("nan"), dtype=torch.float16, device=dev)
+    out = flat[c_offset:c_offset + m * n].view(m, n)
+    g.gemm_nt(ta, tb, out=out, config=config, swizzle=swizzle, grid=grid, epilogue=epilogue)
     torch.cuda.synchronize()
-    return out.cpu().numpy()
+    host = flat.cpu().numpy()
+    # nothing outside C may be touched
+    assert np.isnan(host[:c_offset].astype(np.float32)).all()
+    assert np.isnan(host[c_offset + m * n:].astype(np.float32)).all()
+    return host[c_offset:c_offset + m * n].reshape(m, n)
 
 
 def num_configs(g):
@@ -88,12 +96,17 @@ def test_parity_every_config(g, oracle_mod, shape):
     ref = oracle_mod.gemm(a, b)
     first = None
     for cid in range(num_configs(g)):
-        got = run_gpu(g, a, b, config=cid)
-        assert_within_tolerance(got, ref, f"{shape} config {cid}")
-        if first is None:
-            first = got
-        else:
-            assert_bit_exact(got, first, f"{shape} config {cid} vs config 0")
+        for epi in (0, 1):
+            try:
+                got = run_gpu(g, a, b, config=cid, epilogue=epi)
+            except g.GemmError as e:
+                assert epi == 1 and e.status == g.UNSUPPORTED   # no room to stage C
+                continue
+            assert_within_tolerance(got, ref, f"{shape} config {cid} epilogue {epi}")
+            if first is None:
+                first = got
+            else:
+                assert_bit_exact(got, first, f"{shape} config {cid} epilogue {epi} vs first")
 
 
 @pytest.mark.parametrize("cid", [0, 1, 2, 3, 4, 5])
@@ -115,6 +128,16 @@ def test_edge_m_n(g, oracle_mod, cid):
             a, b = workloads.make_inputs(m, n, 72, "normal", 0.1, seed=m * 1000 + n)
             got = run_gpu(g, a, b, config=cid)
             assert_within_tolerance(got, oracle_mod.gemm(a, b), f"{m}x{n}x72 config {cid}")
+
+
+@pytest.mark.parametrize("c_offset", [1, 2, 3, 4])
+@pytest.mark.parametrize("epi", [0, 1])
+def test_unaligned_c(g, oracle_mod, c_offset, epi):
+    """C only 2-, 4- or 8-byte aligned, and odd N: the epilogue's narrower
+    store paths; every element written once, nothing outside C touched."""
+    a, b = workloads.make_inputs(300, 261, 136, "normal", 0.1, seed=c_offset)
+    got = run_gpu(g, a, b, config=9, epilogue=epi, c_offset=c_offset)
+    assert_within_tolerance(got, oracle_mod.gemm(a, b), f"c_offset {c_offset} epilogue {epi}")
 
 
 def test_k_zero_writes_positive_zero(g):
