@@ -144,8 +144,6 @@ struct Params {
     int32_t M, N, K;
     int32_t tiles_m, tiles_n, tiles;
     int32_t swizzle, grid, xcds;
-    int32_t c_vec;   // 1: C rows allow 8-byte stores (C 8-byte aligned, N % 4 == 0)
-    int32_t c_vec16; // 1: C rows allow 16-byte stores (C 16-byte aligned, N % 8 == 0)
     int32_t staged;  // 1: stage C through LDS for row-contiguous stores
 };
 
@@ -321,8 +319,8 @@ __device__ __forceinline__ void store_tile(const Params &p, const Tile &t,
                     v.z = acc[i][j][4 * g + 2];
                     v.w = acc[i][j][4 * g + 3];
                     const half4_t h = __builtin_convertvector(v, half4_t);
-                    if (p.c_vec && n + 3 < p.N) {
-                        *reinterpret_cast<half4_t *>(crow + n) = h;
+                    if (n + 3 < p.N) {
+                        __builtin_memcpy(crow + n, &h, 8);   // any 2-byte alignment
                     } else {
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
@@ -337,10 +335,9 @@ __device__ __forceinline__ void store_tile(const Params &p, const Tile &t,
 // Epilogue staged through LDS (the stage the next tile's prefill leaves
 // free).  Block row i of every wave -- WM * MI tile rows -- is written to LDS
 // as fp16, rows padded by 16 bytes so that the 32 rows one write instruction
-// touches fall in distinct banks; after a barrier every thread stores whole
-// row segments: 16 bytes per lane when C rows are 16-byte aligned, else one
-// half per lane with a wave covering 64 consecutive columns.  Masked at M and
-// N.  A barrier ends each block row before the buffer is reused.
+// touches fall in distinct banks; after a barrier every thread stores 16-byte
+// row segments, a wave covering 512 consecutive columns.  Masked at M and N.
+// A barrier ends each block row before the buffer is reused.
 template <class CF>
 __device__ __forceinline__ void store_tile_staged(const Params &p, const Tile &t,
                                                   const typename CF::Acc (&acc)[CF::FM][CF::FN],
@@ -371,60 +368,27 @@ __device__ __forceinline__ void store_tile_staged(const Params &p, const Tile &t
             }
         }
         lds_barrier();
-        if (p.c_vec16) {
-            constexpr int SEGS = CF::BN / 8;           // 16-byte segments per row
-            constexpr int ITEMS = CROWS * SEGS;
+        // 16 bytes per lane at any 2-byte alignment: memcpy lets the compiler
+        // emit one 16-byte store, which the target's unaligned-access mode
+        // allows; only the segment crossing N is stored element by element.
+        constexpr int SEGS = CF::BN / 8;           // 8-column segments per row
+        constexpr int ITEMS = CROWS * SEGS;
 #pragma unroll
-            for (int it = 0; it < (ITEMS + CF::THREADS - 1) / CF::THREADS; ++it) {
-                const int c = it * CF::THREADS + tid;
-                if (c < ITEMS) {
-                    const int sr = c / SEGS, sc = c % SEGS;
-                    const int32_t m = t.m0 + (sr / CF::MI) * CF::TM + i * CF::MI + sr % CF::MI;
-                    const int32_t n = t.n0 + sc * 8;
-                    if (m < p.M && n < p.N) {
-                        const half8_t h = *reinterpret_cast<const half8_t *>(buf + sr * PITCH + sc * 16);
-                        _Float16 *dst = reinterpret_cast<_Float16 *>(p.C) + static_cast<int64_t>(m) * p.N + n;
-                        if (n + 8 <= p.N) {
-                            *reinterpret_cast<half8_t *>(dst) = h;
-                        } else {
+        for (int it = 0; it < (ITEMS + CF::THREADS - 1) / CF::THREADS; ++it) {
+            const int c = it * CF::THREADS + tid;
+            if (c < ITEMS) {
+                const int sr = c / SEGS, sc = c % SEGS;
+                const int32_t m = t.m0 + (sr / CF::MI) * CF::TM + i * CF::MI + sr % CF::MI;
+                const int32_t n = t.n0 + sc * 8;
+                if (m < p.M && n < p.N) {
+                    const half8_t h = *reinterpret_cast<const half8_t *>(buf + sr * PITCH + sc * 16);
+                    _Float16 *dst = reinterpret_cast<_Float16 *>(p.C) + static_cast<int64_t>(m) * p.N + n;
+                    if (n + 8 <= p.N) {
+                        __builtin_memcpy(dst, &h, 16);
+                    } else {
 #pragma unroll
-                            for (int e = 0; e < 8; ++e)
-                                if (n + e < p.N) dst[e] = h[e];
-                        }
-                    }
-                }
-            }
-        } else {
-            // Rows are 2-byte aligned at best: store 4-byte pairs starting at
-            // the row's first 4-byte aligned column (lead = 0 or 1); a row
-            // with lead 1 also stores its column 0 alone (item BN / 2).
-            constexpr int ITEMS_ROW = CF::BN / 2 + 1;
-            constexpr int ITEMS = CROWS * ITEMS_ROW;
-            const uint32_t c_half = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p.C) >> 1);
-#pragma unroll 4
-            for (int it = 0; it < (ITEMS + CF::THREADS - 1) / CF::THREADS; ++it) {
-                const int c = it * CF::THREADS + tid;
-                if (c < ITEMS) {
-                    const int sr = c / ITEMS_ROW, q = c % ITEMS_ROW;
-                    const int32_t m = t.m0 + (sr / CF::MI) * CF::TM + i * CF::MI + sr % CF::MI;
-                    if (m < p.M) {
-                        const int64_t row0 = static_cast<int64_t>(m) * p.N + t.n0;   // element index of column 0
-                        const int lead = static_cast<int>((c_half + static_cast<uint32_t>(row0)) & 1u);
-                        const int col = q < CF::BN / 2 ? lead + 2 * q : 0;
-                        const bool pair = q < CF::BN / 2 && col + 1 < CF::BN && t.n0 + col + 1 < p.N;
-                        const bool single = !pair && (q < CF::BN / 2 ? (col < CF::BN && t.n0 + col < p.N)
-                                                                    : (lead == 1 && t.n0 < p.N));
-                        _Float16 *dst = reinterpret_cast<_Float16 *>(p.C) + row0 + col;
-                        const _Float16 *src = reinterpret_cast<const _Float16 *>(buf + sr * PITCH + col * 2);
-                        if (pair) {
-                            typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-                            half2_t h2;
-                            h2.x = src[0];
-                            h2.y = src[1];
-                            *reinterpret_cast<half2_t *>(dst) = h2;
-                        } else if (single) {
-                            dst[0] = src[0];
-                        }
+                        for (int e = 0; e < 8; ++e)
+                            if (n + e < p.N) dst[e] = h[e];
                     }
                 }
             }
@@ -789,8 +753,6 @@ static int launch(const gemm_f16_nt_plan_t &plan, int64_t M, int64_t N, int64_t 
     p.swizzle = plan.swizzle;
     p.grid = plan.grid;
     p.xcds = plan.xcds;
-    p.c_vec = (N % 4 == 0 && reinterpret_cast<uintptr_t>(C) % 8 == 0) ? 1 : 0;
-    p.c_vec16 = (N % 8 == 0 && reinterpret_cast<uintptr_t>(C) % 16 == 0) ? 1 : 0;
     p.staged = plan.epilogue;
     const KernelEntry &e = kKernels[plan.config_id];
     void *args[] = {&p};
