@@ -93,8 +93,12 @@ __host__ __device__ constexpr int chunk_swizzle(int r)
 // MI_ picks the MFMA: 32 -> v_mfma_f32_32x32x16_f16 (16 accumulators per lane
 // per block), 16 -> v_mfma_f32_16x16x32_f16 (4 per block: half the
 // accumulator register traffic per flop).
+// DX_ (two stages only): how many of a slice's DMA instructions are issued
+// early, during the last step of the slice two before it, right after the
+// barrier that frees their stage; the rest go out during the slice before.
+// ADB_: double-buffer the A fragments as well as the B fragments.
 template <int BM_, int BN_, int BK_, int WM_, int WN_, int STAGES_, int MI_ = 32,
-          int DSTEPS_ = 0>
+          int DSTEPS_ = 0, int DX_ = 0, int ADB_ = 0>
 struct Cfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, STAGES = STAGES_;
     static constexpr int MI = MI_;               // MFMA block edge (M and N)
@@ -103,6 +107,8 @@ struct Cfg {
     // steps of a slice that carry refill DMA (0: every step with 3+ stages,
     // the first half with 2)
     static constexpr int DSTEPS = DSTEPS_;
+    static constexpr int DX = DX_;
+    static constexpr bool ADB = ADB_ != 0;
     typedef typename AccVec<ACC_N>::type Acc;
     static constexpr int WAVES = WM * WN;
     static constexpr int THREADS = 64 * WAVES;
@@ -135,6 +141,10 @@ struct Cfg {
     static_assert(STAGES >= 2, "need at least a double buffer");
     static_assert(LDS_BYTES <= LDS_LIMIT, "LDS ring exceeds 160 KB");
     static_assert((STAGES - 1) * LOADS <= 63, "vmcnt counts at most 63 loads");
+    static_assert(DX == 0 || (STAGES == 2 && DX <= LOADS), "early refill needs exactly two stages");
+    // the 16x16x32 MFMAs are hand-issued (see Step): an accumulator must not
+    // feed the MFMA right after the one that wrote it
+    static_assert(MI == 32 || FM * FN >= 4, "16x16 blocks per wave");
 };
 
 struct Params {
@@ -254,11 +264,20 @@ __device__ __forceinline__ void dma_slice(const Params &p, const Tile &t, int st
 // MFMAs, each item after a fixed MFMA:
 //   * the next step's B fragments (double-buffered) over the first half of
 //     the step, so they have the second half to return;
-//   * the next step's A fragment i (single-buffered) right after the last
-//     MFMA of row i, the earliest point its register is free;
+//   * the next step's A fragment i right after the last MFMA of row i, the
+//     earliest point its register is free (single-buffered), or, when A is
+//     double-buffered, over the first half of the step like B;
 //   * NLD global DMA instructions over the whole step, so the vector-memory
 //     queue drains between them instead of stalling the wave.
 // sched_barrier(0) after each MFMA group keeps the compiler from regrouping.
+//
+// The 16x16x32 MFMA goes through inline assembly with its accumulator bound
+// to the AGPR file ("a"): a wave's 128x128 block needs all 256 AGPRs, and
+// with the builtin the register allocator splits the accumulators between
+// the two files and spills.  The compiler then cannot see these MFMAs, so the
+// kernel supplies the wait states the ISA requires around them itself: after
+// the accumulators are zeroed (VALU write, then MFMA reads them) and before
+// they are read back (MFMA write, then VALU read); see the kernel body.
 template <class CF, int NLD>
 struct Step {
     template <class RdA, class RdB, class Ld>
@@ -276,11 +295,18 @@ struct Step {
             if constexpr (CF::MI == 32)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[j], af[i], acc[i][j], 0, 0, 0);
             else
-                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bf[j], af[i], acc[i][j], 0, 0, 0);
+                asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0"
+                             : "+a"(acc[i][j]) : "v"(bf[j]), "v"(af[i]));
 #pragma unroll
             for (int w = 0; w < CF::FN; ++w)
                 if ((w * RSPAN) / CF::FN == t) rdb(w);
-            if (t % CF::FN == CF::FN - 1) rda(i);
+            if constexpr (CF::ADB) {
+#pragma unroll
+                for (int w = 0; w < CF::FM; ++w)
+                    if ((w * RSPAN) / CF::FM == t) rda(w);
+            } else {
+                if (t % CF::FN == CF::FN - 1) rda(i);
+            }
             if constexpr (NLD > 0) {
 #pragma unroll
                 for (int w = 0; w < NLD; ++w)
@@ -291,13 +317,24 @@ struct Step {
     }
 };
 
+// For the hand-issued 16x16x32 MFMAs: an empty volatile statement that
+// "redefines" an accumulator in the AGPR file.  Volatile statements keep their
+// order, so every read of the accumulator after it comes after the wait states
+// the kernel issues once the last MFMA is out, and reads of one block are not
+// hoisted ahead of the stores of the block before.
+template <class CF>
+__device__ __forceinline__ void acc_fence(typename CF::Acc &a)
+{
+    if constexpr (CF::MI == 16) asm volatile("" : "+a"(a));
+}
+
 // Epilogue: RNE to fp16 and masked stores.  The MFMA's first operand holds B
 // rows, so a result block is a block of C^T: lane l holds, for block (i, j),
 // C[m][n .. n+3] with m = l % MI and, per group g of four accumulators,
 //   32x32: n = 8 g + 4 (l / 32)  (g = 0..3),   16x16: n = 4 (l / 16).
 template <class CF>
 __device__ __forceinline__ void store_tile(const Params &p, const Tile &t,
-                                           const typename CF::Acc (&acc)[CF::FM][CF::FN],
+                                           typename CF::Acc (&acc)[CF::FM][CF::FN],
                                            int wave_m, int wave_n, int lane)
 {
     const int lrow = lane % CF::MI;
@@ -309,6 +346,7 @@ __device__ __forceinline__ void store_tile(const Params &p, const Tile &t,
             uint16_t *crow = p.C + static_cast<int64_t>(m) * p.N;
 #pragma unroll
             for (int j = 0; j < CF::FN; ++j) {
+                acc_fence<CF>(acc[i][j]);
 #pragma unroll
                 for (int g = 0; g < CF::ACC_N / 4; ++g) {
                     const int32_t n = t.n0 + wave_n * CF::TN + j * CF::MI +
@@ -340,7 +378,7 @@ __device__ __forceinline__ void store_tile(const Params &p, const Tile &t,
 // A barrier ends each block row before the buffer is reused.
 template <class CF>
 __device__ __forceinline__ void store_tile_staged(const Params &p, const Tile &t,
-                                                  const typename CF::Acc (&acc)[CF::FM][CF::FN],
+                                                  typename CF::Acc (&acc)[CF::FM][CF::FN],
                                                   int wave_m, int wave_n, int lane, uint8_t *smem)
 {
     constexpr int PITCH = CF::BN * 2 + 16;     // bytes per staged row
@@ -355,6 +393,7 @@ __device__ __forceinline__ void store_tile_staged(const Params &p, const Tile &t
         const int srow = wave_m * CF::MI + lrow;   // staged row of this lane
 #pragma unroll
         for (int j = 0; j < CF::FN; ++j) {
+            acc_fence<CF>(acc[i][j]);
 #pragma unroll
             for (int g = 0; g < CF::ACC_N / 4; ++g) {
                 const int ncol = wave_n * CF::TN + j * CF::MI + (CF::MI == 32 ? g * 8 + lq * 4 : lq * 4);
@@ -462,7 +501,12 @@ void gemm_f16_nt_kernel(Params p)
     static_assert(S >= 3 || KK >= 2, "two stages need a slice of 2+ steps");
     constexpr int DSTEPS = CF::DSTEPS > 0 ? CF::DSTEPS : (S >= 3 ? KK : KK / 2);
     static_assert(DSTEPS <= KK && (S >= 3 || DSTEPS < KK), "refill steps");
-    constexpr int DPS = (L + DSTEPS - 1) / DSTEPS;  // DMA instructions per such step (the last may have fewer)
+    // With DX > 0 (two stages), DX instructions of the refill of slice kt + 2
+    // go out during the last step of slice kt, right after the barrier that
+    // frees its stage; the remaining LY during slice kt + 1 as above.
+    constexpr int DX = CF::DX;
+    constexpr int LY = L - DX;
+    constexpr int DPS = (LY + DSTEPS - 1) / DSTEPS;  // DMA instructions per such step (the last may have fewer)
     // outstanding DMA allowed when slice kt + 1 must have landed at the end of
     // slice kt: slices kt+2 .. kt+S-2 and the parts of kt+S-1 issued so far
     // (none of which is slice kt + 1 when S >= 3; with S = 2 it is).
@@ -474,10 +518,10 @@ void gemm_f16_nt_kernel(Params p)
     const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(smem));
     const int KT = (p.K + CF::BK - 1) / CF::BK;
 
-    half8_t af[CF::FM], bf[2][CF::FN];
-    // A fragment i / B fragment j of step kk of `stage`
-    auto read_a = [&](int stage, int kk, int i) {
-        af[i] = *reinterpret_cast<const half8_t *>(smem + stage * CF::STAGE_BYTES +
+    half8_t af[CF::ADB ? 2 : 1][CF::FM], bf[2][CF::FN];
+    // A fragment i / B fragment j of step kk of `stage`, into buffer `buf`
+    auto read_a = [&](int buf, int stage, int kk, int i) {
+        af[buf][i] = *reinterpret_cast<const half8_t *>(smem + stage * CF::STAGE_BYTES +
                                                     w.frag_off[i & 1][kk] + w.a_frag_base +
                                                     i * CF::MI * CF::ROW_BYTES);
     };
@@ -500,14 +544,30 @@ void gemm_f16_nt_kernel(Params p)
     while (true) {
         typename CF::Acc acc[CF::FM][CF::FN];
         zero_acc<CF>(acc);
+        if constexpr (CF::MI == 16) {
+            // the zeros are in the AGPRs before the wait states that separate
+            // their (VALU) writes from the first MFMA reading them
+#pragma unroll
+            for (int i = 0; i < CF::FM; ++i)
+#pragma unroll
+                for (int j = 0; j < CF::FN; ++j) acc_fence<CF>(acc[i][j]);
+            asm volatile("s_nop 4");
+        }
         if (KT > 0) {
             // slice 0 landed (slices 1 .. S-2 may still be in flight)
             wait_vmcnt<(S - 2) * L>();
             lds_barrier();
 #pragma unroll
-            for (int i = 0; i < CF::FM; ++i) read_a(0, 0, i);
+            for (int i = 0; i < CF::FM; ++i) read_a(0, 0, 0, i);
 #pragma unroll
             for (int j = 0; j < CF::FN; ++j) read_b(0, 0, 0, j);
+            // early part of slice 1, into stage 1: free, since the previous
+            // tile's epilogue ended with a barrier
+            if constexpr (DX > 0) {
+#pragma unroll
+                for (int d = 0; d < DX; ++d)
+                    dma_one<CF>(p, cur, 1, 1, d, lds0, w.wave, w.lane, w.row_pitch);
+            }
         }
 
         // One branch-free loop over the slices.  Slice kt streams in the refill
@@ -523,16 +583,22 @@ void gemm_f16_nt_kernel(Params p)
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) {
                 auto dma = [&](int d) {
-                    if (kk * DPS + d < L)
-                        dma_one<CF>(p, cur, pst, pkt, kk * DPS + d, lds0, w.wave, w.lane, w.row_pitch);
+                    if (kk * DPS + d < LY)
+                        dma_one<CF>(p, cur, pst, pkt, DX + kk * DPS + d, lds0, w.wave, w.lane,
+                                    w.row_pitch);
+                };
+                // early part of slice kt + 2, into stage rd, which the barrier
+                // of this slice's last step has just freed
+                auto dma_early = [&](int d) {
+                    dma_one<CF>(p, cur, rd, kt + 2, d, lds0, w.wave, w.lane, w.row_pitch);
                 };
                 if (kk + 1 < KK) {
-                    auto ra = [&](int i) { read_a(rd, kk + 1, i); };
+                    auto ra = [&](int i) { read_a(CF::ADB ? (kk + 1) & 1 : 0, rd, kk + 1, i); };
                     auto rb = [&](int j) { read_b((kk + 1) & 1, rd, kk + 1, j); };
                     if (kk < DSTEPS)
-                        Step<CF, DPS>::run(acc, af, bf[kk & 1], ra, rb, dma);
+                        Step<CF, DPS>::run(acc, af[CF::ADB ? kk & 1 : 0], bf[kk & 1], ra, rb, dma);
                     else
-                        Step<CF, 0>::run(acc, af, bf[kk & 1], ra, rb, none);
+                        Step<CF, 0>::run(acc, af[CF::ADB ? kk & 1 : 0], bf[kk & 1], ra, rb, none);
                 } else {
                     // End of the slice (the last step's B fragments are in
                     // registers; its A fragments were all read before any
@@ -544,18 +610,24 @@ void gemm_f16_nt_kernel(Params p)
                     // (in bounds).
                     wait_vmcnt<VM_STEADY>();
                     lds_barrier();
-                    auto ra = [&](int i) { read_a(rd_next, 0, i); };
+                    auto ra = [&](int i) { read_a(0, rd_next, 0, i); };
                     auto rb = [&](int j) { read_b(0, rd_next, 0, j); };
-                    if (kk < DSTEPS)
-                        Step<CF, DPS>::run(acc, af, bf[kk & 1], ra, rb, dma);
+                    if constexpr (DX > 0)
+                        Step<CF, DX>::run(acc, af[CF::ADB ? kk & 1 : 0], bf[kk & 1], ra, rb, dma_early);
+                    else if (kk < DSTEPS)
+                        Step<CF, DPS>::run(acc, af[CF::ADB ? kk & 1 : 0], bf[kk & 1], ra, rb, dma);
                     else
-                        Step<CF, 0>::run(acc, af, bf[kk & 1], ra, rb, none);
+                        Step<CF, 0>::run(acc, af[CF::ADB ? kk & 1 : 0], bf[kk & 1], ra, rb, none);
                 }
             }
             pst = rd;
             rd = rd_next;
         }
 
+        // Wait states between the last hand-issued MFMA writing an accumulator
+        // and the first VALU read of it: 24, more than the ISA asks for after
+        // any MFMA, whatever its pass count.
+        if constexpr (CF::MI == 16) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
         // Every wave is done with the ring (and every DMA has landed): the next
         // tile's prefill may start, and it flies while this tile is stored.
         wait_vmcnt<0>();
@@ -613,12 +685,18 @@ static const KernelEntry kKernels[] = {
     entry<Cfg<256, 256, 32, 2, 4, 5>>(8, 0.00f),   // 8: 8 waves of 128x64, 5 stages of K 32
     entry<Cfg<256, 256, 64, 2, 2, 2>>(8, 1.00f),   // 9: 4 waves of 128x128, 2 stages of K 64
     entry<Cfg<256, 256, 64, 2, 4, 2>>(8, 0.00f),   // 10: 8 waves of 128x64, 2 stages of K 64
-    entry<Cfg<256, 256, 64, 2, 2, 2, 16>>(8, 0.00f),   // 11: as 9 with 16x16x32 MFMAs
+    // 11: as 9 with 16x16x32 MFMAs, the whole refill issued early, A double-buffered
+    entry<Cfg<256, 256, 64, 2, 2, 2, 16, 0, 16, 1>>(8, 1.06f),
     entry<Cfg<256, 128, 64, 2, 2, 3, 16>>(8, 0.00f),   // 12: as 2 with 16x16x32 MFMAs
     entry<Cfg<192, 256, 64, 2, 2, 2>>(8, 0.80f),   // 13: 4 waves of 96x128, 2 stages of K 64
     entry<Cfg<256, 192, 64, 2, 2, 2>>(8, 0.82f),   // 14: 4 waves of 128x96, 2 stages of K 64
     entry<Cfg<192, 256, 32, 2, 2, 5>>(8, 0.00f),   // 15: 4 waves of 96x128, 5 stages of K 32
     entry<Cfg<256, 192, 32, 2, 2, 5>>(8, 0.00f),   // 16: 4 waves of 128x96, 5 stages of K 32
+    // 17-20: the scheme of 11 on smaller tiles
+    entry<Cfg<256, 192, 64, 2, 2, 2, 16, 0, 14, 1>>(8, 0.96f),   // 17: 4 waves of 128x96
+    entry<Cfg<192, 256, 64, 2, 2, 2, 16, 0, 14, 1>>(8, 0.96f),   // 18: 4 waves of 96x128
+    entry<Cfg<256, 128, 64, 2, 2, 2, 16, 0, 12, 1>>(8, 0.00f),   // 19: 4 waves of 128x64
+    entry<Cfg<128, 128, 64, 2, 2, 2, 16, 0, 8, 1>>(8, 0.00f),    // 20: 4 waves of 64x64
 };
 constexpr int kNumKernels = sizeof(kKernels) / sizeof(kKernels[0]);
 
