@@ -72,21 +72,35 @@ constexpr int DEFAULT_XCDS = 8;        // MI355X: 8 XCDs x 32 CUs
 constexpr int DMA_BYTES = 64 * 16;     // one direct-to-LDS instruction: 64 lanes x 16 B
 
 // XOR applied to the 16-byte chunk index of LDS tile row r (rows are BK * 2
-// bytes = CHUNKS chunks).  An MFMA fragment read has 32 lanes reading rows
-// r0 .. r0 + 31 (r0 a multiple of 32) at one logical chunk.  The swizzle
-// depends on r mod 32 only and makes any 8 consecutive rows of such a read
-// cover 128 distinct bytes of bank space and any 16 consecutive rows 256
-// distinct bytes, i.e. conflict-free whether a ds_read_b128 is served 8 or 16
-// lanes at a time from 32 or 64 banks.
+// bytes = CHUNKS chunks), chosen per fragment shape so that the lanes the LDS
+// serves together hit distinct banks.
+//
+// 32x32x16 fragments: 32 lanes read rows r0 .. r0 + 31 (r0 a multiple of 32)
+// at one logical chunk.  The swizzle depends on r mod 32 only and makes any 8
+// consecutive rows of such a read cover 128 distinct bytes of bank space and
+// any 16 consecutive rows 256 distinct bytes, i.e. conflict-free whether a
+// ds_read_b128 is served 8 or 16 lanes at a time from 32 or 64 banks.
 //   8 chunks (128 B rows): row parity picks the 128-byte half of a 256-byte
 //   bank line, so the chunk XOR must differ across 8 consecutive rows and
 //   across the 8 even (odd) rows of 16: (r & 7) ^ ((r >> 3) & 3).
 //   4 chunks (64 B rows): r mod 4 picks the 64-byte quarter; the XOR must
 //   differ across the 4 rows of one quarter within 16 rows and across the
 //   even (odd) rows of 8: ((r >> 1) & 3) ^ ((r >> 3) & 1).
-template <int CHUNKS>
+//
+// 16x16x32 fragments (128 B rows only): lane l reads row l % 16 at logical
+// chunk c + l / 16, so four lanes share each row.  With the 32x32 swizzle
+// these reads cost twice the LDS cycles of a contiguous read (the hardware
+// counter put half of all LDS cycles in bank conflicts).  The pattern that
+// avoids this was found by measurement, not derived: all 4096 swizzles
+// linear in the bits of r mod 16 were timed as 16x16 fragment reads at both
+// K steps and both 16-row parities, and this one (one of 392 that read as
+// fast as a contiguous 1 KB) was chosen:
+//   bit 0 = r1, bit 1 = r2, bit 2 = r0 ^ r3.
+template <int CHUNKS, int MI = 32>
 __host__ __device__ constexpr int chunk_swizzle(int r)
 {
+    if (MI == 16)
+        return ((r >> 1) & 1) | (((r >> 2) & 1) << 1) | (((r ^ (r >> 3)) & 1) << 2);
     return CHUNKS == 8 ? ((r & 7) ^ ((r >> 3) & 3)) : (((r >> 1) & 3) ^ ((r >> 3) & 1));
 }
 
@@ -135,6 +149,7 @@ struct Cfg {
     static_assert(BK == 32 || BK == 64, "BK is 32 or 64");
     static_assert(KK % 2 == 0, "fragment double buffer alternates within a slice");
     static_assert(MI == 32 || MI == 16, "MFMA is 32x32x16 or 16x16x32");
+    static_assert(MI == 32 || CHUNKS == 8, "16x16x32 fragments need 128-byte rows");
     static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be whole 32-row blocks");
     static_assert(BM % (DMA_ROWS * WAVES) == 0 && BN % (DMA_ROWS * WAVES) == 0,
                   "every wave issues the same number of DMA instructions");
@@ -240,7 +255,7 @@ __device__ __forceinline__ void dma_one(const Params &p, const Tile &t, int stag
     const bool is_a = i < CF::A_LOADS;
     const int rblk = (is_a ? i : i - CF::A_LOADS) * CF::WAVES + wave;
     const int row = rblk * CF::DMA_ROWS + lane / CF::CHUNKS;
-    const int chunk = (lane % CF::CHUNKS) ^ chunk_swizzle<CF::CHUNKS>(row);
+    const int chunk = (lane % CF::CHUNKS) ^ chunk_swizzle<CF::CHUNKS, CF::MI>(row);
     uint32_t v = static_cast<uint32_t>(row) * row_pitch + chunk * 16 + k0 * 2;
     if (k0 + chunk * 8 >= static_cast<uint32_t>(p.K)) v = OOB_OFFSET;
     dma16(is_a ? t.rsrc_a : t.rsrc_b, v,
@@ -463,7 +478,7 @@ struct WaveCtx {
                 const int row32 = par * 16 + lrow;
                 const int chunk = kk * (CF::MK / 8) + lq;
                 frag_off[par][kk] = lrow * CF::ROW_BYTES +
-                                    ((chunk ^ chunk_swizzle<CF::CHUNKS>(CF::MI == 16 ? row32 : lrow)) * 16);
+                                    ((chunk ^ chunk_swizzle<CF::CHUNKS, CF::MI>(CF::MI == 16 ? row32 : lrow)) * 16);
             }
         a_frag_base = wave_m * CF::TM * CF::ROW_BYTES;
         b_frag_base = CF::A_BYTES + wave_n * CF::TN * CF::ROW_BYTES;
