@@ -263,6 +263,35 @@ __device__ __forceinline__ void dma_one(const Params &p, const Tile &t, int stag
               rblk * CF::DMA_ROWS * CF::ROW_BYTES);
 }
 
+// Fast form of dma_one for a slice that lies wholly inside K: the lane's
+// row offset `voff` (from dma_lane_offset, fixed for the whole kernel) goes in
+// the VGPR operand and the slice's K offset in the scalar offset, so issuing
+// it takes no vector ALU work.  Rows past M or N still start past the
+// resource's range on their own, so they read zeros as before.
+// (ip: the instruction's index within the A part or within the B part; both
+// parts use the same row pattern)
+template <class CF>
+__device__ __forceinline__ uint32_t dma_lane_offset(int ip, int wave, int lane, uint32_t row_pitch)
+{
+    const int rblk = ip * CF::WAVES + wave;
+    const int row = rblk * CF::DMA_ROWS + lane / CF::CHUNKS;
+    const int chunk = (lane % CF::CHUNKS) ^ chunk_swizzle<CF::CHUNKS, CF::MI>(row);
+    return static_cast<uint32_t>(row) * row_pitch + chunk * 16;
+}
+
+template <class CF>
+__device__ __forceinline__ void dma_full(const Tile &t, uint32_t voff, uint32_t koff, int stage,
+                                         int i, uint32_t lds0, int wave)
+{
+    const bool is_a = i < CF::A_LOADS;
+    const int rblk = (is_a ? i : i - CF::A_LOADS) * CF::WAVES + wave;
+    const uint32_t lds = lds0 + stage * CF::STAGE_BYTES + (is_a ? 0 : CF::A_BYTES) +
+                         rblk * CF::DMA_ROWS * CF::ROW_BYTES;
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+                 :
+                 : "v"(voff), "s"(is_a ? t.rsrc_a : t.rsrc_b), "s"(koff), "{m0}"(lds));
+}
+
 // All DMA instructions of one slice, back to back (prefill only).
 template <class CF>
 __device__ __forceinline__ void dma_slice(const Params &p, const Tile &t, int stage, int kt,
@@ -530,6 +559,13 @@ void gemm_f16_nt_kernel(Params p)
     static_assert((S - 1) * L <= 63 && VM_STEADY <= 63, "vmcnt counts at most 63 loads");
 
     const WaveCtx<CF> w(p);
+    // With two stages and the whole refill issued early, the refill of a
+    // slice wholly inside K takes the fast form (dma_full).
+    constexpr bool FAST_DMA = S == 2 && DX == L;
+    constexpr int NVOFF = FAST_DMA ? (CF::A_LOADS > CF::B_LOADS ? CF::A_LOADS : CF::B_LOADS) : 1;
+    uint32_t dvoff[NVOFF];
+#pragma unroll
+    for (int i = 0; i < NVOFF; ++i) dvoff[i] = dma_lane_offset<CF>(i, w.wave, w.lane, w.row_pitch);
     const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(smem));
     const int KT = (p.K + CF::BK - 1) / CF::BK;
 
@@ -592,7 +628,8 @@ void gemm_f16_nt_kernel(Params p)
         // Their accounting is therefore identical to the real ones.
         int rd = 0;        // stage holding slice kt
         int pst = S - 1;   // stage receiving slice kt + S - 1, freed before slice kt
-        for (int kt = 0; kt < KT; ++kt) {
+        auto slice = [&](int kt, auto fast) {
+            constexpr bool FAST = decltype(fast)::value;
             const int rd_next = rd + 1 == S ? 0 : rd + 1;
             const int pkt = kt + S - 1;
 #pragma unroll
@@ -605,7 +642,12 @@ void gemm_f16_nt_kernel(Params p)
                 // early part of slice kt + 2, into stage rd, which the barrier
                 // of this slice's last step has just freed
                 auto dma_early = [&](int d) {
-                    dma_one<CF>(p, cur, rd, kt + 2, d, lds0, w.wave, w.lane, w.row_pitch);
+                    if constexpr (FAST)
+                        dma_full<CF>(cur, dvoff[d < CF::A_LOADS ? d : d - CF::A_LOADS],
+                                     static_cast<uint32_t>(kt + 2) * (CF::BK * 2), rd, d, lds0,
+                                     w.wave);
+                    else
+                        dma_one<CF>(p, cur, rd, kt + 2, d, lds0, w.wave, w.lane, w.row_pitch);
                 };
                 if (kk + 1 < KK) {
                     auto ra = [&](int i) { read_a(CF::ADB ? (kk + 1) & 1 : 0, rd, kk + 1, i); };
@@ -637,7 +679,12 @@ void gemm_f16_nt_kernel(Params p)
             }
             pst = rd;
             rd = rd_next;
-        }
+        };
+        // slices whose early refill (slice kt + 2) lies wholly inside K, then the rest
+        const int kt_fast = FAST_DMA ? min(max(p.K / CF::BK - 2, 0), KT) : 0;
+        int kt = 0;
+        for (; kt < kt_fast; ++kt) slice(kt, std::true_type{});
+        for (; kt < KT; ++kt) slice(kt, std::false_type{});
 
         // Wait states between the last hand-issued MFMA writing an accumulator
         // and the first VALU read of it: 24, more than the ISA asks for after
