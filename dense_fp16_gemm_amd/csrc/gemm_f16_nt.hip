@@ -755,8 +755,8 @@ static const KernelEntry kKernels[] = {
     entry<Cfg<192, 256, 32, 2, 2, 5>>(8, 0.00f),   // 15: 4 waves of 96x128, 5 stages of K 32
     entry<Cfg<256, 192, 32, 2, 2, 5>>(8, 0.00f),   // 16: 4 waves of 128x96, 5 stages of K 32
     // 17-20: the scheme of 11 on smaller tiles
-    entry<Cfg<256, 192, 64, 2, 2, 2, 16, 0, 14, 1>>(8, 0.96f),   // 17: 4 waves of 128x96
-    entry<Cfg<192, 256, 64, 2, 2, 2, 16, 0, 14, 1>>(8, 0.96f),   // 18: 4 waves of 96x128
+    entry<Cfg<256, 192, 64, 2, 2, 2, 16, 0, 14, 1>>(8, 0.94f),   // 17: 4 waves of 128x96
+    entry<Cfg<192, 256, 64, 2, 2, 2, 16, 0, 14, 1>>(8, 0.97f),   // 18: 4 waves of 96x128
     entry<Cfg<256, 128, 64, 2, 2, 2, 16, 0, 12, 1>>(8, 0.00f),   // 19: 4 waves of 128x64
     entry<Cfg<128, 128, 64, 2, 2, 2, 16, 0, 8, 1>>(8, 0.00f),    // 20: 4 waves of 64x64
 };
