@@ -759,6 +759,10 @@ static const KernelEntry kKernels[] = {
     entry<Cfg<192, 256, 64, 2, 2, 2, 16, 0, 14, 1>>(8, 0.97f),   // 18: 4 waves of 96x128
     entry<Cfg<256, 128, 64, 2, 2, 2, 16, 0, 12, 1>>(8, 0.00f),   // 19: 4 waves of 128x64
     entry<Cfg<128, 128, 64, 2, 2, 2, 16, 0, 8, 1>>(8, 0.00f),    // 20: 4 waves of 64x64
+    // 21: 4 waves of 32x64.  For a small M the two tile rows that share a B
+    // strip run together on one XCD, and B, the operand streamed from HBM,
+    // holds two thirds of every stage (a 128x64 tile gives it one third).
+    entry<Cfg<64, 128, 64, 2, 2, 6>>(8, 0.65f),
 };
 constexpr int kNumKernels = sizeof(kKernels) / sizeof(kKernels[0]);
 
