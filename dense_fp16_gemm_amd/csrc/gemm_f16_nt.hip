@@ -717,6 +717,137 @@ void gemm_f16_nt_kernel(Params p)
 }
 
 // ---------------------------------------------------------------------------
+// General kernel: any K and A, B at any 2-byte alignment
+// ---------------------------------------------------------------------------
+// The direct-to-LDS path needs every 16-byte chunk of a row 16-byte aligned
+// (K a multiple of 8, A and B 16-byte aligned) and 32-bit buffer offsets
+// (K <= 2^21).  This path drops all three: each thread loads its 16-byte
+// chunks of the next slice into registers with plain global loads (at any
+// 2-byte alignment; element by element for the chunk that crosses K, zeros
+// for rows past M or N) and writes them to a double-buffered LDS tile in the
+// same swizzled layout, while the waves compute the current slice.  One
+// barrier per slice: it publishes the slice just written and frees the one
+// just read.  32x32x16 MFMAs in the same K order as every other
+// configuration, so results are identical to theirs.
+template <class CF>
+__device__ __forceinline__ half8_t load_chunk(const uint16_t *base, int32_t rows_valid, int row,
+                                              int64_t K, int64_t k)
+{
+    half8_t v = {};
+    if (row < rows_valid && k < K) {
+        const _Float16 *src = reinterpret_cast<const _Float16 *>(base) + row * K + k;
+        if (k + 8 <= K) {
+            __builtin_memcpy(&v, src, 16);   // one 16-byte load at any 2-byte alignment
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (k + e < K) v[e] = src[e];
+        }
+    }
+    return v;
+}
+
+template <class CF>
+__global__ __launch_bounds__(CF::THREADS)
+__attribute__((amdgpu_waves_per_eu(3)))
+void gemm_f16_nt_any_kernel(Params p)
+{
+    static_assert(CF::MI == 32 && CF::STAGES == 2, "general path: 32x32x16 MFMAs, 2 buffers");
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[CF::LDS_BYTES];
+    constexpr int KK = CF::KK;
+    constexpr int A_CH = CF::BM * CF::CHUNKS / CF::THREADS;   // chunks per thread per slice
+    constexpr int B_CH = CF::BN * CF::CHUNKS / CF::THREADS;
+    static_assert(A_CH * CF::THREADS == CF::BM * CF::CHUNKS &&
+                  B_CH * CF::THREADS == CF::BN * CF::CHUNKS, "whole chunks per thread");
+    const WaveCtx<CF> w(p);
+    const int tid = threadIdx.x;
+    const int64_t K = p.K;
+    const int KT = static_cast<int>((K + CF::BK - 1) / CF::BK);
+    half8_t ra[A_CH], rb[B_CH];
+    half8_t af[CF::FM], bf[CF::FN];
+
+    int32_t slot = blockIdx.x;
+    if (slot >= p.tiles) return;
+    while (true) {
+        int32_t tile_m, tile_n;
+        grouped_tile(slot_to_linear(slot, p.grid, p.tiles, p.xcds), p.tiles_m, p.tiles_n,
+                     p.swizzle, tile_m, tile_n);
+        Tile t;
+        t.m0 = tile_m * CF::BM;
+        t.n0 = tile_n * CF::BN;
+        const int32_t rows_a = min(CF::BM, p.M - t.m0), rows_b = min(CF::BN, p.N - t.n0);
+        const uint16_t *a0 = p.A + static_cast<int64_t>(t.m0) * K;
+        const uint16_t *b0 = p.B + static_cast<int64_t>(t.n0) * K;
+        auto load = [&](int kt) {
+#pragma unroll
+            for (int q = 0; q < A_CH; ++q) {
+                const int c = q * CF::THREADS + tid;
+                ra[q] = load_chunk<CF>(a0, rows_a, c / CF::CHUNKS, K,
+                                       static_cast<int64_t>(kt) * CF::BK + (c % CF::CHUNKS) * 8);
+            }
+#pragma unroll
+            for (int q = 0; q < B_CH; ++q) {
+                const int c = q * CF::THREADS + tid;
+                rb[q] = load_chunk<CF>(b0, rows_b, c / CF::CHUNKS, K,
+                                       static_cast<int64_t>(kt) * CF::BK + (c % CF::CHUNKS) * 8);
+            }
+        };
+        auto store = [&](int stage) {
+#pragma unroll
+            for (int q = 0; q < A_CH; ++q) {
+                const int c = q * CF::THREADS + tid, row = c / CF::CHUNKS;
+                const int phys = (c % CF::CHUNKS) ^ chunk_swizzle<CF::CHUNKS, CF::MI>(row);
+                *reinterpret_cast<half8_t *>(smem + stage * CF::STAGE_BYTES + row * CF::ROW_BYTES +
+                                             phys * 16) = ra[q];
+            }
+#pragma unroll
+            for (int q = 0; q < B_CH; ++q) {
+                const int c = q * CF::THREADS + tid, row = c / CF::CHUNKS;
+                const int phys = (c % CF::CHUNKS) ^ chunk_swizzle<CF::CHUNKS, CF::MI>(row);
+                *reinterpret_cast<half8_t *>(smem + stage * CF::STAGE_BYTES + CF::A_BYTES +
+                                             row * CF::ROW_BYTES + phys * 16) = rb[q];
+            }
+        };
+
+        typename CF::Acc acc[CF::FM][CF::FN];
+        zero_acc<CF>(acc);
+        if (KT > 0) {
+            load(0);
+            store(0);
+        }
+        lds_barrier();
+        for (int kt = 0; kt < KT; ++kt) {
+            const int cur = kt & 1;
+            if (kt + 1 < KT) load(kt + 1);     // in flight during this slice's MFMAs
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) {
+#pragma unroll
+                for (int i = 0; i < CF::FM; ++i)
+                    af[i] = *reinterpret_cast<const half8_t *>(
+                        smem + cur * CF::STAGE_BYTES + w.frag_off[0][kk] + w.a_frag_base +
+                        i * CF::MI * CF::ROW_BYTES);
+#pragma unroll
+                for (int j = 0; j < CF::FN; ++j)
+                    bf[j] = *reinterpret_cast<const half8_t *>(
+                        smem + cur * CF::STAGE_BYTES + w.frag_off[0][kk] + w.b_frag_base +
+                        j * CF::MI * CF::ROW_BYTES);
+#pragma unroll
+                for (int i = 0; i < CF::FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < CF::FN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[j], af[i], acc[i][j],
+                                                                          0, 0, 0);
+            }
+            if (kt + 1 < KT) store(cur ^ 1);
+            lds_barrier();
+        }
+        store_tile<CF>(p, t, acc, w.wave_m, w.wave_n, w.lane);
+        slot += p.grid;
+        if (slot >= p.tiles) break;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Kernel table
 // ---------------------------------------------------------------------------
 struct KernelEntry {
@@ -725,6 +856,8 @@ struct KernelEntry {
     int32_t default_swizzle;
     float rel_rate;   // relative MFMA rate per tile area, for the plan cost model
     int32_t staged_ok;
+    int32_t general;  // the general kernel: any K, A and B at any 2-byte alignment
+    int32_t per_cu;   // workgroups resident per CU (the persistent grid's multiple of the CUs)
 };
 
 template <class CF>
@@ -732,7 +865,15 @@ constexpr KernelEntry entry(int swizzle, float rate)
 {
     return KernelEntry{reinterpret_cast<const void *>(&gemm_f16_nt_kernel<CF>),
                        CF::BM, CF::BN, CF::BK, CF::WAVES, CF::STAGES, CF::LDS_BYTES, CF::THREADS,
-                       swizzle, rate, CF::STAGED_OK ? 1 : 0};
+                       swizzle, rate, CF::STAGED_OK ? 1 : 0, 0, 1};
+}
+
+template <class CF>
+constexpr KernelEntry entry_general(int swizzle)
+{
+    return KernelEntry{reinterpret_cast<const void *>(&gemm_f16_nt_any_kernel<CF>),
+                       CF::BM, CF::BN, CF::BK, CF::WAVES, CF::STAGES, CF::LDS_BYTES, CF::THREADS,
+                       swizzle, 0.0f, 0, 1, 3};
 }
 
 static const KernelEntry kKernels[] = {
@@ -763,8 +904,12 @@ static const KernelEntry kKernels[] = {
     // strip run together on one XCD, and B, the operand streamed from HBM,
     // holds two thirds of every stage (a 128x64 tile gives it one third).
     entry<Cfg<64, 128, 64, 2, 2, 6>>(8, 0.65f),
+    // 22: the general kernel, 4 waves of 64x64, two register-staged buffers of
+    // K 32; planned only when the direct-to-LDS path cannot run
+    entry_general<Cfg<128, 128, 32, 2, 2, 2>>(8),
 };
 constexpr int kNumKernels = sizeof(kKernels) / sizeof(kKernels[0]);
+constexpr int kGeneralConfig = kNumKernels - 1;
 
 // ---------------------------------------------------------------------------
 // Host side
@@ -787,14 +932,25 @@ static int validate(int64_t M, int64_t N, int64_t K, const void *A, const void *
         return GEMM_F16_INVALID_ARG;
     if (overlaps(C, c_bytes, A, a_bytes) || overlaps(C, c_bytes, B, b_bytes))
         return GEMM_F16_INVALID_ARG;
-    if (K % 8 != 0 || K > MAX_K) return GEMM_F16_UNSUPPORTED;
-    if ((a_bytes > 0 && reinterpret_cast<uintptr_t>(A) % 16 != 0) ||
-        (b_bytes > 0 && reinterpret_cast<uintptr_t>(B) % 16 != 0))
+    if (K > INT32_MAX) return GEMM_F16_UNSUPPORTED;
+    // fp16 elements: every matrix at least 2-byte aligned
+    if ((a_bytes > 0 && reinterpret_cast<uintptr_t>(A) % 2 != 0) ||
+        (b_bytes > 0 && reinterpret_cast<uintptr_t>(B) % 2 != 0) ||
+        (c_bytes > 0 && reinterpret_cast<uintptr_t>(C) % 2 != 0))
         return GEMM_F16_UNSUPPORTED;
-    if (c_bytes > 0 && reinterpret_cast<uintptr_t>(C) % 2 != 0) return GEMM_F16_UNSUPPORTED;
     // the smallest tile (128 x 64) must leave the tile count within int32
     if (cdiv(M, 128) * cdiv(N, 64) > INT32_MAX) return GEMM_F16_UNSUPPORTED;
     return GEMM_F16_OK;
+}
+
+// Whether the direct-to-LDS configurations can run these arguments: K a
+// multiple of 8 and at most 2^21, A and B 16-byte aligned.  Otherwise only
+// the general kernel can.
+static bool needs_general(int64_t K, const void *A, const void *B, bool check_pointers)
+{
+    if (K % 8 != 0 || K > MAX_K) return true;
+    if (!check_pointers) return false;
+    return reinterpret_cast<uintptr_t>(A) % 16 != 0 || reinterpret_cast<uintptr_t>(B) % 16 != 0;
 }
 
 static void fill_info(int id, gemm_f16_nt_plan_t *out)
@@ -832,7 +988,7 @@ static void make_plan(int id, int64_t M, int64_t N, int32_t num_cus, int32_t swi
     out->tiles = static_cast<int64_t>(out->tiles_m) * out->tiles_n;
     if (swizzle > 0) out->swizzle = swizzle;
     if (out->swizzle > out->tiles_n) out->swizzle = out->tiles_n > 0 ? out->tiles_n : 1;
-    const int64_t cap = grid > 0 ? grid : (num_cus > 0 ? num_cus : 1);
+    const int64_t cap = grid > 0 ? grid : (num_cus > 0 ? int64_t(num_cus) * kKernels[id].per_cu : 1);
     out->grid = static_cast<int32_t>(out->tiles < cap ? out->tiles : cap);
 }
 
@@ -914,10 +1070,13 @@ static int run(int64_t M, int64_t N, int64_t K, const void *A, const void *B, vo
     if (v != GEMM_F16_OK) return v;
     if (config_id >= kNumKernels) return GEMM_F16_INVALID_ARG;
     if (M == 0 || N == 0) return GEMM_F16_OK;
+    const bool general = needs_general(K, A, B, K > 0);
+    if (general && config_id >= 0 && !kKernels[config_id].general) return GEMM_F16_UNSUPPORTED;
     int32_t cus = 0;
     const int s = current_cus(&cus);
     if (s != GEMM_F16_OK) return s;
-    const int id = config_id >= 0 ? config_id : choose_config(M, N, cus);
+    const int id = config_id >= 0 ? config_id
+                                  : (general ? kGeneralConfig : choose_config(M, N, cus));
     gemm_f16_nt_plan_t plan;
     make_plan(id, M, N, cus, swizzle, grid, &plan);
     if (epilogue < 0) {
@@ -969,9 +1128,11 @@ extern "C" int gemm_f16_nt_plan(int64_t M, int64_t N, int64_t K, int32_t num_cus
                                 gemm_f16_nt_plan_t *plan)
 {
     if (!plan || M < 0 || N < 0 || K < 0 || num_cus <= 0) return GEMM_F16_INVALID_ARG;
-    if (M > INT32_MAX || N > INT32_MAX || cdiv(M, 128) * cdiv(N, 64) > INT32_MAX)
+    if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX || cdiv(M, 128) * cdiv(N, 64) > INT32_MAX)
         return GEMM_F16_UNSUPPORTED;
-    make_plan(choose_config(M, N, num_cus), M, N, num_cus, 0, 0, plan);
+    const int id = needs_general(K, nullptr, nullptr, false) ? kGeneralConfig
+                                                              : choose_config(M, N, num_cus);
+    make_plan(id, M, N, num_cus, 0, 0, plan);
     return GEMM_F16_OK;
 }
 

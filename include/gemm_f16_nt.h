@@ -39,9 +39,10 @@ enum {
     /* a dimension < 0; a NULL pointer for a matrix with elements; C
      * overlapping A or B; an unknown configuration id */
     GEMM_F16_INVALID_ARG = 1,
-    /* valid but outside what the kernels handle: K not a multiple of 8, A or B
-     * not 16-byte aligned, C not 2-byte aligned, K > 2^21, or more than
-     * 2^31 - 1 output tiles */
+    /* valid but outside what the kernels handle: A, B or C not 2-byte aligned
+     * (not fp16 element addresses), M, N or K above 2^31 - 1, or more than
+     * 2^31 - 1 output tiles; also a forced configuration that cannot take the
+     * arguments (see gemm_f16_nt_with_config) */
     GEMM_F16_UNSUPPORTED = 2,
     /* the HIP runtime reported an error when launching (hipGetLastError) or
      * when querying the current device */
@@ -58,6 +59,10 @@ enum {
  *
  * M = 0 or N = 0: nothing to compute, returns GEMM_F16_OK without a launch.
  * K = 0: C is filled with +0 (the empty sum).
+ * Any K and any 2-byte alignment of A, B and C are accepted.  The fast
+ * kernels load with 16-byte direct-to-LDS DMA and need K a multiple of 8, at
+ * most 2^21, and A and B 16-byte aligned; other arguments run the general
+ * kernel (register-staged loads), which gives the same results, more slowly.
  * Results are deterministic: no atomics, and each element's K order depends
  * only on K, never on the element's position or on the launch shape.
  */
@@ -77,8 +82,9 @@ int gemm_f16_nt_validate(int64_t M, int64_t N, int64_t K,
 
 /*
  * The launch plan the library would use for (M, N, K) on a device with
- * `num_cus` compute units.  Pure host function (no device access): used by
- * tests and by the benchmark to report what runs.
+ * `num_cus` compute units, for 16-byte aligned A and B (otherwise the general
+ * kernel, the last configuration, runs).  Pure host function (no device
+ * access): used by tests and by the benchmark to report what runs.
  */
 typedef struct {
     int32_t config_id;   /* index into the compiled kernel table           */
@@ -113,8 +119,11 @@ int gemm_f16_nt_config_info(int32_t config_id, gemm_f16_nt_plan_t *info);
  * grid <= 0: one workgroup per compute unit, capped by the tile count;
  * swizzle <= 0: the configuration's default;
  * epilogue < 0: the library's choice, 0: direct stores, 1: staged through
- * LDS -- GEMM_F16_UNSUPPORTED if the configuration has no room for it).  Same
- * semantics, ownership and status codes as gemm_f16_nt; the result is
+ * LDS -- GEMM_F16_UNSUPPORTED if the configuration has no room for it).  A
+ * direct-to-LDS configuration forced on arguments only the general kernel
+ * takes (K not a multiple of 8 or above 2^21, A or B not 16-byte aligned)
+ * returns GEMM_F16_UNSUPPORTED.  Otherwise the same semantics, ownership
+ * and status codes as gemm_f16_nt; the result is
  * identical for every configuration, swizzle, grid and epilogue, because the
  * K order of each element does not depend on them.  For tests and tuning
  * sweeps.

@@ -63,12 +63,16 @@ A0, B0, C0 = 0x10000, 0x20000000, 0x40000000   # fake, well-separated, aligned a
     ((64, 64, 64, A0, B0, A0 + 100), 1),       # C overlaps A
     ((64, 64, 64, A0, B0, B0 + 8192 - 2), 1),  # C overlaps the end of B
     ((64, 64, 64, A0, B0, B0 + 8192), 0),      # C right after B
-    ((64, 64, 60, A0, B0, C0), 2),             # K % 8 != 0
-    ((64, 64, 64, A0 + 8, B0, C0), 2),         # A not 16-byte aligned
-    ((64, 64, 64, A0, B0 + 2, C0), 2),
+    ((64, 64, 60, A0, B0, C0), 0),             # K % 8 != 0: the general kernel
+    ((64, 64, 1, A0, B0, C0), 0),
+    ((64, 64, 64, A0 + 8, B0, C0), 0),         # A only 8-byte aligned: general kernel
+    ((64, 64, 64, A0, B0 + 2, C0), 0),         # B only 2-byte aligned: general kernel
+    ((64, 64, 64, A0 + 1, B0, C0), 2),         # A not 2-byte aligned
+    ((64, 64, 64, A0, B0 + 3, C0), 2),         # B not 2-byte aligned
     ((64, 64, 64, A0, B0, C0 + 1), 2),         # C not 2-byte aligned
     ((64, 64, 64, A0, B0, C0 + 2), 0),         # C 2-byte aligned is fine
-    ((8, 8, (1 << 21) + 8, A0, B0 + (1 << 40), C0 + (1 << 41)), 2),   # K too large
+    ((8, 8, (1 << 21) + 8, A0, B0 + (1 << 40), C0 + (1 << 41)), 0),   # K past the DMA path
+    ((8, 8, (1 << 31), A0, B0 + (1 << 40), C0 + (1 << 41)), 2),       # K beyond int32
     ((1 << 31, 8, 8, A0, B0 + (1 << 40), C0 + (1 << 41)), 2),         # M beyond int32
 ])
 def test_validate(g, args, status):
@@ -82,6 +86,8 @@ def test_config_table(g):
         info = g.gemm_f16_nt_config_info(cid)
         assert info.config_id == cid
         assert info.block_k in (32, 64)
+        # (the last entry, the general kernel, stages through registers into
+        # two LDS buffers with the same layout)
         # the LDS ring: stages * (BM + BN) * BK * 2 bytes within 160 KB
         assert info.lds_bytes == info.stages * (info.block_m + info.block_n) * info.block_k * 2
         assert info.lds_bytes <= 160 * 1024
@@ -99,6 +105,14 @@ def test_plan_basics(g, shape):
     assert p.tiles == p.tiles_m * p.tiles_n
     assert 1 <= p.grid <= min(256, p.tiles)
     assert 1 <= p.swizzle <= max(1, p.tiles_n)
+
+
+@pytest.mark.parametrize("k", [1, 7, 60, 100, 4097, (1 << 21) + 8])
+def test_plan_general_for_k(g, k):
+    # K that the direct-to-LDS configurations cannot take goes to the general kernel
+    general = g.gemm_f16_nt_num_configs() - 1
+    assert g.gemm_f16_nt_plan(300, 200, k, 256).config_id == general
+    assert g.gemm_f16_nt_plan(300, 200, 64, 256).config_id != general
 
 
 def test_plan_headline_and_skinny(g):

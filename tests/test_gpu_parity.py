@@ -320,3 +320,76 @@ def test_integer_workload_full_matrix(g):
     got = run_gpu(g, a, b)
     exact = (a.astype(np.float64) @ b.astype(np.float64).T).astype(np.float16)
     assert_bit_exact(got, exact, "4096^3 int2 full matrix")
+
+
+# ---------------------------------------------------------------------------
+# the general kernel: any K, A and B at any 2-byte alignment
+# ---------------------------------------------------------------------------
+def run_gpu_offset(g, a, b, a_offset=0, b_offset=0, config=None):
+    """As run_gpu, with A and B placed a_offset / b_offset fp16 elements into
+    larger buffers (to test A and B alignment)."""
+    import torch
+
+    _say(f"  gpu gemm {a.shape[0]}x{b.shape[0]}x{a.shape[1]} a_offset={a_offset} "
+         f"b_offset={b_offset} config={config}")
+    dev = torch.device("cuda:0")
+    m, k = a.shape
+    n = b.shape[0]
+    fa = torch.zeros(m * k + a_offset + 8, dtype=torch.float16, device=dev)
+    fb = torch.zeros(n * k + b_offset + 8, dtype=torch.float16, device=dev)
+    ta = fa[a_offset:a_offset + m * k].view(m, k)
+    tb = fb[b_offset:b_offset + n * k].view(n, k)
+    ta.copy_(torch.from_numpy(np.ascontiguousarray(a)))
+    tb.copy_(torch.from_numpy(np.ascontiguousarray(b)))
+    flat = torch.full((m * n + 8,), float("nan"), dtype=torch.float16, device=dev)
+    out = flat[:m * n].view(m, n)
+    g.gemm_nt(ta, tb, out=out, config=config)
+    torch.cuda.synchronize()
+    host = flat.cpu().numpy()
+    assert np.isnan(host[m * n:].astype(np.float32)).all()
+    return host[:m * n].reshape(m, n)
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 7, 9, 15, 17, 33, 100, 255, 1001])
+def test_general_any_k(g, oracle_mod, k):
+    """K that is not a multiple of 8 runs the general kernel (tails in M, N
+    and within the last 16-byte chunk of every row)."""
+    a, b = workloads.make_inputs(130, 70, k, "uniform", 1.0 / np.sqrt(k), seed=k + 500)
+    got = run_gpu(g, a, b)
+    assert_within_tolerance(got, oracle_mod.gemm(a, b), f"k={k}")
+    ai, bi = workloads.make_inputs(130, 70, k, "int2", 1.0, seed=k + 600)
+    assert_bit_exact(run_gpu(g, ai, bi), oracle_mod.gemm(ai, bi), f"int k={k}")
+
+
+@pytest.mark.parametrize("a_offset,b_offset", [(1, 0), (0, 1), (3, 5), (4, 4), (7, 2)])
+def test_general_unaligned_a_b(g, oracle_mod, a_offset, b_offset):
+    """A or B only 2-, 4- or 8-byte aligned runs the general kernel; the
+    result equals the aligned direct-to-LDS path's bit for bit (same K order)."""
+    a, b = workloads.make_inputs(300, 260, 136, "normal", 0.1, seed=a_offset * 8 + b_offset)
+    got = run_gpu_offset(g, a, b, a_offset, b_offset)
+    assert_within_tolerance(got, oracle_mod.gemm(a, b), f"offsets {a_offset},{b_offset}")
+    assert_bit_exact(got, run_gpu(g, a, b), f"offsets {a_offset},{b_offset} vs aligned")
+
+
+def test_general_matches_direct_path(g):
+    """The general kernel forced on aligned inputs gives the default plan's
+    result bit for bit."""
+    general = g.gemm_f16_nt_num_configs() - 1
+    a, b = workloads.make_inputs(517, 389, 264, "normal", 0.06, seed=77)
+    assert_bit_exact(run_gpu(g, a, b, config=general), run_gpu(g, a, b), "general vs default")
+
+
+def test_forced_direct_config_rejects_general_arguments(g):
+    """A direct-to-LDS configuration forced on arguments it cannot take is an
+    error, not a wrong result."""
+    a, b = workloads.make_inputs(64, 64, 60, "uniform", 0.1, seed=3)
+    with pytest.raises(g.GemmError) as e:
+        run_gpu(g, a, b, config=11)
+    assert e.value.status == g.UNSUPPORTED
+
+
+def test_general_large_k(g, oracle_mod):
+    """K beyond 2^21 (past the direct path's 32-bit buffer offsets)."""
+    k = (1 << 21) + 24
+    a, b = workloads.make_inputs(8, 9, k, "uniform", 1.0 / np.sqrt(k), seed=91)
+    assert_within_tolerance(run_gpu(g, a, b), oracle_mod.gemm(a, b), f"k={k}")
