@@ -86,6 +86,8 @@ constexpr int DMA_BYTES = 64 * 16;     // one direct-to-LDS instruction: 64 lane
 //   4 chunks (64 B rows): r mod 4 picks the 64-byte quarter; the XOR must
 //   differ across the 4 rows of one quarter within 16 rows and across the
 //   even (odd) rows of 8: ((r >> 1) & 3) ^ ((r >> 3) & 1).
+//   16 chunks (256 B rows): every row starts on the same bank, so the XOR
+//   must differ across any 16 consecutive rows: r & 15.
 //
 // 16x16x32 fragments (128 B rows only): lane l reads row l % 16 at logical
 // chunk c + l / 16, so four lanes share each row.  With the 32x32 swizzle
@@ -101,6 +103,7 @@ __host__ __device__ constexpr int chunk_swizzle(int r)
 {
     if (MI == 16)
         return ((r >> 1) & 1) | (((r >> 2) & 1) << 1) | (((r ^ (r >> 3)) & 1) << 2);
+    if (CHUNKS == 16) return r & 15;
     return CHUNKS == 8 ? ((r & 7) ^ ((r >> 3) & 3)) : (((r >> 1) & 3) ^ ((r >> 3) & 1));
 }
 
@@ -146,7 +149,7 @@ struct Cfg {
     // the LDS-staged epilogue writes one block row of every wave (WM * MI tile
     // rows of BN halves, rows padded by 16 bytes) into one ring stage
     static constexpr bool STAGED_OK = WM * MI * (BN * 2 + 16) <= STAGE_BYTES;
-    static_assert(BK == 32 || BK == 64, "BK is 32 or 64");
+    static_assert(BK == 32 || BK == 64 || BK == 128, "BK is 32, 64 or 128");
     static_assert(KK % 2 == 0, "fragment double buffer alternates within a slice");
     static_assert(MI == 32 || MI == 16, "MFMA is 32x32x16 or 16x16x32");
     static_assert(MI == 32 || CHUNKS == 8, "16x16x32 fragments need 128-byte rows");
@@ -212,8 +215,7 @@ __device__ __forceinline__ void lds_barrier()
 // Coordinates and buffer resources of one output tile.
 struct Tile {
     int32_t m0, n0;
-    i32x4_t rsrc_a, rsrc_b;              // for the DMA asm
-    __amdgpu_buffer_rsrc_t ra, rb;       // the same ranges, for register loads
+    i32x4_t rsrc_a, rsrc_b;              // buffer resources for the DMA asm
 };
 
 template <class CF>
@@ -232,12 +234,6 @@ __device__ __forceinline__ Tile make_tile(const Params &p, int32_t slot, uint32_
                          static_cast<uint32_t>(rows_a) * row_pitch);
     t.rsrc_b = make_rsrc(p.B + static_cast<int64_t>(t.n0) * p.K,
                          static_cast<uint32_t>(rows_b) * row_pitch);
-    t.ra = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t *>(p.A + static_cast<int64_t>(t.m0) * p.K), static_cast<short>(0),
-        static_cast<int32_t>(static_cast<uint32_t>(rows_a) * row_pitch), 0x00020000);
-    t.rb = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t *>(p.B + static_cast<int64_t>(t.n0) * p.K), static_cast<short>(0),
-        static_cast<int32_t>(static_cast<uint32_t>(rows_b) * row_pitch), 0x00020000);
     return t;
 }
 
@@ -683,6 +679,19 @@ void gemm_f16_nt_kernel(Params p)
         // slices whose early refill (slice kt + 2) lies wholly inside K, then the rest
         const int kt_fast = FAST_DMA ? min(max(p.K / CF::BK - 2, 0), KT) : 0;
         int kt = 0;
+        if constexpr (FAST_DMA) {
+            // two slices per trip (FAST_DMA implies two stages), so the ring
+            // stage of each is a compile-time constant: LDS addresses and M0
+            // values become loop-invariant registers
+            for (; kt + 1 < kt_fast; kt += 2) {
+                rd = 0;
+                pst = 1;
+                slice(kt, std::true_type{});
+                rd = 1;
+                pst = 0;
+                slice(kt + 1, std::true_type{});
+            }
+        }
         for (; kt < kt_fast; ++kt) slice(kt, std::true_type{});
         for (; kt < KT; ++kt) slice(kt, std::false_type{});
 
@@ -904,7 +913,10 @@ static const KernelEntry kKernels[] = {
     // strip run together on one XCD, and B, the operand streamed from HBM,
     // holds two thirds of every stage (a 128x64 tile gives it one third).
     entry<Cfg<64, 128, 64, 2, 2, 6>>(8, 0.65f),
-    // 22: the general kernel, 4 waves of 64x64, two register-staged buffers of
+    // 22: 21 with K 128 per stage (256-byte rows): twice the contiguous bytes
+    // per row and DMA instruction, which the HBM stream of B prefers
+    entry<Cfg<64, 128, 128, 2, 2, 3>>(8, 0.66f),
+    // 23: the general kernel, 4 waves of 64x64, two register-staged buffers of
     // K 32; planned only when the direct-to-LDS path cannot run
     entry_general<Cfg<128, 128, 32, 2, 2, 2>>(8),
 };

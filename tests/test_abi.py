@@ -85,7 +85,7 @@ def test_config_table(g):
     for cid in range(n):
         info = g.gemm_f16_nt_config_info(cid)
         assert info.config_id == cid
-        assert info.block_k in (32, 64)
+        assert info.block_k in (32, 64, 128)
         # (the last entry, the general kernel, stages through registers into
         # two LDS buffers with the same layout)
         # the LDS ring: stages * (BM + BN) * BK * 2 bytes within 160 KB
