@@ -4,7 +4,8 @@
 // Multicast, and a Persistent Kernel", opening paragraphs).
 //
 // One kernel template, every workgroup doing every job (the pages' V2 shape,
-// which suits CDNA's in-order waves sharing one barrier):
+// which suits CDNA's in-order waves sharing one barrier), plus a general
+// kernel for the arguments the template's loads cannot take:
 //
 //  * persistent tile loop: grid = min(tiles, CUs); workgroup wg walks slots
 //    wg, wg + grid, ... through the grouped, XCD-aware order of
@@ -16,30 +17,37 @@
 //    VGPR staging).  A DMA instruction writes 64 x 16 B contiguously, so the
 //    XOR swizzle that keeps the MFMA fragment reads free of bank conflicts is
 //    applied on the global side: the lane that fills physical 16-byte chunk p
-//    of row r fetches logical chunk p ^ swz(r);
+//    of row r fetches logical chunk p ^ swz(r).  With two stages the refill
+//    of slice kt + 2 starts right after the barrier of slice kt's last step
+//    (the "early refill"), and a refill inside K carries its K offset in the
+//    instruction's scalar offset;
 //  * stage bookkeeping without mbarriers: "full" = s_waitcnt vmcnt(n) on the
 //    wave's own DMA queue + s_barrier; "empty" = s_waitcnt lgkmcnt(0) before
 //    that same barrier, so one barrier per K-slice serves both roles (page 3
-//    "Producer-Consumer Barriers" describe the two roles); the loop is
-//    unrolled by STAGES so stage offsets are compile-time constants (page 2
-//    "Loop Unrolling and Stage Indices");
-//  * v_mfma_f32_32x32x16_f16 with fp32 accumulators held in AGPRs; the
+//    "Producer-Consumer Barriers" describe the two roles); with two stages
+//    the loop runs two slices per trip so stage offsets are compile-time
+//    constants (page 2 "Loop Unrolling and Stage Indices");
+//  * v_mfma_f32_32x32x16_f16 (builtin) or v_mfma_f32_16x16x32_f16 (inline
+//    assembly with accumulators bound to AGPRs) with fp32 accumulators; the
 //    output tile is split over a WM x WN grid of waves that share A rows and
 //    B rows through LDS (page 4 "Two Consumer Warp Groups"); fragments for
-//    the next 16-deep K step are read while the current step's MFMAs run
-//    (the lesson of the pages' V5: never let the matrix pipe drain);
+//    the next K step are read while the current step's MFMAs run (the lesson
+//    of the pages' V5: never let the matrix pipe drain);
 //  * epilogue: round-to-nearest-even fp32 -> fp16 (v_cvt_f16_f32 under the
-//    default MODE), masked M/N tails, 8-byte stores where alignment allows.
+//    default MODE), staged through a free ring stage for 16-byte row stores
+//    at any 2-byte alignment (page 6 "Shared-Memory Epilogue"), or stored
+//    straight from the MFMA layout; masked M/N tails.
 //
-// Operand roles: the MFMA's first operand (rows of its 32x32 result) takes a
-// 32-row slice of the B tile and the second operand (columns) a 32-row slice
-// of the A tile, so the result block is C^T and each lane ends up holding 4
-// consecutive N columns of one M row -- ready for packed fp16 stores.
+// Operand roles: the MFMA's first operand (rows of its result block) takes
+// rows of the B tile and the second operand (columns) rows of the A tile, so
+// the result block is C^T and each lane ends up holding 4 consecutive N
+// columns of one M row -- ready for packed fp16 stores.
 //
 // Tails: the buffer resource of a tile starts at its first row and covers
 // exactly its valid rows, so rows beyond M (or N) read as zero; a 16-byte
 // chunk beyond K is given an offset past the resource, which also reads as
-// zero (K is a multiple of 8, so chunks never straddle K).
+// zero (the template needs K a multiple of 8, so chunks never straddle K;
+// other K, and A or B not 16-byte aligned, go to the general kernel).
 #include <hip/hip_runtime.h>
 
 #include <mutex>
