@@ -393,3 +393,30 @@ def test_general_large_k(g, oracle_mod):
     k = (1 << 21) + 24
     a, b = workloads.make_inputs(8, 9, k, "uniform", 1.0 / np.sqrt(k), seed=91)
     assert_within_tolerance(run_gpu(g, a, b), oracle_mod.gemm(a, b), f"k={k}")
+
+
+# ---------------------------------------------------------------------------
+# seeded random shapes across every configuration and alignment
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("case", range(24))
+def test_random_shapes_every_path(g, oracle_mod, case):
+    """Seeded random M, N, K (K a multiple of 8 or not), a random
+    configuration that can take them, and random A/B offsets: parity with
+    the oracle, and for K a multiple of 8 with aligned operands, equality
+    with the default plan bit for bit."""
+    rng = np.random.default_rng(9000 + case)
+    m = int(rng.integers(1, 700))
+    n = int(rng.integers(1, 700))
+    k = int(rng.integers(1, 600))
+    if case % 2 == 0:
+        k = max(8, k - k % 8)
+    a_off = int(rng.choice([0, 0, 8, 1, 3]))
+    b_off = int(rng.choice([0, 0, 8, 2, 5]))
+    general = g.gemm_f16_nt_num_configs() - 1
+    fast_ok = k % 8 == 0 and a_off % 8 == 0 and b_off % 8 == 0
+    cid = int(rng.integers(0, g.gemm_f16_nt_num_configs())) if fast_ok else general
+    a, b = workloads.make_inputs(m, n, k, "normal", 1.0 / np.sqrt(k), seed=case)
+    got = run_gpu_offset(g, a, b, a_off, b_off, config=cid)
+    assert_within_tolerance(got, oracle_mod.gemm(a, b), f"case {case}: {m}x{n}x{k} config {cid}")
+    if fast_ok:
+        assert_bit_exact(got, run_gpu(g, a, b), f"case {case}: config {cid} vs default")
