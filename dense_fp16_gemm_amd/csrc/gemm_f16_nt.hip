@@ -930,7 +930,10 @@ static const KernelEntry kKernels[] = {
     // 22: 21 with K 128 per stage (256-byte rows): twice the contiguous bytes
     // per row and DMA instruction, which the HBM stream of B prefers
     entry<Cfg<64, 128, 128, 2, 2, 3>>(8, 0.66f),
-    // 23: the general kernel, 4 waves of 64x64, two register-staged buffers of
+    // 23: 4 waves of 32x32, five stages of K 128: more tiles for a small M
+    // whose 64x128 tiles would leave CUs idle (M <= 256, N of a few thousand)
+    entry<Cfg<64, 64, 128, 2, 2, 5>>(8, 0.62f),
+    // 24: the general kernel, 4 waves of 64x64, two register-staged buffers of
     // K 32; planned only when the direct-to-LDS path cannot run
     entry_general<Cfg<128, 128, 32, 2, 2, 2>>(8),
 };

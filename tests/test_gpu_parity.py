@@ -109,7 +109,7 @@ def test_parity_every_config(g, oracle_mod, shape):
                 assert_bit_exact(got, first, f"{shape} config {cid} epilogue {epi} vs first")
 
 
-@pytest.mark.parametrize("cid", [0, 1, 2, 3, 4, 5, 9, 11, 17, 18, 19, 20, 21, 22])
+@pytest.mark.parametrize("cid", [0, 1, 2, 3, 4, 5, 9, 11, 17, 18, 19, 20, 21, 22, 23])
 @pytest.mark.parametrize("k", [8, 24, 32, 40, 64, 72, 128, 136, 160, 192, 200, 256, 264, 328])
 def test_short_and_ragged_k(g, oracle_mod, cid, k):
     """K with fewer slices than stages, exactly the stages, one more, and
@@ -119,7 +119,7 @@ def test_short_and_ragged_k(g, oracle_mod, cid, k):
     assert_within_tolerance(got, oracle_mod.gemm(a, b), f"k={k} config {cid}")
 
 
-@pytest.mark.parametrize("cid", [0, 2, 4, 5, 11, 17, 18, 19, 20, 21, 22])
+@pytest.mark.parametrize("cid", [0, 2, 4, 5, 11, 17, 18, 19, 20, 21, 22, 23])
 def test_edge_m_n(g, oracle_mod, cid):
     info = g.gemm_f16_nt_config_info(cid)
     bm, bn = info.block_m, info.block_n
