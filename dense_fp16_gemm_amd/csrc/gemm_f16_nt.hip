@@ -967,8 +967,8 @@ static int validate(int64_t M, int64_t N, int64_t K, const void *A, const void *
         (b_bytes > 0 && reinterpret_cast<uintptr_t>(B) % 2 != 0) ||
         (c_bytes > 0 && reinterpret_cast<uintptr_t>(C) % 2 != 0))
         return GEMM_F16_UNSUPPORTED;
-    // the smallest tile (128 x 64) must leave the tile count within int32
-    if (cdiv(M, 128) * cdiv(N, 64) > INT32_MAX) return GEMM_F16_UNSUPPORTED;
+    // the smallest tile (64 x 64) must leave the tile count within int32
+    if (cdiv(M, 64) * cdiv(N, 64) > INT32_MAX) return GEMM_F16_UNSUPPORTED;
     return GEMM_F16_OK;
 }
 
@@ -1000,18 +1000,13 @@ static void fill_info(int id, gemm_f16_nt_plan_t *out)
 // Epilogue policy: stage C through LDS whenever the configuration has room
 // for it (row-contiguous stores measured faster than direct stores from the
 // MFMA layout for aligned and unaligned C alike).
-static int32_t choose_epilogue(int id, int64_t N, bool c_aligned8)
-{
-    (void)N;
-    (void)c_aligned8;
-    return kKernels[id].staged_ok ? 1 : 0;
-}
+static int32_t choose_epilogue(int id) { return kKernels[id].staged_ok ? 1 : 0; }
 
 static void make_plan(int id, int64_t M, int64_t N, int32_t num_cus, int32_t swizzle,
                       int32_t grid, gemm_f16_nt_plan_t *out)
 {
     fill_info(id, out);
-    out->epilogue = choose_epilogue(id, N, true);
+    out->epilogue = choose_epilogue(id);
     out->tiles_m = static_cast<int32_t>(cdiv(M, out->block_m));
     out->tiles_n = static_cast<int32_t>(cdiv(N, out->block_n));
     out->tiles = static_cast<int64_t>(out->tiles_m) * out->tiles_n;
@@ -1085,10 +1080,10 @@ static int launch(const gemm_f16_nt_plan_t &plan, int64_t M, int64_t N, int64_t 
     p.staged = plan.epilogue;
     const KernelEntry &e = kKernels[plan.config_id];
     void *args[] = {&p};
-    hipError_t err = hipLaunchKernel(e.fn, dim3(plan.grid), dim3(e.threads), args, 0, stream);
-    if (err != hipSuccess) return GEMM_F16_LAUNCH_FAILED;
-    if (hipGetLastError() != hipSuccess) return GEMM_F16_LAUNCH_FAILED;
-    return GEMM_F16_OK;
+    // the launch's own status only: the thread's sticky error state (which may
+    // hold an unrelated earlier error) is neither read nor cleared
+    const hipError_t err = hipLaunchKernel(e.fn, dim3(plan.grid), dim3(e.threads), args, 0, stream);
+    return err == hipSuccess ? GEMM_F16_OK : GEMM_F16_LAUNCH_FAILED;
 }
 
 static int run(int64_t M, int64_t N, int64_t K, const void *A, const void *B, void *C,
@@ -1109,7 +1104,7 @@ static int run(int64_t M, int64_t N, int64_t K, const void *A, const void *B, vo
     gemm_f16_nt_plan_t plan;
     make_plan(id, M, N, cus, swizzle, grid, &plan);
     if (epilogue < 0) {
-        plan.epilogue = choose_epilogue(id, N, reinterpret_cast<uintptr_t>(C) % 8 == 0);
+        plan.epilogue = choose_epilogue(id);
     } else {
         if (epilogue > 1 || (epilogue == 1 && !kKernels[id].staged_ok)) return GEMM_F16_UNSUPPORTED;
         plan.epilogue = epilogue;
@@ -1157,7 +1152,7 @@ extern "C" int gemm_f16_nt_plan(int64_t M, int64_t N, int64_t K, int32_t num_cus
                                 gemm_f16_nt_plan_t *plan)
 {
     if (!plan || M < 0 || N < 0 || K < 0 || num_cus <= 0) return GEMM_F16_INVALID_ARG;
-    if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX || cdiv(M, 128) * cdiv(N, 64) > INT32_MAX)
+    if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX || cdiv(M, 64) * cdiv(N, 64) > INT32_MAX)
         return GEMM_F16_UNSUPPORTED;
     const int id = needs_general(K, nullptr, nullptr, false) ? kGeneralConfig
                                                               : choose_config(M, N, num_cus);

@@ -44,8 +44,9 @@ enum {
      * 2^31 - 1 output tiles; also a forced configuration that cannot take the
      * arguments (see gemm_f16_nt_with_config) */
     GEMM_F16_UNSUPPORTED = 2,
-    /* the HIP runtime reported an error when launching (hipGetLastError) or
-     * when querying the current device */
+    /* the HIP runtime reported an error for the kernel launch (the status
+     * hipLaunchKernel returns; the thread's last-error state is left as it
+     * was) or when querying the current device */
     GEMM_F16_LAUNCH_FAILED = 3
 };
 
