@@ -65,6 +65,13 @@ def load():
         lib.gemm_f16_nt_validate.restype = ctypes.c_int
         lib.gemm_f16_nt_plan.argtypes = [i64, i64, i64, i32, ctypes.POINTER(Plan)]
         lib.gemm_f16_nt_plan.restype = ctypes.c_int
+        lib.gemm_f16_nt_splitk_plan.argtypes = [i64, i64, i64, i32, i32, ctypes.POINTER(Plan),
+                                                ctypes.POINTER(i32), ctypes.POINTER(i64)]
+        lib.gemm_f16_nt_splitk_plan.restype = ctypes.c_int
+        lib.gemm_f16_nt_splitk.argtypes = [i64, i64, i64, p, p, p, i32, p, i64, p]
+        lib.gemm_f16_nt_splitk.restype = ctypes.c_int
+        lib.gemm_f16_nt_splitk_with_config.argtypes = [i64, i64, i64, p, p, p, i32, p, i64, p, i32]
+        lib.gemm_f16_nt_splitk_with_config.restype = ctypes.c_int
         lib.gemm_f16_nt_num_configs.argtypes = []
         lib.gemm_f16_nt_num_configs.restype = ctypes.c_int
         lib.gemm_f16_nt_config_info.argtypes = [i32, ctypes.POINTER(Plan)]
@@ -107,6 +114,30 @@ def gemm_f16_nt_plan(M: int, N: int, K: int, num_cus: int) -> Plan:
     plan = Plan()
     _check(load().gemm_f16_nt_plan(M, N, K, num_cus, ctypes.byref(plan)), "gemm_f16_nt_plan")
     return plan
+
+
+def gemm_f16_nt_splitk_plan(M: int, N: int, K: int, num_cus: int,
+                            splits: int = 0) -> tuple[Plan, int, int]:
+    """(plan, effective splits, workspace bytes) for the split-K entry point."""
+    plan, eff, wsb = Plan(), ctypes.c_int32(), ctypes.c_int64()
+    _check(load().gemm_f16_nt_splitk_plan(M, N, K, num_cus, splits, ctypes.byref(plan),
+                                          ctypes.byref(eff), ctypes.byref(wsb)),
+           "gemm_f16_nt_splitk_plan")
+    return plan, eff.value, wsb.value
+
+
+def gemm_f16_nt_splitk(M: int, N: int, K: int, A: int, B: int, C: int, splits: int,
+                       workspace: int, workspace_bytes: int, stream: int = 0) -> None:
+    _check(load().gemm_f16_nt_splitk(M, N, K, A, B, C, splits, workspace, workspace_bytes,
+                                     stream), "gemm_f16_nt_splitk")
+
+
+def gemm_f16_nt_splitk_with_config(M: int, N: int, K: int, A: int, B: int, C: int,
+                                   splits: int, workspace: int, workspace_bytes: int,
+                                   stream: int, config_id: int) -> None:
+    _check(load().gemm_f16_nt_splitk_with_config(M, N, K, A, B, C, splits, workspace,
+                                                 workspace_bytes, stream, config_id),
+           "gemm_f16_nt_splitk_with_config")
 
 
 def gemm_f16_nt_num_configs() -> int:
@@ -160,4 +191,44 @@ def gemm_nt(a, b, out=None, config: int | None = None, swizzle: int = 0, grid: i
             gemm_f16_nt_with_config(m, n, k, a.data_ptr(), b.data_ptr(), out.data_ptr(),
                                     s.cuda_stream, -1 if config is None else config, swizzle,
                                     grid, epilogue)
+    return out
+
+
+def gemm_nt_splitk(a, b, splits: int = 0, out=None, workspace=None, config: int | None = None,
+                   stream=None):
+    """C = a @ b.T with K split (gemm_f16_nt_splitk) for fp16 tensors a [M,K], b [N,K].
+
+    splits <= 0: the library's choice.  The fp32 workspace is allocated with
+    torch unless `workspace` (a device tensor of at least the planned bytes)
+    is given.  Same checks as gemm_nt.
+    """
+    import torch
+
+    if a.dtype != torch.float16 or b.dtype != torch.float16:
+        raise TypeError("a and b must be torch.float16")
+    if a.dim() != 2 or b.dim() != 2 or a.shape[1] != b.shape[1]:
+        raise ValueError(f"shape mismatch: a{tuple(a.shape)} b{tuple(b.shape)}")
+    if not (a.is_cuda and b.is_cuda) or a.device != b.device:
+        raise ValueError("a and b must be on the same GPU")
+    if not (a.is_contiguous() and b.is_contiguous()):
+        raise ValueError("a and b must be contiguous (row-major)")
+    m, k = a.shape
+    n = b.shape[0]
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float16, device=a.device)
+    elif (out.dtype != torch.float16 or tuple(out.shape) != (m, n) or not out.is_contiguous()
+          or out.device != a.device):
+        raise ValueError("out must be a contiguous float16 [M, N] tensor on a's device")
+    cus = torch.cuda.get_device_properties(a.device).multi_processor_count
+    _, _, need = gemm_f16_nt_splitk_plan(m, n, k, cus, splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=a.device)
+    elif not workspace.is_cuda or workspace.device != a.device:
+        raise ValueError("workspace must be a tensor on a's device")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    s = stream if stream is not None else torch.cuda.current_stream(a.device)
+    with torch.cuda.device(a.device):
+        gemm_f16_nt_splitk_with_config(m, n, k, a.data_ptr(), b.data_ptr(), out.data_ptr(),
+                                       splits, workspace.data_ptr(), ws_bytes, s.cuda_stream,
+                                       -1 if config is None else config)
     return out

@@ -181,6 +181,14 @@ struct Params {
     int32_t tiles_m, tiles_n, tiles;
     int32_t swizzle, grid, xcds;
     int32_t staged;  // 1: stage C through LDS for row-contiguous stores
+    // Split over K: work unit u (after the XCD order) is tile u % (tiles_m *
+    // tiles_n) over K range [s * k_split, min((s + 1) * k_split, K)), s = u /
+    // (tiles_m * tiles_n); `tiles` counts the units.  With splits > 1 each
+    // unit stores its fp32 partial sums to W + s * split_stride (an M x N
+    // row-major matrix) instead of writing C.
+    int32_t splits, k_split;
+    int64_t split_stride;
+    float *W;
 };
 
 // Buffer resource (V#) for raw byte addressing of `bytes` bytes at `base`:
@@ -223,6 +231,7 @@ __device__ __forceinline__ void lds_barrier()
 // Coordinates and buffer resources of one output tile.
 struct Tile {
     int32_t m0, n0;
+    int32_t split, klen;                 // K split index and the unit's K length
     i32x4_t rsrc_a, rsrc_b;              // buffer resources for the DMA asm
 };
 
@@ -230,17 +239,23 @@ template <class CF>
 __device__ __forceinline__ Tile make_tile(const Params &p, int32_t slot, uint32_t row_pitch)
 {
     int32_t tile_m, tile_n;
-    grouped_tile(slot_to_linear(slot, p.grid, p.tiles, p.xcds), p.tiles_m, p.tiles_n,
-                 p.swizzle, tile_m, tile_n);
+    const int32_t unit = slot_to_linear(slot, p.grid, p.tiles, p.xcds);
+    const int32_t tiles_mn = p.tiles_m * p.tiles_n;
     Tile t;
+    t.split = p.splits > 1 ? unit / tiles_mn : 0;
+    grouped_tile(unit - t.split * tiles_mn, p.tiles_m, p.tiles_n, p.swizzle, tile_m, tile_n);
     t.m0 = tile_m * CF::BM;
     t.n0 = tile_n * CF::BN;
-    // the resource covers exactly the tile's valid rows: rows past M (N) read 0
+    const int32_t k0 = t.split * p.k_split;
+    t.klen = min(p.k_split, p.K - k0);
+    // the resource starts at the unit's first column and covers exactly the
+    // tile's valid rows: rows past M (N) read 0; columns past the unit's K
+    // range are never addressed (they get an out-of-range offset)
     const int32_t rows_a = min(CF::BM, p.M - t.m0);
     const int32_t rows_b = min(CF::BN, p.N - t.n0);
-    t.rsrc_a = make_rsrc(p.A + static_cast<int64_t>(t.m0) * p.K,
+    t.rsrc_a = make_rsrc(p.A + static_cast<int64_t>(t.m0) * p.K + k0,
                          static_cast<uint32_t>(rows_a) * row_pitch);
-    t.rsrc_b = make_rsrc(p.B + static_cast<int64_t>(t.n0) * p.K,
+    t.rsrc_b = make_rsrc(p.B + static_cast<int64_t>(t.n0) * p.K + k0,
                          static_cast<uint32_t>(rows_b) * row_pitch);
     return t;
 }
@@ -261,7 +276,7 @@ __device__ __forceinline__ void dma_one(const Params &p, const Tile &t, int stag
     const int row = rblk * CF::DMA_ROWS + lane / CF::CHUNKS;
     const int chunk = (lane % CF::CHUNKS) ^ chunk_swizzle<CF::CHUNKS, CF::MI>(row);
     uint32_t v = static_cast<uint32_t>(row) * row_pitch + chunk * 16 + k0 * 2;
-    if (k0 + chunk * 8 >= static_cast<uint32_t>(p.K)) v = OOB_OFFSET;
+    if (k0 + chunk * 8 >= static_cast<uint32_t>(t.klen)) v = OOB_OFFSET;
     dma16(is_a ? t.rsrc_a : t.rsrc_b, v,
           lds0 + stage * CF::STAGE_BYTES + (is_a ? 0 : CF::A_BYTES) +
               rblk * CF::DMA_ROWS * CF::ROW_BYTES);
@@ -424,6 +439,46 @@ __device__ __forceinline__ void store_tile(const Params &p, const Tile &t,
     }
 }
 
+// Split over K: the unit's fp32 partial sums, in the layout of store_tile, to
+// its M x N slice of the workspace (16-byte stores, masked at M and N).
+template <class CF>
+__device__ __forceinline__ void store_tile_f32(const Params &p, const Tile &t,
+                                               typename CF::Acc (&acc)[CF::FM][CF::FN],
+                                               int wave_m, int wave_n, int lane)
+{
+    float *ws = p.W + t.split * p.split_stride;
+    const int lrow = lane % CF::MI;
+    const int lq = lane / CF::MI;
+#pragma unroll
+    for (int i = 0; i < CF::FM; ++i) {
+        const int32_t m = t.m0 + wave_m * CF::TM + i * CF::MI + lrow;
+        if (m < p.M) {
+            float *wrow = ws + static_cast<int64_t>(m) * p.N;
+#pragma unroll
+            for (int j = 0; j < CF::FN; ++j) {
+                acc_fence<CF>(acc[i][j]);
+#pragma unroll
+                for (int g = 0; g < CF::ACC_N / 4; ++g) {
+                    const int32_t n = t.n0 + wave_n * CF::TN + j * CF::MI +
+                                      (CF::MI == 32 ? g * 8 + lq * 4 : lq * 4);
+                    f32x4_t v;
+                    v.x = acc[i][j][4 * g + 0];
+                    v.y = acc[i][j][4 * g + 1];
+                    v.z = acc[i][j][4 * g + 2];
+                    v.w = acc[i][j][4 * g + 3];
+                    if (n + 3 < p.N) {
+                        __builtin_memcpy(wrow + n, &v, 16);   // rows are 4-byte aligned
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (n + e < p.N) wrow[n + e] = v[e];
+                    }
+                }
+            }
+        }
+    }
+}
+
 // Epilogue staged through LDS (the stage the next tile's prefill leaves
 // free).  Block row i of every wave -- WM * MI tile rows -- is written to LDS
 // as fp16, rows padded by 16 bytes so that the 32 rows one write instruction
@@ -577,7 +632,6 @@ void gemm_f16_nt_kernel(Params p)
 #pragma unroll
     for (int i = 0; i < NVOFF; ++i) dvoff[i] = dma_lane_offset<CF>(i, w.wave, w.lane, w.row_pitch);
     const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(smem));
-    const int KT = (p.K + CF::BK - 1) / CF::BK;
 
     half8_t af[CF::ADB ? 2 : 1][CF::FM], bf[2][CF::FN];
     // A fragment i / B fragment j of step kk of `stage`, into buffer `buf`
@@ -603,6 +657,7 @@ void gemm_f16_nt_kernel(Params p)
     for (int s = 0; s < S - 1; ++s) dma_slice<CF>(p, cur, s, s, lds0, w.wave, w.lane, w.row_pitch);
 
     while (true) {
+        const int KT = (cur.klen + CF::BK - 1) / CF::BK;   // slices of this unit
         typename CF::Acc acc[CF::FM][CF::FN];
         zero_acc<CF>(acc);
         if constexpr (CF::MI == 16) {
@@ -691,7 +746,7 @@ void gemm_f16_nt_kernel(Params p)
             rd = rd_next;
         };
         // slices whose early refill (slice kt + 2) lies wholly inside K, then the rest
-        const int kt_fast = FAST_DMA ? min(max(p.K / CF::BK - 2, 0), KT) : 0;
+        const int kt_fast = FAST_DMA ? min(max(cur.klen / CF::BK - 2, 0), KT) : 0;
         int kt = 0;
         if constexpr (FAST_DMA) {
             // two slices per trip (FAST_DMA implies two stages), so the ring
@@ -725,7 +780,9 @@ void gemm_f16_nt_kernel(Params p)
             for (int s = 0; s < S - 1; ++s)
                 dma_slice<CF>(p, nxt, s, s, lds0, w.wave, w.lane, w.row_pitch);
         }
-        if constexpr (CF::STAGED_OK) {
+        if (p.splits > 1) {
+            store_tile_f32<CF>(p, cur, acc, w.wave_m, w.wave_n, w.lane);
+        } else if constexpr (CF::STAGED_OK) {
             if (p.staged)
                 store_tile_staged<CF>(p, cur, acc, w.wave_m, w.wave_n, w.lane, smem);
             else
@@ -736,6 +793,36 @@ void gemm_f16_nt_kernel(Params p)
         if (next >= p.tiles) break;
         slot = next;
         cur = nxt;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Split-K reduction
+// ---------------------------------------------------------------------------
+// C = fp16_rne(W_0 + W_1 + ... + W_{splits-1}), summed in fp32 in split order,
+// so the result is deterministic.  The partials are M x N row-major and so is
+// C, so both are walked as flat arrays: four elements per thread and step
+// (each partial starts 256-byte aligned, so the fp32 loads are 16-byte
+// aligned), then the last M N mod 4 elements one by one.
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restrict__ W,
+                                                            int32_t splits, int64_t stride,
+                                                            int64_t count, uint16_t *__restrict__ C)
+{
+    const int64_t nvec = count / 4;
+    const int64_t step = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    for (int64_t v = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; v < nvec;
+         v += step) {
+        f32x4_t sum = *reinterpret_cast<const f32x4_t *>(W + 4 * v);
+        for (int32_t s = 1; s < splits; ++s)
+            sum += *reinterpret_cast<const f32x4_t *>(W + s * stride + 4 * v);
+        const half4_t h = __builtin_convertvector(sum, half4_t);
+        __builtin_memcpy(C + 4 * v, &h, 8);   // C is only 2-byte aligned
+    }
+    for (int64_t e = 4 * nvec + static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+         e < count; e += step) {
+        float sum = W[e];
+        for (int32_t s = 1; s < splits; ++s) sum += W[s * stride + e];
+        reinterpret_cast<_Float16 *>(C)[e] = static_cast<_Float16>(sum);
     }
 }
 
@@ -1061,8 +1148,81 @@ static int current_cus(int32_t *cus)
     return GEMM_F16_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Split over K (for tile counts that leave most CUs idle)
+// ---------------------------------------------------------------------------
+constexpr int32_t kMaxSplits = 64;
+constexpr int64_t kMinSplitK = 512;   // K per unit the planner goes down to
+
+// fp32 elements between the partials of consecutive splits: M N rounded up to
+// 64, so each partial starts 256-byte aligned when the workspace does
+static int64_t split_stride(int64_t M, int64_t N) { return cdiv(M * N, 64) * 64; }
+
+// K per unit when K is split `splits` ways for configuration `id`: a multiple
+// of its K slice, so every unit but the last covers whole slices.  The
+// effective split count is then cdiv(K, k_split) <= splits.
+static int64_t split_k_len(int id, int64_t K, int32_t splits)
+{
+    const int64_t bk = kKernels[id].block_k;
+    return cdiv(cdiv(K, splits), bk) * bk;
+}
+
+// Estimated time of configuration `id` with K split `splits` ways: rounds of
+// the persistent grid times one unit's MFMA work at the configuration's
+// relative rate (absolute scale: one CU at about 55% of its dense fp16 peak),
+// plus, when K is actually split, the fp32 partials written and read back at
+// about 4 TB/s and the reduction launch.
+static double split_cost(int id, int64_t M, int64_t N, int64_t K, int32_t splits, int32_t cus,
+                         int64_t *splits_eff)
+{
+    constexpr double kCuFlops = 2.5e15 / 256 * 0.55;
+    constexpr double kBytesPerSec = 4e12;
+    constexpr double kLaunchSec = 4e-6;
+    const KernelEntry &e = kKernels[id];
+    const int64_t ks = split_k_len(id, K, splits);
+    const int64_t eff = cdiv(K, ks);
+    const int64_t units = cdiv(M, e.block_m) * cdiv(N, e.block_n) * eff;
+    const double rounds = static_cast<double>(cdiv(units, cus > 0 ? cus : 1));
+    double t = rounds * e.block_m * e.block_n * static_cast<double>(ks) * 2.0 / (e.rel_rate * kCuFlops);
+    if (eff > 1)
+        t += (2.0 * eff * static_cast<double>(M * N) * 4.0 + static_cast<double>(M * N) * 2.0) /
+                 kBytesPerSec + kLaunchSec;
+    *splits_eff = eff;
+    return t;
+}
+
+// Configuration and effective split count for the split-K entry points
+// (K > 0, direct-to-LDS arguments).  splits > 0 fixes the requested count,
+// config_id >= 0 the configuration; otherwise the cheapest by split_cost.
+// With one split this picks what choose_config picks.
+static void choose_split(int64_t M, int64_t N, int64_t K, int32_t cus, int32_t config_id,
+                         int32_t splits, int *id_out, int32_t *splits_out)
+{
+    double best = 0.0;
+    int best_id = -1;
+    int64_t best_eff = 1;
+    for (int id = 0; id < kNumKernels; ++id) {
+        if (config_id >= 0 ? id != config_id : kKernels[id].rel_rate <= 0.0f) continue;
+        const int32_t s_lo = splits > 0 ? splits : 1;
+        const int32_t s_hi = splits > 0 ? splits : kMaxSplits;
+        for (int32_t sp = s_lo; sp <= s_hi; ++sp) {
+            if (splits <= 0 && sp > 1 && cdiv(K, sp) < kMinSplitK) break;
+            int64_t eff = 1;
+            const double c = split_cost(id, M, N, K, sp, cus, &eff);
+            if (best_id < 0 || c < best) {
+                best = c;
+                best_id = id;
+                best_eff = eff;
+            }
+        }
+    }
+    *id_out = best_id;
+    *splits_out = static_cast<int32_t>(best_eff);
+}
+
 static int launch(const gemm_f16_nt_plan_t &plan, int64_t M, int64_t N, int64_t K,
-                  const void *A, const void *B, void *C, hipStream_t stream)
+                  const void *A, const void *B, void *C, hipStream_t stream,
+                  int32_t splits = 1, int64_t k_split = 0, float *W = nullptr)
 {
     Params p;
     p.A = static_cast<const uint16_t *>(A);
@@ -1078,6 +1238,11 @@ static int launch(const gemm_f16_nt_plan_t &plan, int64_t M, int64_t N, int64_t 
     p.grid = plan.grid;
     p.xcds = plan.xcds;
     p.staged = plan.epilogue;
+    p.splits = splits;
+    p.k_split = static_cast<int32_t>(splits > 1 ? k_split : K);
+    p.split_stride = splits > 1 ? split_stride(M, N) : 0;
+    p.W = W;
+    if (splits > 1) p.tiles = static_cast<int32_t>(plan.tiles * splits);
     const KernelEntry &e = kKernels[plan.config_id];
     void *args[] = {&p};
     // the launch's own status only: the thread's sticky error state (which may
@@ -1110,6 +1275,57 @@ static int run(int64_t M, int64_t N, int64_t K, const void *A, const void *B, vo
         plan.epilogue = epilogue;
     }
     return launch(plan, M, N, K, A, B, C, stream);
+}
+
+static int run_splitk(int64_t M, int64_t N, int64_t K, const void *A, const void *B, void *C,
+                      int32_t splits, void *workspace, int64_t workspace_bytes,
+                      hipStream_t stream, int32_t config_id)
+{
+    const int v = validate(M, N, K, A, B, C);
+    if (v != GEMM_F16_OK) return v;
+    if (config_id >= kNumKernels || splits > kMaxSplits || workspace_bytes < 0)
+        return GEMM_F16_INVALID_ARG;
+    if (M == 0 || N == 0) return GEMM_F16_OK;
+    // arguments only the general kernel takes, and K = 0: no split
+    if (K == 0 || needs_general(K, A, B, true) || (config_id >= 0 && kKernels[config_id].general))
+        return run(M, N, K, A, B, C, stream, config_id, 0, 0, -1);
+    int32_t cus = 0;
+    const int s = current_cus(&cus);
+    if (s != GEMM_F16_OK) return s;
+    int id = -1;
+    int32_t eff = 1;
+    choose_split(M, N, K, cus, config_id, splits, &id, &eff);
+    if (eff <= 1) return run(M, N, K, A, B, C, stream, id, 0, 0, -1);
+    gemm_f16_nt_plan_t plan;
+    make_plan(id, M, N, cus, 0, 0, &plan);
+    if (plan.tiles * eff > INT32_MAX) return GEMM_F16_UNSUPPORTED;
+    const int64_t stride = split_stride(M, N);
+    const int64_t need = eff * stride * 4;
+    if (!workspace || workspace_bytes < need) return GEMM_F16_INVALID_ARG;
+    if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0) return GEMM_F16_UNSUPPORTED;
+    if (overlaps(workspace, need, A, M * K * 2) || overlaps(workspace, need, B, N * K * 2) ||
+        overlaps(workspace, need, C, M * N * 2))
+        return GEMM_F16_INVALID_ARG;
+    const int64_t units = plan.tiles * eff;
+    const int64_t cap = int64_t(cus) * kKernels[id].per_cu;
+    plan.grid = static_cast<int32_t>(units < cap ? units : cap);
+    plan.epilogue = 0;
+    float *W = static_cast<float *>(workspace);
+    const int l = launch(plan, M, N, K, A, B, C, stream, eff, split_k_len(id, K, eff), W);
+    if (l != GEMM_F16_OK) return l;
+    const int64_t count = M * N;
+    const int64_t blocks = cdiv(cdiv(count, 4), 256);
+    const int64_t rgrid = blocks < int64_t(cus) * 8 ? (blocks > 0 ? blocks : 1) : int64_t(cus) * 8;
+    int64_t stride_arg = stride;
+    int64_t count_arg = count;
+    int32_t splits_arg = eff;
+    const float *w_arg = W;
+    uint16_t *c_arg = static_cast<uint16_t *>(C);
+    void *args[] = {&w_arg, &splits_arg, &stride_arg, &count_arg, &c_arg};
+    const hipError_t err = hipLaunchKernel(reinterpret_cast<const void *>(&splitk_reduce_kernel),
+                                           dim3(static_cast<uint32_t>(rgrid)), dim3(256), args, 0,
+                                           stream);
+    return err == hipSuccess ? GEMM_F16_OK : GEMM_F16_LAUNCH_FAILED;
 }
 
 }  // namespace gemm_f16
@@ -1158,6 +1374,51 @@ extern "C" int gemm_f16_nt_plan(int64_t M, int64_t N, int64_t K, int32_t num_cus
                                                               : choose_config(M, N, num_cus);
     make_plan(id, M, N, num_cus, 0, 0, plan);
     return GEMM_F16_OK;
+}
+
+extern "C" int gemm_f16_nt_splitk_plan(int64_t M, int64_t N, int64_t K, int32_t num_cus,
+                                       int32_t splits, gemm_f16_nt_plan_t *plan,
+                                       int32_t *splits_out, int64_t *workspace_bytes)
+{
+    if (!plan || !splits_out || !workspace_bytes || M < 0 || N < 0 || K < 0 || num_cus <= 0 ||
+        splits > kMaxSplits)
+        return GEMM_F16_INVALID_ARG;
+    if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX || cdiv(M, 64) * cdiv(N, 64) > INT32_MAX)
+        return GEMM_F16_UNSUPPORTED;
+    *splits_out = 1;
+    *workspace_bytes = 0;
+    if (K == 0 || M == 0 || N == 0 || needs_general(K, nullptr, nullptr, false))
+        return gemm_f16_nt_plan(M, N, K, num_cus, plan);
+    int id = -1;
+    int32_t eff = 1;
+    choose_split(M, N, K, num_cus, -1, splits, &id, &eff);
+    make_plan(id, M, N, num_cus, 0, 0, plan);
+    if (eff > 1) {
+        if (plan->tiles * eff > INT32_MAX) return GEMM_F16_UNSUPPORTED;
+        const int64_t units = plan->tiles * eff;
+        const int64_t cap = int64_t(num_cus) * kKernels[id].per_cu;
+        plan->grid = static_cast<int32_t>(units < cap ? units : cap);
+        plan->epilogue = 0;
+        *splits_out = eff;
+        *workspace_bytes = eff * split_stride(M, N) * 4;
+    }
+    return GEMM_F16_OK;
+}
+
+extern "C" int gemm_f16_nt_splitk(int64_t M, int64_t N, int64_t K, const void *A, const void *B,
+                                  void *C, int32_t splits, void *workspace,
+                                  int64_t workspace_bytes, hipStream_t stream)
+{
+    return run_splitk(M, N, K, A, B, C, splits, workspace, workspace_bytes, stream, -1);
+}
+
+extern "C" int gemm_f16_nt_splitk_with_config(int64_t M, int64_t N, int64_t K, const void *A,
+                                              const void *B, void *C, int32_t splits,
+                                              void *workspace, int64_t workspace_bytes,
+                                              hipStream_t stream, int32_t config_id)
+{
+    return run_splitk(M, N, K, A, B, C, splits, workspace, workspace_bytes, stream,
+                      config_id < 0 ? -1 : config_id);
 }
 
 extern "C" int gemm_f16_nt_num_configs(void) { return kNumKernels; }

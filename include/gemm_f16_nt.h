@@ -55,7 +55,8 @@ enum {
  *
  * A, B and C are device pointers owned by the caller; they must stay valid
  * until the enqueued work has finished.  The library allocates nothing and
- * uses no workspace.  The call returns once the kernel is enqueued; a fault
+ * uses no workspace (gemm_f16_nt_splitk below is the variant that takes
+ * one).  The call returns once the kernel is enqueued; a fault
  * inside the kernel surfaces at the caller's next synchronisation.
  *
  * M = 0 or N = 0: nothing to compute, returns GEMM_F16_OK without a launch.
@@ -133,6 +134,60 @@ int gemm_f16_nt_with_config(int64_t M, int64_t N, int64_t K,
                             const void *A, const void *B, void *C,
                             hipStream_t stream, int32_t config_id,
                             int32_t swizzle, int32_t grid, int32_t epilogue);
+
+/*
+ * Split over K, for shapes whose output tiles leave most compute units idle
+ * (a small M x N with a long K).  The pages split the work over output tiles
+ * only, and note what an under-filled last round of tiles costs (Tilus
+ * tutorial "Hopper matmul", page "6. Register Reallocation, Multicast, and a
+ * Persistent Kernel", the results and the closing caution on other shapes).
+ * Here K is also cut into `splits` ranges of whole K slices, one work unit
+ * per (range, output tile); each unit writes its fp32 partial sums to a
+ * caller-provided workspace, and a second kernel on the same stream forms
+ *
+ *     C[i][j] = fp16_rne( P_0[i][j] + P_1[i][j] + ... )      (fp32, in range order)
+ *
+ * so results are deterministic, but they differ from gemm_f16_nt's in the
+ * fp32 rounding of the sum (exact for sums that fp32 represents exactly,
+ * e.g. small integers).
+ *
+ * gemm_f16_nt_splitk_plan: pure host function.  For (M, N, K) on `num_cus`
+ * compute units and 16-byte aligned A and B, writes the kernel configuration
+ * (plan, with grid = the persistent grid over all units), the effective split
+ * count (*splits_out, at most `splits`: ranges are whole K slices) and the
+ * workspace size in bytes (*workspace_bytes, 0 when there is no split).
+ * splits <= 0 lets the library choose (it weighs the rounds of MFMA work
+ * against the partial-sum traffic); splits = 1 is gemm_f16_nt's plan.
+ * GEMM_F16_INVALID_ARG for NULL outputs, negative sizes, num_cus <= 0 or
+ * splits > 64.
+ *
+ * gemm_f16_nt_splitk: C = A * B^T with K split as the plan above says, for
+ * the current device.  `workspace` is caller-owned device memory, 16-byte
+ * aligned (else GEMM_F16_UNSUPPORTED), of at least the planned bytes, not
+ * overlapping A, B or C (else GEMM_F16_INVALID_ARG); its contents on entry
+ * do not matter and are overwritten.  It may be NULL when the plan has no
+ * split.  Concurrent calls need separate workspaces unless they are ordered
+ * on one stream.  Arguments only the general kernel takes (K not a multiple
+ * of 8 or above 2^21, A or B not 16-byte aligned), K = 0, and a plan with
+ * one split run gemm_f16_nt itself, with the same result.  Otherwise the
+ * same semantics, ownership and status codes as gemm_f16_nt, plus
+ * GEMM_F16_INVALID_ARG for splits > 64.
+ *
+ * gemm_f16_nt_splitk_with_config: the same with the kernel configuration
+ * fixed (config_id < 0: the planner's choice), for tests and sweeps.
+ */
+int gemm_f16_nt_splitk_plan(int64_t M, int64_t N, int64_t K, int32_t num_cus,
+                            int32_t splits, gemm_f16_nt_plan_t *plan,
+                            int32_t *splits_out, int64_t *workspace_bytes);
+int gemm_f16_nt_splitk(int64_t M, int64_t N, int64_t K,
+                       const void *A, const void *B, void *C,
+                       int32_t splits, void *workspace, int64_t workspace_bytes,
+                       hipStream_t stream);
+int gemm_f16_nt_splitk_with_config(int64_t M, int64_t N, int64_t K,
+                                   const void *A, const void *B, void *C,
+                                   int32_t splits, void *workspace,
+                                   int64_t workspace_bytes, hipStream_t stream,
+                                   int32_t config_id);
 
 /*
  * The tile order the kernel walks (Tilus tutorial "Hopper matmul", page

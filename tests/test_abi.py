@@ -206,3 +206,75 @@ def test_wave_quantization_figure(g):
     assert round((1 - (rounds - int(rounds))) * 100) == fig["idle_fraction_last_round_percent"]
     p = g.gemm_f16_nt_plan(8192, 8192, 8192, 256)
     assert p.tiles % p.grid == 0 and p.tiles // p.grid == 4
+
+
+# ---------------------------------------------------------------------------
+# split over K: the planner (pure host functions)
+# ---------------------------------------------------------------------------
+def _split_stride(m, n):
+    return -(-m * n // 64) * 64
+
+
+@pytest.mark.parametrize("shape", [(256, 256, 65536), (512, 512, 65536), (300, 200, 100000),
+                                   (64, 64, 1 << 20), (256, 256, 4096)])
+def test_splitk_plan_splits_underfilled_shapes(g, shape):
+    m, n, k = shape
+    plan, eff, ws = g.gemm_f16_nt_splitk_plan(m, n, k, 256)
+    assert 1 < eff <= 64
+    assert ws == eff * _split_stride(m, n) * 4
+    assert plan.tiles == plan.tiles_m * plan.tiles_n
+    assert plan.grid == min(plan.tiles * eff, 256)
+    # more work units than the tiles alone give
+    assert plan.tiles * eff > g.gemm_f16_nt_plan(m, n, k, 256).tiles
+
+
+@pytest.mark.parametrize("shape", [(8192, 8192, 8192), (4999, 7001, 4160), (128, 16384, 16384),
+                                   (4096, 4096, 4096), (1024, 1024, 1024), (256, 256, 256)])
+def test_splitk_plan_keeps_filled_shapes_whole(g, shape):
+    plan, eff, ws = g.gemm_f16_nt_splitk_plan(*shape, 256)
+    p1 = g.gemm_f16_nt_plan(*shape, 256)
+    assert eff == 1 and ws == 0
+    assert plan.as_dict() == p1.as_dict()
+
+
+@pytest.mark.parametrize("shape", [(256, 256, 65536), (300, 200, 100000), (77, 129, 2056)])
+def test_splitk_plan_one_split_is_the_plain_plan(g, shape):
+    plan, eff, ws = g.gemm_f16_nt_splitk_plan(*shape, 256, 1)
+    assert eff == 1 and ws == 0
+    assert plan.as_dict() == g.gemm_f16_nt_plan(*shape, 256).as_dict()
+
+
+@pytest.mark.parametrize("splits", [2, 3, 5, 7, 16, 64])
+@pytest.mark.parametrize("k", [64, 200, 2056, 40000])
+def test_splitk_plan_forced_count(g, splits, k):
+    plan, eff, ws = g.gemm_f16_nt_splitk_plan(77, 129, k, 256, splits)
+    bk = plan.block_k
+    ks = -(-(-(-k // splits)) // bk) * bk          # K per unit: whole slices
+    assert eff == -(-k // ks) and 1 <= eff <= splits
+    assert (eff - 1) * ks < k                       # no empty unit
+    assert ws == (eff * _split_stride(77, 129) * 4 if eff > 1 else 0)
+
+
+@pytest.mark.parametrize("k", [0, 1, 60, 4097, (1 << 21) + 8])
+def test_splitk_plan_no_split_where_the_plain_path_runs(g, k):
+    plan, eff, ws = g.gemm_f16_nt_splitk_plan(300, 200, k, 256, 8)
+    assert eff == 1 and ws == 0
+    assert plan.as_dict() == g.gemm_f16_nt_plan(300, 200, k, 256).as_dict()
+
+
+def test_splitk_plan_invalid(g):
+    for args in [(64, 64, 64, 256, 65), (-1, 64, 64, 256, 0), (64, 64, 64, 0, 0)]:
+        with pytest.raises(g.GemmError) as e:
+            g.gemm_f16_nt_splitk_plan(*args)
+        assert e.value.status == 1
+
+
+def test_splitk_host_checks_before_any_device_access(g):
+    lib = g.load()
+    # nothing to compute: OK without a launch; bad sizes and split counts: INVALID_ARG
+    assert lib.gemm_f16_nt_splitk(0, 64, 64, A0, B0, C0, 4, 0, 0, None) == 0
+    assert lib.gemm_f16_nt_splitk(64, 0, 64, A0, B0, C0, 4, 0, 0, None) == 0
+    assert lib.gemm_f16_nt_splitk(-1, 64, 64, A0, B0, C0, 4, 0, 0, None) == 1
+    assert lib.gemm_f16_nt_splitk(64, 64, 64, A0, B0, C0, 65, 0, 0, None) == 1
+    assert lib.gemm_f16_nt_splitk(64, 64, 64, A0, B0, C0, 4, 0, -1, None) == 1
+    assert lib.gemm_f16_nt_splitk(64, 64, 64, A0, B0, A0, 4, 0, 0, None) == 1   # C overlaps A
