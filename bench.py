@@ -115,6 +115,9 @@ def main() -> int:
     ap.add_argument("--grid", type=int, default=0)
     ap.add_argument("--epilogue", type=int, default=-1,
                     help="-1: library choice, 0: direct stores, 1: staged through LDS")
+    ap.add_argument("--splitk", type=int, default=None,
+                    help="time gemm_f16_nt_splitk with this many K splits (0: the library's "
+                         "choice); a step is then the split GEMM and its reduction")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -141,7 +144,7 @@ def main() -> int:
     if args.copy_bytes > 0:
         return copy_probe(args)
     name = args.workload or workloads.HEADLINE
-    w = workloads.WORKLOADS[name]
+    w = workloads.ALL_WORKLOADS[name]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
@@ -161,9 +164,22 @@ def main() -> int:
 
     stream = torch.cuda.current_stream(dev)
 
-    def launch():
-        g.gemm_nt(a, b, out=c, config=args.config, swizzle=args.swizzle, grid=args.grid,
-                  stream=stream, epilogue=args.epilogue)
+    if args.splitk is not None:
+        # the workspace is allocated once, before anything is timed
+        sk_plan, splits, ws_bytes = g.gemm_f16_nt_splitk_plan(w.M, w.N, w.K, cus, args.splitk)
+        plan = sk_plan.as_dict()
+        plan.update({"splits": splits, "workspace_bytes": ws_bytes})
+        ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+
+        def launch():
+            g.gemm_f16_nt_splitk_with_config(w.M, w.N, w.K, a.data_ptr(), b.data_ptr(),
+                                             c.data_ptr(), args.splitk, ws.data_ptr(), ws_bytes,
+                                             stream.cuda_stream,
+                                             -1 if args.config is None else args.config)
+    else:
+        def launch():
+            g.gemm_nt(a, b, out=c, config=args.config, swizzle=args.swizzle, grid=args.grid,
+                      stream=stream, epilogue=args.epilogue)
 
     # cooldown first (the pages' protocol), then the warm-up launches bring
     # the clock back up from idle before the timed window opens
@@ -194,7 +210,7 @@ def main() -> int:
 
     tflops = w.flops / (ms_per_step * 1e-3) / 1e12
     compute_bound = w.flops / w.algorithmic_bytes > (PEAK_FP16_TFLOPS * 1e12) / (PEAK_HBM_GBS * 1e9)
-    traffic = measured_traffic(name)
+    traffic = measured_traffic(name if args.splitk is None else f"{name}_splitk")
     if compute_bound:
         achieved = w.flops / (kernel_avg_ms * 1e-3) / 1e12
         roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP16_TFLOPS,

@@ -155,3 +155,21 @@ def test_splitk_torch_wrapper(g, oracle_mod):
     c = g.gemm_nt_splitk(torch.from_numpy(a).cuda(), torch.from_numpy(b).cuda())
     torch.cuda.synchronize()
     assert_within_tolerance(c.cpu().numpy(), oracle_mod.gemm(a, b), "gemm_nt_splitk")
+
+
+@pytest.mark.parametrize("name", list(workloads.EXTRA_WORKLOADS))
+def test_full_size_underfilled_workload(g, oracle_mod, name):
+    """The under-filled workload at full size, split as the benchmark's
+    --splitk 0 launch splits it; sampled elements (random positions plus the
+    first and last rows and the last column) against the oracle."""
+    w = workloads.EXTRA_WORKLOADS[name]
+    a, b = workloads.workload_inputs(name)
+    got, eff = run_splitk(g, a, b, 0)
+    assert eff > 1
+    assert not np.isnan(got).any(), "unwritten (NaN-poisoned) output elements"
+    rng = np.random.default_rng(w.seed)
+    rows = [rng.integers(0, w.M, 4096), np.zeros(w.N, np.int64), np.full(w.N, w.M - 1),
+            np.arange(w.M)]
+    cols = [rng.integers(0, w.N, 4096), np.arange(w.N), np.arange(w.N), np.full(w.M, w.N - 1)]
+    r, c = np.concatenate(rows), np.concatenate(cols)
+    assert_within_tolerance(got[r, c], oracle_mod.gemm_sampled(a, b, r, c), name)

@@ -65,6 +65,19 @@ WORKLOADS = {
     )
 }
 
+#: A shape beyond the five: an output whose tiles leave most compute units
+#: idle (16 tiles of 256 x 256) over a long reduction, the case the split over
+#: K is for.  Not a workload of the pages.
+EXTRA_WORKLOADS = {
+    w.name: w
+    for w in (
+        Workload("underfilled1024x1024x65536", 1024, 1024, 65536, "uniform", _inv_sqrt(65536),
+                 106, "entries uniform in [-1, 1]/sqrt(K): few output tiles, a long K"),
+    )
+}
+
+ALL_WORKLOADS = {**WORKLOADS, **EXTRA_WORKLOADS}
+
 #: The workload the benchmark times.
 HEADLINE = "square8192"
 
@@ -94,5 +107,5 @@ def make_inputs(M: int, N: int, K: int, dist: str = "uniform", scale: float = 1.
 
 
 def workload_inputs(name: str):
-    w = WORKLOADS[name]
+    w = ALL_WORKLOADS[name]
     return make_inputs(w.M, w.N, w.K, w.dist, w.scale, w.seed)
