@@ -33,7 +33,8 @@ class Plan(ctypes.Structure):
                 ("config_id", "block_m", "block_n", "block_k", "waves", "stages",
                  "swizzle", "tiles_m", "tiles_n", "grid")] + \
                [("tiles", ctypes.c_int64), ("lds_bytes", ctypes.c_int32),
-                ("xcds", ctypes.c_int32), ("epilogue", ctypes.c_int32)]
+                ("xcds", ctypes.c_int32), ("epilogue", ctypes.c_int32),
+                ("b_layout", ctypes.c_int32)]
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -72,6 +73,12 @@ def load():
         lib.gemm_f16_nt_splitk.restype = ctypes.c_int
         lib.gemm_f16_nt_splitk_with_config.argtypes = [i64, i64, i64, p, p, p, i32, p, i64, p, i32]
         lib.gemm_f16_nt_splitk_with_config.restype = ctypes.c_int
+        lib.gemm_f16_nn.argtypes = [i64, i64, i64, p, p, p, p]
+        lib.gemm_f16_nn.restype = ctypes.c_int
+        lib.gemm_f16_nn_with_config.argtypes = [i64, i64, i64, p, p, p, p, i32, i32, i32, i32]
+        lib.gemm_f16_nn_with_config.restype = ctypes.c_int
+        lib.gemm_f16_nn_plan.argtypes = [i64, i64, i64, i32, ctypes.POINTER(Plan)]
+        lib.gemm_f16_nn_plan.restype = ctypes.c_int
         lib.gemm_f16_nt_num_configs.argtypes = []
         lib.gemm_f16_nt_num_configs.restype = ctypes.c_int
         lib.gemm_f16_nt_config_info.argtypes = [i32, ctypes.POINTER(Plan)]
@@ -113,6 +120,25 @@ def gemm_f16_nt_validate(M: int, N: int, K: int, A: int, B: int, C: int) -> int:
 def gemm_f16_nt_plan(M: int, N: int, K: int, num_cus: int) -> Plan:
     plan = Plan()
     _check(load().gemm_f16_nt_plan(M, N, K, num_cus, ctypes.byref(plan)), "gemm_f16_nt_plan")
+    return plan
+
+
+def gemm_f16_nn(M: int, N: int, K: int, A: int, B: int, C: int, stream: int = 0) -> None:
+    """C = A * B for device pointers A [M,K], B [K,N], C [M,N] (fp16)."""
+    _check(load().gemm_f16_nn(M, N, K, A, B, C, stream), "gemm_f16_nn")
+
+
+def gemm_f16_nn_with_config(M: int, N: int, K: int, A: int, B: int, C: int, stream: int,
+                            config_id: int, swizzle: int = 0, grid: int = 0,
+                            epilogue: int = -1) -> None:
+    _check(load().gemm_f16_nn_with_config(M, N, K, A, B, C, stream, config_id, swizzle, grid,
+                                          epilogue),
+           "gemm_f16_nn_with_config")
+
+
+def gemm_f16_nn_plan(M: int, N: int, K: int, num_cus: int) -> Plan:
+    plan = Plan()
+    _check(load().gemm_f16_nn_plan(M, N, K, num_cus, ctypes.byref(plan)), "gemm_f16_nn_plan")
     return plan
 
 
@@ -231,4 +257,33 @@ def gemm_nt_splitk(a, b, splits: int = 0, out=None, workspace=None, config: int 
         gemm_f16_nt_splitk_with_config(m, n, k, a.data_ptr(), b.data_ptr(), out.data_ptr(),
                                        splits, workspace.data_ptr(), ws_bytes, s.cuda_stream,
                                        -1 if config is None else config)
+    return out
+
+
+def gemm_nn(a, b, out=None, config: int | None = None, swizzle: int = 0, grid: int = 0,
+            stream=None, epilogue: int = -1):
+    """C = a @ b for fp16 tensors a [M,K] and b [K,N] (gemm_f16_nn).  Same
+    checks as gemm_nt."""
+    import torch
+
+    if a.dtype != torch.float16 or b.dtype != torch.float16:
+        raise TypeError("a and b must be torch.float16")
+    if a.dim() != 2 or b.dim() != 2 or a.shape[1] != b.shape[0]:
+        raise ValueError(f"shape mismatch: a{tuple(a.shape)} b{tuple(b.shape)}")
+    if not (a.is_cuda and b.is_cuda) or a.device != b.device:
+        raise ValueError("a and b must be on the same GPU")
+    if not (a.is_contiguous() and b.is_contiguous()):
+        raise ValueError("a and b must be contiguous (row-major)")
+    m, k = a.shape
+    n = b.shape[1]
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float16, device=a.device)
+    elif (out.dtype != torch.float16 or tuple(out.shape) != (m, n) or not out.is_contiguous()
+          or out.device != a.device):
+        raise ValueError("out must be a contiguous float16 [M, N] tensor on a's device")
+    s = stream if stream is not None else torch.cuda.current_stream(a.device)
+    with torch.cuda.device(a.device):
+        gemm_f16_nn_with_config(m, n, k, a.data_ptr(), b.data_ptr(), out.data_ptr(),
+                                s.cuda_stream, -1 if config is None else config, swizzle,
+                                grid, epilogue)
     return out

@@ -115,6 +115,25 @@ __host__ __device__ constexpr int chunk_swizzle(int r)
     return CHUNKS == 8 ? ((r & 7) ^ ((r >> 3) & 3)) : (((r >> 1) & 3) ^ ((r >> 3) & 1));
 }
 
+// B stored [K, N] (N contiguous): its LDS tile keeps that layout, one row of
+// BN halves per k, and the MFMA fragments are read with the transposing LDS
+// read (ds_read_b64_tr_b16).  Within each group of 16 lanes that read takes
+// the 8-byte pieces the 16 lanes address as a 16 x 4 block and returns to lane
+// j element j % 4 of the pieces of lanes j / 4, j / 4 + 4, j / 4 + 8 and
+// j / 4 + 12 (measured).  Lane i addressing row k0 + i / 4 at columns
+// n0 + 4 (i % 4) .. + 3 therefore gets column n0 + j at rows k0 .. k0 + 3:
+// four consecutive k of one n, the 16x16x32 operand layout; two reads make
+// the lane's eight.  One read touches 16 rows (4 per lane group, groups 8
+// rows apart) at 32 bytes each; rows of 256 or 512 bytes start on the same
+// bank, so each row's 16-byte chunks are XORed with an even value that spreads
+// those 16 rows over 8 distinct 32-byte windows (two rows per window, the
+// minimum for 512 bytes):
+//   chunk ^ 2 ((k & 3) | ((k >> 3) & 1) << 2)
+__host__ __device__ constexpr int kn_swizzle(int k)
+{
+    return 2 * ((k & 3) | (((k >> 3) & 1) << 2));
+}
+
 // MI_ picks the MFMA: 32 -> v_mfma_f32_32x32x16_f16 (16 accumulators per lane
 // per block), 16 -> v_mfma_f32_16x16x32_f16 (4 per block: half the
 // accumulator register traffic per flop).
@@ -122,10 +141,13 @@ __host__ __device__ constexpr int chunk_swizzle(int r)
 // early, during the last step of the slice two before it, right after the
 // barrier that frees their stage; the rest go out during the slice before.
 // ADB_: double-buffer the A fragments as well as the B fragments.
+// BL_: B's layout in memory: 0 = [N, K] (K contiguous, the pages' NT form),
+// 1 = [K, N] (N contiguous: C = A B with B row-major).
 template <int BM_, int BN_, int BK_, int WM_, int WN_, int STAGES_, int MI_ = 32,
-          int DSTEPS_ = 0, int DX_ = 0, int ADB_ = 0>
+          int DSTEPS_ = 0, int DX_ = 0, int ADB_ = 0, int BL_ = 0>
 struct Cfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, STAGES = STAGES_;
+    static constexpr int BL = BL_;
     static constexpr int MI = MI_;               // MFMA block edge (M and N)
     static constexpr int MK = 512 / MI;          // K per MFMA: 16 or 32
     static constexpr int ACC_N = MI * MI / 64;   // accumulators per lane per block
@@ -152,7 +174,18 @@ struct Cfg {
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
     static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
     static constexpr int A_LOADS = BM / DMA_ROWS / WAVES;    // DMA instructions per wave per stage
-    static constexpr int B_LOADS = BN / DMA_ROWS / WAVES;
+    // the B tile in LDS: BN rows of BK halves (BL 0, like A) or BK rows of
+    // BN halves (BL 1)
+    static constexpr int B_ROW_BYTES = BL ? BN * 2 : ROW_BYTES;
+    static constexpr int B_CHUNKS = B_ROW_BYTES / 16;
+    static constexpr int B_DMA_ROWS = DMA_BYTES / B_ROW_BYTES;
+    static constexpr int B_LOADS = (BL ? BK : BN) / B_DMA_ROWS / WAVES;
+    // [K, N] B: instruction ip covers rows ip * B_RB + ...; kn_swizzle repeats
+    // every 16 rows, so lane offsets repeat every B_NB instructions and the
+    // rest is a multiple of 16 rows, carried in the scalar offset
+    static constexpr int B_RB = WAVES * B_DMA_ROWS;
+    static constexpr int B_NB = (16 / (B_RB < 16 ? B_RB : 16)) < B_LOADS
+                                    ? (16 / (B_RB < 16 ? B_RB : 16)) : B_LOADS;
     static constexpr int LOADS = A_LOADS + B_LOADS;
     // the LDS-staged epilogue writes one block row of every wave (WM * MI tile
     // rows of BN halves, rows padded by 16 bytes) into one ring stage
@@ -162,8 +195,11 @@ struct Cfg {
     static_assert(MI == 32 || MI == 16, "MFMA is 32x32x16 or 16x16x32");
     static_assert(MI == 32 || CHUNKS == 8, "16x16x32 fragments need 128-byte rows");
     static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be whole 32-row blocks");
-    static_assert(BM % (DMA_ROWS * WAVES) == 0 && BN % (DMA_ROWS * WAVES) == 0,
+    static_assert(BM % (DMA_ROWS * WAVES) == 0 &&
+                      (BL ? BK % (B_DMA_ROWS * WAVES) : BN % (DMA_ROWS * WAVES)) == 0,
                   "every wave issues the same number of DMA instructions");
+    static_assert(BL == 0 || (MI == 16 && (BN == 128 || BN == 256) && BK % 32 == 0),
+                  "[K, N] B: 16x16x32 fragments, 256- or 512-byte rows");
     static_assert(STAGES >= 2, "need at least a double buffer");
     static_assert(LDS_BYTES <= LDS_LIMIT, "LDS ring exceeds 160 KB");
     static_assert((STAGES - 1) * LOADS <= 63, "vmcnt counts at most 63 loads");
@@ -235,19 +271,28 @@ struct Tile {
     i32x4_t rsrc_a, rsrc_b;              // buffer resources for the DMA asm
 };
 
-template <class CF>
+// SPLIT: the kernel instance for K split into ranges (see Params); the
+// unsplit instance carries none of that arithmetic.
+template <class CF, bool SPLIT>
 __device__ __forceinline__ Tile make_tile(const Params &p, int32_t slot, uint32_t row_pitch)
 {
     int32_t tile_m, tile_n;
     const int32_t unit = slot_to_linear(slot, p.grid, p.tiles, p.xcds);
-    const int32_t tiles_mn = p.tiles_m * p.tiles_n;
     Tile t;
-    t.split = p.splits > 1 ? unit / tiles_mn : 0;
-    grouped_tile(unit - t.split * tiles_mn, p.tiles_m, p.tiles_n, p.swizzle, tile_m, tile_n);
+    int32_t k0 = 0;
+    if constexpr (SPLIT) {
+        const int32_t tiles_mn = p.tiles_m * p.tiles_n;
+        t.split = unit / tiles_mn;
+        grouped_tile(unit - t.split * tiles_mn, p.tiles_m, p.tiles_n, p.swizzle, tile_m, tile_n);
+        k0 = t.split * p.k_split;
+        t.klen = min(p.k_split, p.K - k0);
+    } else {
+        t.split = 0;
+        grouped_tile(unit, p.tiles_m, p.tiles_n, p.swizzle, tile_m, tile_n);
+        t.klen = p.K;
+    }
     t.m0 = tile_m * CF::BM;
     t.n0 = tile_n * CF::BN;
-    const int32_t k0 = t.split * p.k_split;
-    t.klen = min(p.k_split, p.K - k0);
     // the resource starts at the unit's first column and covers exactly the
     // tile's valid rows: rows past M (N) read 0; columns past the unit's K
     // range are never addressed (they get an out-of-range offset)
@@ -255,8 +300,17 @@ __device__ __forceinline__ Tile make_tile(const Params &p, int32_t slot, uint32_
     const int32_t rows_b = min(CF::BN, p.N - t.n0);
     t.rsrc_a = make_rsrc(p.A + static_cast<int64_t>(t.m0) * p.K + k0,
                          static_cast<uint32_t>(rows_a) * row_pitch);
-    t.rsrc_b = make_rsrc(p.B + static_cast<int64_t>(t.n0) * p.K + k0,
-                         static_cast<uint32_t>(rows_b) * row_pitch);
+    if constexpr (CF::BL == 0) {
+        t.rsrc_b = make_rsrc(p.B + static_cast<int64_t>(t.n0) * p.K + k0,
+                             static_cast<uint32_t>(rows_b) * row_pitch);
+    } else {
+        // [K, N]: rows are k.  The resource starts at (k0, n0) and spans the
+        // unit's rows; columns past N get out-of-range offsets per lane
+        // (the host keeps K N 2 below 2^32)
+        t.rsrc_b = make_rsrc(p.B + static_cast<int64_t>(k0) * p.N + t.n0,
+                             static_cast<uint32_t>(t.klen) * static_cast<uint32_t>(p.N) * 2u -
+                                 static_cast<uint32_t>(t.n0) * 2u);
+    }
     return t;
 }
 
@@ -273,6 +327,19 @@ __device__ __forceinline__ void dma_one(const Params &p, const Tile &t, int stag
     const uint32_t k0 = static_cast<uint32_t>(kt) * CF::BK;
     const bool is_a = i < CF::A_LOADS;
     const int rblk = (is_a ? i : i - CF::A_LOADS) * CF::WAVES + wave;
+    if constexpr (CF::BL == 1) {
+        if (!is_a) {
+            // row k0 + r of the [K, N] tile: lane l fetches logical chunk
+            // (l % B_CHUNKS) ^ kn_swizzle(r) of it (8 columns), zero past K or N
+            const int r = rblk * CF::B_DMA_ROWS + lane / CF::B_CHUNKS;
+            const int chunk = (lane % CF::B_CHUNKS) ^ kn_swizzle(r);
+            const uint32_t ldb = static_cast<uint32_t>(p.N) * 2u;
+            uint32_t v = (k0 + r) * ldb + chunk * 16;
+            if (k0 + r >= static_cast<uint32_t>(t.klen) || t.n0 + chunk * 8 >= p.N) v = OOB_OFFSET;
+            dma16(t.rsrc_b, v, lds0 + stage * CF::STAGE_BYTES + CF::A_BYTES + rblk * DMA_BYTES);
+            return;
+        }
+    }
     const int row = rblk * CF::DMA_ROWS + lane / CF::CHUNKS;
     const int chunk = (lane % CF::CHUNKS) ^ chunk_swizzle<CF::CHUNKS, CF::MI>(row);
     uint32_t v = static_cast<uint32_t>(row) * row_pitch + chunk * 16 + k0 * 2;
@@ -296,6 +363,19 @@ __device__ __forceinline__ uint32_t dma_lane_offset(int ip, int wave, int lane, 
     const int row = rblk * CF::DMA_ROWS + lane / CF::CHUNKS;
     const int chunk = (lane % CF::CHUNKS) ^ chunk_swizzle<CF::CHUNKS, CF::MI>(row);
     return static_cast<uint32_t>(row) * row_pitch + chunk * 16;
+}
+
+// The same for the [K, N] B tile: fixed per tile (its columns past N get an
+// out-of-range offset), with the slice's row offset k0 N 2 in the scalar
+// offset.
+template <class CF>
+__device__ __forceinline__ uint32_t dma_lane_offset_kn(int ip, int wave, int lane, int32_t n0,
+                                                       int32_t N)
+{
+    const int r = (ip * CF::WAVES + wave) * CF::B_DMA_ROWS + lane / CF::B_CHUNKS;
+    const int chunk = (lane % CF::B_CHUNKS) ^ kn_swizzle(r);
+    if (n0 + chunk * 8 >= N) return OOB_OFFSET;
+    return static_cast<uint32_t>(r) * static_cast<uint32_t>(N) * 2u + chunk * 16;
 }
 
 template <class CF>
@@ -555,6 +635,13 @@ struct WaveCtx {
     // swizzle depends on the row mod 32, so a 16-row block at an odd multiple
     // of 16 (parity 1) sees a different pattern.
     uint32_t frag_off[2][CF::KK];
+    // [K, N] B: the lane's byte offset in the B tile for the first
+    // transposing read of step 0 of fragment 0 (row 8 (l / 16) + (l % 16) / 4,
+    // columns 4 (l % 4) of the wave's block).  Fragment j's 16 columns sit 2 j
+    // chunks on, in chunk bits the swizzle XOR shares but the wave's and the
+    // lane's own bits do not, so its offset is btr0 ^ 32 j.  Later steps and
+    // the second read (4 rows on) keep the row's swizzle: constant offsets.
+    uint32_t btr0;
 
     __device__ __forceinline__ WaveCtx(const Params &p)
     {
@@ -576,8 +663,24 @@ struct WaveCtx {
             }
         a_frag_base = wave_m * CF::TM * CF::ROW_BYTES;
         b_frag_base = CF::A_BYTES + wave_n * CF::TN * CF::ROW_BYTES;
+        btr0 = 0;
+        if constexpr (CF::BL == 1) {
+            static_assert(CF::TN % 128 == 0 || CF::TN == 64, "wave column offset clear of the XOR bits");
+            const int r = 8 * (lane / 16) + (lane % 16) / 4;
+            const int n = wave_n * CF::TN + 4 * (lane % 4);
+            btr0 = r * CF::B_ROW_BYTES + (((n / 8) ^ kn_swizzle(r)) * 16) + (n % 8) * 2;
+        }
     }
 };
+
+// One transposing LDS read (see kn_swizzle): four 16-bit elements.
+__device__ __forceinline__ half4_t lds_read_tr16(const uint8_t *p)
+{
+    typedef short s4_t __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s4_t lds_s4_t;
+    const s4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_t *)(p));
+    return __builtin_bit_cast(half4_t, v);
+}
 
 template <class CF>
 __device__ __forceinline__ void zero_acc(typename CF::Acc (&acc)[CF::FM][CF::FN])
@@ -593,7 +696,7 @@ __device__ __forceinline__ void zero_acc(typename CF::Acc (&acc)[CF::FM][CF::FN]
 // ---------------------------------------------------------------------------
 // Kernel, direct-to-LDS fill
 // ---------------------------------------------------------------------------
-template <class CF>
+template <class CF, bool SPLIT>
 __global__ __launch_bounds__(CF::THREADS)
 __attribute__((amdgpu_waves_per_eu(CF::WAVES_PER_SIMD, CF::WAVES_PER_SIMD)))
 void gemm_f16_nt_kernel(Params p)
@@ -627,10 +730,16 @@ void gemm_f16_nt_kernel(Params p)
     // With two stages and the whole refill issued early, the refill of a
     // slice wholly inside K takes the fast form (dma_full).
     constexpr bool FAST_DMA = S == 2 && DX == L;
-    constexpr int NVOFF = FAST_DMA ? (CF::A_LOADS > CF::B_LOADS ? CF::A_LOADS : CF::B_LOADS) : 1;
+    // fast-form lane offsets: shared by the A and B parts for [N, K] B; for
+    // [K, N] B the B part has its own, set per tile
+    constexpr int NVOFF = !FAST_DMA ? 1
+                          : CF::BL ? CF::A_LOADS
+                                   : (CF::A_LOADS > CF::B_LOADS ? CF::A_LOADS : CF::B_LOADS);
     uint32_t dvoff[NVOFF];
 #pragma unroll
     for (int i = 0; i < NVOFF; ++i) dvoff[i] = dma_lane_offset<CF>(i, w.wave, w.lane, w.row_pitch);
+    uint32_t dvoffb[FAST_DMA && CF::BL ? CF::B_NB : 1];
+    const uint32_t ldb = static_cast<uint32_t>(p.N) * 2u;   // [K, N] B row pitch
     const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(smem));
 
     half8_t af[CF::ADB ? 2 : 1][CF::FM], bf[2][CF::FN];
@@ -641,15 +750,28 @@ void gemm_f16_nt_kernel(Params p)
                                                     i * CF::MI * CF::ROW_BYTES);
     };
     auto read_b = [&](int buf, int stage, int kk, int j) {
-        bf[buf][j] = *reinterpret_cast<const half8_t *>(smem + stage * CF::STAGE_BYTES +
-                                                         w.frag_off[j & 1][kk] + w.b_frag_base +
-                                                         j * CF::MI * CF::ROW_BYTES);
+        if constexpr (CF::BL == 0) {
+            bf[buf][j] = *reinterpret_cast<const half8_t *>(smem + stage * CF::STAGE_BYTES +
+                                                             w.frag_off[j & 1][kk] + w.b_frag_base +
+                                                             j * CF::MI * CF::ROW_BYTES);
+        } else {
+            // the XOR is issued at the read (an asm the compiler cannot hoist):
+            // hoisted, the FN offsets would each hold a register for the
+            // whole loop
+            uint32_t off;
+            asm volatile("v_xor_b32 %0, %2, %1" : "=v"(off) : "v"(w.btr0), "n"(32 * j));
+            const uint8_t *q = smem + stage * CF::STAGE_BYTES + CF::A_BYTES + off +
+                               kk * 32 * CF::B_ROW_BYTES;
+            const half4_t lo = lds_read_tr16(q);
+            const half4_t hi = lds_read_tr16(q + 4 * CF::B_ROW_BYTES);
+            bf[buf][j] = half8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
     };
     auto none = [](int) {};
 
     int32_t slot = blockIdx.x;
     if (slot >= p.tiles) return;
-    Tile cur = make_tile<CF>(p, slot, w.row_pitch);
+    Tile cur = make_tile<CF, SPLIT>(p, slot, w.row_pitch);
     // Prefill: slices 0 .. S-2 into stages 0 .. S-2; stage S-1 is refilled
     // while slice 0 is computed.  Issued even when K has fewer slices (those
     // move no data), so every wait below counts the same instructions.
@@ -658,6 +780,11 @@ void gemm_f16_nt_kernel(Params p)
 
     while (true) {
         const int KT = (cur.klen + CF::BK - 1) / CF::BK;   // slices of this unit
+        if constexpr (FAST_DMA && CF::BL == 1) {
+#pragma unroll
+            for (int i = 0; i < CF::B_NB; ++i)
+                dvoffb[i] = dma_lane_offset_kn<CF>(i, w.wave, w.lane, cur.n0, p.N);
+        }
         typename CF::Acc acc[CF::FM][CF::FN];
         zero_acc<CF>(acc);
         if constexpr (CF::MI == 16) {
@@ -707,7 +834,17 @@ void gemm_f16_nt_kernel(Params p)
                 // early part of slice kt + 2, into stage rd, which the barrier
                 // of this slice's last step has just freed
                 auto dma_early = [&](int d) {
-                    if constexpr (FAST)
+                    if constexpr (FAST && CF::BL == 1) {
+                        if (d < CF::A_LOADS)
+                            dma_full<CF>(cur, dvoff[d], static_cast<uint32_t>(kt + 2) * (CF::BK * 2),
+                                         rd, d, lds0, w.wave);
+                        else
+                            dma_full<CF>(cur, dvoffb[(d - CF::A_LOADS) % CF::B_NB],
+                                         (static_cast<uint32_t>(kt + 2) * CF::BK +
+                                          static_cast<uint32_t>((d - CF::A_LOADS) / CF::B_NB) *
+                                              CF::B_NB * CF::B_RB) * ldb,
+                                         rd, d, lds0, w.wave);
+                    } else if constexpr (FAST)
                         dma_full<CF>(cur, dvoff[d < CF::A_LOADS ? d : d - CF::A_LOADS],
                                      static_cast<uint32_t>(kt + 2) * (CF::BK * 2), rd, d, lds0,
                                      w.wave);
@@ -775,12 +912,12 @@ void gemm_f16_nt_kernel(Params p)
         const int32_t next = slot + p.grid;
         Tile nxt;
         if (next < p.tiles) {
-            nxt = make_tile<CF>(p, next, w.row_pitch);
+            nxt = make_tile<CF, SPLIT>(p, next, w.row_pitch);
 #pragma unroll
             for (int s = 0; s < S - 1; ++s)
                 dma_slice<CF>(p, nxt, s, s, lds0, w.wave, w.lane, w.row_pitch);
         }
-        if (p.splits > 1) {
+        if constexpr (SPLIT) {
             store_tile_f32<CF>(p, cur, acc, w.wave_m, w.wave_n, w.lane);
         } else if constexpr (CF::STAGED_OK) {
             if (p.staged)
@@ -962,28 +1099,39 @@ void gemm_f16_nt_any_kernel(Params p)
 // ---------------------------------------------------------------------------
 struct KernelEntry {
     const void *fn;
+    const void *fn_split;   // the instance for K split into ranges (NT configurations)
     int32_t block_m, block_n, block_k, waves, stages, lds_bytes, threads;
     int32_t default_swizzle;
     float rel_rate;   // relative MFMA rate per tile area, for the plan cost model
     int32_t staged_ok;
     int32_t general;  // the general kernel: any K, A and B at any 2-byte alignment
     int32_t per_cu;   // workgroups resident per CU (the persistent grid's multiple of the CUs)
+    int32_t layout;   // B in memory: 0 [N, K] (gemm_f16_nt), 1 [K, N] (gemm_f16_nn)
 };
 
 template <class CF>
-constexpr KernelEntry entry(int swizzle, float rate)
+const void *split_instance()
 {
-    return KernelEntry{reinterpret_cast<const void *>(&gemm_f16_nt_kernel<CF>),
-                       CF::BM, CF::BN, CF::BK, CF::WAVES, CF::STAGES, CF::LDS_BYTES, CF::THREADS,
-                       swizzle, rate, CF::STAGED_OK ? 1 : 0, 0, 1};
+    if constexpr (CF::BL == 0)
+        return reinterpret_cast<const void *>(&gemm_f16_nt_kernel<CF, true>);
+    else
+        return nullptr;
 }
 
 template <class CF>
-constexpr KernelEntry entry_general(int swizzle)
+KernelEntry entry(int swizzle, float rate)
 {
-    return KernelEntry{reinterpret_cast<const void *>(&gemm_f16_nt_any_kernel<CF>),
+    return KernelEntry{reinterpret_cast<const void *>(&gemm_f16_nt_kernel<CF, false>),
+                       split_instance<CF>(), CF::BM, CF::BN, CF::BK, CF::WAVES, CF::STAGES, CF::LDS_BYTES, CF::THREADS,
+                       swizzle, rate, CF::STAGED_OK ? 1 : 0, 0, 1, CF::BL};
+}
+
+template <class CF>
+KernelEntry entry_general(int swizzle)
+{
+    return KernelEntry{reinterpret_cast<const void *>(&gemm_f16_nt_any_kernel<CF>), nullptr,
                        CF::BM, CF::BN, CF::BK, CF::WAVES, CF::STAGES, CF::LDS_BYTES, CF::THREADS,
-                       swizzle, 0.0f, 0, 1, 3};
+                       swizzle, 0.0f, 0, 1, 3, 0};
 }
 
 static const KernelEntry kKernels[] = {
@@ -1020,7 +1168,14 @@ static const KernelEntry kKernels[] = {
     // 23: 4 waves of 32x32, five stages of K 128: more tiles for a small M
     // whose 64x128 tiles would leave CUs idle (M <= 256, N of a few thousand)
     entry<Cfg<64, 64, 128, 2, 2, 5>>(8, 0.62f),
-    // 24: the general kernel, 4 waves of 64x64, two register-staged buffers of
+    // 24-28: B stored [K, N] (gemm_f16_nn), the scheme of 11 with transposing
+    // fragment reads of B
+    entry<Cfg<256, 256, 64, 2, 2, 2, 16, 0, 16, 0, 1>>(8, 1.06f),   // 24: as 11, A single-buffered
+    entry<Cfg<192, 256, 64, 2, 2, 2, 16, 0, 14, 1, 1>>(8, 0.97f),   // 25: as 18
+    entry<Cfg<256, 128, 64, 2, 2, 2, 16, 0, 12, 1, 1>>(8, 0.85f),   // 26: as 19
+    entry<Cfg<128, 128, 64, 2, 2, 2, 16, 0, 8, 1, 1>>(8, 0.75f),    // 27: as 20
+    entry<Cfg<64, 128, 64, 2, 2, 2, 16, 0, 6, 1, 1>>(8, 0.62f),     // 28: 4 waves of 32x64
+    // 29: the general kernel, 4 waves of 64x64, two register-staged buffers of
     // K 32; planned only when the direct-to-LDS path cannot run
     entry_general<Cfg<128, 128, 32, 2, 2, 2>>(8),
 };
@@ -1082,6 +1237,7 @@ static void fill_info(int id, gemm_f16_nt_plan_t *out)
     out->swizzle = e.default_swizzle;
     out->lds_bytes = e.lds_bytes;
     out->xcds = DEFAULT_XCDS;
+    out->b_layout = e.layout;
 }
 
 // Epilogue policy: stage C through LDS whenever the configuration has room
@@ -1106,13 +1262,13 @@ static void make_plan(int id, int64_t M, int64_t N, int32_t num_cus, int32_t swi
 // Cost model: rounds of the persistent grid times the time one tile takes,
 // which scales with its area over the configuration's relative MFMA rate.
 // Entries with rel_rate 0 are compiled for sweeps but never planned.
-static int choose_config(int64_t M, int64_t N, int32_t num_cus)
+static int choose_config(int64_t M, int64_t N, int32_t num_cus, int32_t layout = 0)
 {
     int best = -1;
     double best_cost = 0.0;
     for (int id = 0; id < kNumKernels; ++id) {
         const KernelEntry &e = kKernels[id];
-        if (e.rel_rate <= 0.0f) continue;
+        if (e.rel_rate <= 0.0f || e.layout != layout) continue;
         const int64_t tiles = cdiv(M, e.block_m) * cdiv(N, e.block_n);
         const int64_t rounds = cdiv(tiles, num_cus > 0 ? num_cus : 1);
         const double cost = static_cast<double>(rounds) * e.block_m * e.block_n / e.rel_rate;
@@ -1202,7 +1358,9 @@ static void choose_split(int64_t M, int64_t N, int64_t K, int32_t cus, int32_t c
     int best_id = -1;
     int64_t best_eff = 1;
     for (int id = 0; id < kNumKernels; ++id) {
-        if (config_id >= 0 ? id != config_id : kKernels[id].rel_rate <= 0.0f) continue;
+        if (config_id >= 0 ? id != config_id
+                           : (kKernels[id].rel_rate <= 0.0f || kKernels[id].layout != 0))
+            continue;
         const int32_t s_lo = splits > 0 ? splits : 1;
         const int32_t s_hi = splits > 0 ? splits : kMaxSplits;
         for (int32_t sp = s_lo; sp <= s_hi; ++sp) {
@@ -1247,7 +1405,9 @@ static int launch(const gemm_f16_nt_plan_t &plan, int64_t M, int64_t N, int64_t 
     void *args[] = {&p};
     // the launch's own status only: the thread's sticky error state (which may
     // hold an unrelated earlier error) is neither read nor cleared
-    const hipError_t err = hipLaunchKernel(e.fn, dim3(plan.grid), dim3(e.threads), args, 0, stream);
+    const void *fn = splits > 1 ? e.fn_split : e.fn;
+    if (!fn) return GEMM_F16_UNSUPPORTED;
+    const hipError_t err = hipLaunchKernel(fn, dim3(plan.grid), dim3(e.threads), args, 0, stream);
     return err == hipSuccess ? GEMM_F16_OK : GEMM_F16_LAUNCH_FAILED;
 }
 
@@ -1257,7 +1417,8 @@ static int run(int64_t M, int64_t N, int64_t K, const void *A, const void *B, vo
 {
     const int v = validate(M, N, K, A, B, C);
     if (v != GEMM_F16_OK) return v;
-    if (config_id >= kNumKernels) return GEMM_F16_INVALID_ARG;
+    if (config_id >= kNumKernels || (config_id >= 0 && kKernels[config_id].layout != 0))
+        return GEMM_F16_INVALID_ARG;
     if (M == 0 || N == 0) return GEMM_F16_OK;
     const bool general = needs_general(K, A, B, K > 0);
     if (general && config_id >= 0 && !kKernels[config_id].general) return GEMM_F16_UNSUPPORTED;
@@ -1277,13 +1438,52 @@ static int run(int64_t M, int64_t N, int64_t K, const void *A, const void *B, vo
     return launch(plan, M, N, K, A, B, C, stream);
 }
 
+// C = A B with B stored [K, N] (N contiguous): only the direct-to-LDS
+// kernels of layout 1 take it.  Their preconditions: A's rows as for the
+// direct-to-LDS NT path (K a multiple of 8, at most 2^21, A 16-byte aligned),
+// B's rows 16-byte aligned (N a multiple of 8, B 16-byte aligned), and B's
+// byte offsets within 2^31 (K N 2 < 2^31).
+static bool nn_supported(int64_t N, int64_t K, const void *A, const void *B, bool check_pointers)
+{
+    if (K % 8 != 0 || K > MAX_K || N % 8 != 0 || K * N * 2 > INT32_MAX) return false;
+    if (!check_pointers) return true;
+    return reinterpret_cast<uintptr_t>(A) % 16 == 0 && reinterpret_cast<uintptr_t>(B) % 16 == 0;
+}
+
+static int run_nn(int64_t M, int64_t N, int64_t K, const void *A, const void *B, void *C,
+                  hipStream_t stream, int32_t config_id, int32_t swizzle, int32_t grid,
+                  int32_t epilogue)
+{
+    const int v = validate(M, N, K, A, B, C);   // B holds K N elements either way
+    if (v != GEMM_F16_OK) return v;
+    if (config_id >= kNumKernels || (config_id >= 0 && kKernels[config_id].layout != 1))
+        return GEMM_F16_INVALID_ARG;
+    if (M == 0 || N == 0) return GEMM_F16_OK;
+    if (K == 0) return run(M, N, 0, A, B, C, stream, -1, 0, 0, -1);   // the empty sum, B unread
+    if (!nn_supported(N, K, A, B, true)) return GEMM_F16_UNSUPPORTED;
+    int32_t cus = 0;
+    const int s = current_cus(&cus);
+    if (s != GEMM_F16_OK) return s;
+    const int id = config_id >= 0 ? config_id : choose_config(M, N, cus, 1);
+    gemm_f16_nt_plan_t plan;
+    make_plan(id, M, N, cus, swizzle, grid, &plan);
+    if (epilogue < 0) {
+        plan.epilogue = choose_epilogue(id);
+    } else {
+        if (epilogue > 1 || (epilogue == 1 && !kKernels[id].staged_ok)) return GEMM_F16_UNSUPPORTED;
+        plan.epilogue = epilogue;
+    }
+    return launch(plan, M, N, K, A, B, C, stream);
+}
+
 static int run_splitk(int64_t M, int64_t N, int64_t K, const void *A, const void *B, void *C,
                       int32_t splits, void *workspace, int64_t workspace_bytes,
                       hipStream_t stream, int32_t config_id)
 {
     const int v = validate(M, N, K, A, B, C);
     if (v != GEMM_F16_OK) return v;
-    if (config_id >= kNumKernels || splits > kMaxSplits || workspace_bytes < 0)
+    if (config_id >= kNumKernels || (config_id >= 0 && kKernels[config_id].layout != 0) ||
+        splits > kMaxSplits || workspace_bytes < 0)
         return GEMM_F16_INVALID_ARG;
     if (M == 0 || N == 0) return GEMM_F16_OK;
     // arguments only the general kernel takes, and K = 0: no split
@@ -1419,6 +1619,33 @@ extern "C" int gemm_f16_nt_splitk_with_config(int64_t M, int64_t N, int64_t K, c
 {
     return run_splitk(M, N, K, A, B, C, splits, workspace, workspace_bytes, stream,
                       config_id < 0 ? -1 : config_id);
+}
+
+extern "C" int gemm_f16_nn(int64_t M, int64_t N, int64_t K, const void *A, const void *B,
+                           void *C, hipStream_t stream)
+{
+    return run_nn(M, N, K, A, B, C, stream, -1, 0, 0, -1);
+}
+
+extern "C" int gemm_f16_nn_with_config(int64_t M, int64_t N, int64_t K, const void *A,
+                                       const void *B, void *C, hipStream_t stream,
+                                       int32_t config_id, int32_t swizzle, int32_t grid,
+                                       int32_t epilogue)
+{
+    return run_nn(M, N, K, A, B, C, stream, config_id < 0 ? -1 : config_id, swizzle, grid,
+                  epilogue);
+}
+
+extern "C" int gemm_f16_nn_plan(int64_t M, int64_t N, int64_t K, int32_t num_cus,
+                                gemm_f16_nt_plan_t *plan)
+{
+    if (!plan || M < 0 || N < 0 || K < 0 || num_cus <= 0) return GEMM_F16_INVALID_ARG;
+    if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX || cdiv(M, 64) * cdiv(N, 64) > INT32_MAX)
+        return GEMM_F16_UNSUPPORTED;
+    if (K == 0) return gemm_f16_nt_plan(M, N, K, num_cus, plan);
+    if (!nn_supported(N, K, nullptr, nullptr, false)) return GEMM_F16_UNSUPPORTED;
+    make_plan(choose_config(M, N, num_cus, 1), M, N, num_cus, 0, 0, plan);
+    return GEMM_F16_OK;
 }
 
 extern "C" int gemm_f16_nt_num_configs(void) { return kNumKernels; }

@@ -278,3 +278,42 @@ def test_splitk_host_checks_before_any_device_access(g):
     assert lib.gemm_f16_nt_splitk(64, 64, 64, A0, B0, C0, 65, 0, 0, None) == 1
     assert lib.gemm_f16_nt_splitk(64, 64, 64, A0, B0, C0, 4, 0, -1, None) == 1
     assert lib.gemm_f16_nt_splitk(64, 64, 64, A0, B0, A0, 4, 0, 0, None) == 1   # C overlaps A
+
+
+# ---------------------------------------------------------------------------
+# B stored [K, N] (gemm_f16_nn): planner and host checks
+# ---------------------------------------------------------------------------
+def test_nn_configs_are_their_own(g):
+    nn = [c for c in range(g.gemm_f16_nt_num_configs()) if g.gemm_f16_nt_config_info(c).b_layout == 1]
+    assert nn, "no [K, N] configurations compiled"
+    for c in nn:
+        info = g.gemm_f16_nt_config_info(c)
+        assert info.block_n in (128, 256) and info.block_k == 64
+    # the NT planner never picks one, the NN planner always does
+    for shape in [(8192, 8192, 8192), (128, 16384, 16384), (4999, 7000, 4160), (300, 264, 200)]:
+        assert g.gemm_f16_nt_plan(*shape, 256).b_layout == 0
+        p = g.gemm_f16_nn_plan(*shape, 256)
+        assert p.b_layout == 1 and p.config_id in nn
+        assert p.tiles == p.tiles_m * p.tiles_n and 1 <= p.grid <= min(256, p.tiles)
+
+
+@pytest.mark.parametrize("shape", [(64, 60, 64), (64, 64, 60), (64, 64, (1 << 21) + 8),
+                                   (8, 65536, 65536)])
+def test_nn_plan_unsupported(g, shape):
+    # N or K not a multiple of 8, K above 2^21, K N 2 >= 2^31
+    with pytest.raises(g.GemmError) as e:
+        g.gemm_f16_nn_plan(*shape, 256)
+    assert e.value.status == 2
+
+
+def test_nn_host_checks_before_any_device_access(g):
+    lib = g.load()
+    nt_cfg = g.gemm_f16_nt_plan(64, 64, 64, 256).config_id
+    assert lib.gemm_f16_nn(0, 64, 64, A0, B0, C0, None) == 0
+    assert lib.gemm_f16_nn(-1, 64, 64, A0, B0, C0, None) == 1
+    assert lib.gemm_f16_nn(64, 60, 64, A0, B0, C0, None) == 2            # N % 8
+    assert lib.gemm_f16_nn(64, 64, 60, A0, B0, C0, None) == 2            # K % 8
+    assert lib.gemm_f16_nn(64, 64, 64, A0, B0 + 8, C0, None) == 2        # B 8-byte aligned
+    assert lib.gemm_f16_nn_with_config(64, 64, 64, A0, B0, C0, None, nt_cfg, 0, 0, -1) == 1
+    nn_cfg = g.gemm_f16_nn_plan(64, 64, 64, 256).config_id
+    assert lib.gemm_f16_nt_with_config(64, 64, 64, A0, B0, C0, None, nn_cfg, 0, 0, -1) == 1
