@@ -118,6 +118,9 @@ def main() -> int:
     ap.add_argument("--splitk", type=int, default=None,
                     help="time gemm_f16_nt_splitk with this many K splits (0: the library's "
                          "choice); a step is then the split GEMM and its reduction")
+    ap.add_argument("--nn", action="store_true",
+                    help="time gemm_f16_nn: B is handed over transposed, [K, N] row-major "
+                         "(transposed before anything is timed; same result bits as NT)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -164,7 +167,21 @@ def main() -> int:
 
     stream = torch.cuda.current_stream(dev)
 
-    if args.splitk is not None:
+    if args.nn and args.splitk is not None:
+        print("bench.py: --nn and --splitk do not combine", file=sys.stderr)
+        return 2
+    if args.nn:
+        b_kn = b.t().contiguous()
+        plan = g.gemm_f16_nn_plan(w.M, w.N, w.K, cus).as_dict()
+        if args.config is not None:
+            info = g.gemm_f16_nt_config_info(args.config).as_dict()
+            plan.update({k: info[k] for k in ("config_id", "block_m", "block_n", "block_k",
+                                              "waves", "stages", "lds_bytes", "b_layout")})
+
+        def launch():
+            g.gemm_nn(a, b_kn, out=c, config=args.config, swizzle=args.swizzle, grid=args.grid,
+                      stream=stream, epilogue=args.epilogue)
+    elif args.splitk is not None:
         # the workspace is allocated once, before anything is timed
         sk_plan, splits, ws_bytes = g.gemm_f16_nt_splitk_plan(w.M, w.N, w.K, cus, args.splitk)
         plan = sk_plan.as_dict()
@@ -210,7 +227,8 @@ def main() -> int:
 
     tflops = w.flops / (ms_per_step * 1e-3) / 1e12
     compute_bound = w.flops / w.algorithmic_bytes > (PEAK_FP16_TFLOPS * 1e12) / (PEAK_HBM_GBS * 1e9)
-    traffic = measured_traffic(name if args.splitk is None else f"{name}_splitk")
+    traffic = measured_traffic(name + ("_splitk" if args.splitk is not None else
+                                       "_nn" if args.nn else ""))
     if compute_bound:
         achieved = w.flops / (kernel_avg_ms * 1e-3) / 1e12
         roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP16_TFLOPS,
@@ -232,7 +250,10 @@ def main() -> int:
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
-        "vs_baseline": round(tflops / PAGES_H100_TFLOPS, 3) if name == workloads.HEADLINE else None,
+        # the pages' figure is for the NT form of the headline shape only
+        "vs_baseline": (round(tflops / PAGES_H100_TFLOPS, 3)
+                        if name == workloads.HEADLINE and not args.nn and args.splitk is None
+                        else None),
         "dtype": "f16",
         "data": "synthetic",
         "config": {"workload": name, "M": w.M, "N": w.N, "K": w.K, "inputs": w.note,

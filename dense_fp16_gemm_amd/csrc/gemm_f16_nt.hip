@@ -1168,14 +1168,17 @@ static const KernelEntry kKernels[] = {
     // 23: 4 waves of 32x32, five stages of K 128: more tiles for a small M
     // whose 64x128 tiles would leave CUs idle (M <= 256, N of a few thousand)
     entry<Cfg<64, 64, 128, 2, 2, 5>>(8, 0.62f),
-    // 24-28: B stored [K, N] (gemm_f16_nn), the scheme of 11 with transposing
-    // fragment reads of B
+    // 24-29: B stored [K, N] (gemm_f16_nn), the schemes of 11 and 18-21 with
+    // transposing fragment reads of B
     entry<Cfg<256, 256, 64, 2, 2, 2, 16, 0, 16, 0, 1>>(8, 1.06f),   // 24: as 11, A single-buffered
     entry<Cfg<192, 256, 64, 2, 2, 2, 16, 0, 14, 1, 1>>(8, 0.97f),   // 25: as 18
     entry<Cfg<256, 128, 64, 2, 2, 2, 16, 0, 12, 1, 1>>(8, 0.85f),   // 26: as 19
     entry<Cfg<128, 128, 64, 2, 2, 2, 16, 0, 8, 1, 1>>(8, 0.75f),    // 27: as 20
     entry<Cfg<64, 128, 64, 2, 2, 2, 16, 0, 6, 1, 1>>(8, 0.62f),     // 28: 4 waves of 32x64
-    // 29: the general kernel, 4 waves of 64x64, two register-staged buffers of
+    // 29: 28 with 6 stages, the refill spread over each slice: more of B in
+    // flight for a small M (the streamed operand)
+    entry<Cfg<64, 128, 64, 2, 2, 6, 16, 0, 0, 0, 1>>(8, 0.66f),
+    // 30: the general kernel, 4 waves of 64x64, two register-staged buffers of
     // K 32; planned only when the direct-to-LDS path cannot run
     entry_general<Cfg<128, 128, 32, 2, 2, 2>>(8),
 };
