@@ -34,7 +34,12 @@ class Plan(ctypes.Structure):
                  "swizzle", "tiles_m", "tiles_n", "grid")] + \
                [("tiles", ctypes.c_int64), ("lds_bytes", ctypes.c_int32),
                 ("xcds", ctypes.c_int32), ("epilogue", ctypes.c_int32),
-                ("b_layout", ctypes.c_int32)]
+                ("b_layout", ctypes.c_int32), ("a_layout", ctypes.c_int32)]
+
+    @property
+    def layout(self) -> str:
+        """'nt', 'nn', 'tn' or 'tt': how A and B are stored."""
+        return ("t" if self.a_layout else "n") + ("n" if self.b_layout else "t")
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -73,12 +78,16 @@ def load():
         lib.gemm_f16_nt_splitk.restype = ctypes.c_int
         lib.gemm_f16_nt_splitk_with_config.argtypes = [i64, i64, i64, p, p, p, i32, p, i64, p, i32]
         lib.gemm_f16_nt_splitk_with_config.restype = ctypes.c_int
-        lib.gemm_f16_nn.argtypes = [i64, i64, i64, p, p, p, p]
-        lib.gemm_f16_nn.restype = ctypes.c_int
-        lib.gemm_f16_nn_with_config.argtypes = [i64, i64, i64, p, p, p, p, i32, i32, i32, i32]
-        lib.gemm_f16_nn_with_config.restype = ctypes.c_int
-        lib.gemm_f16_nn_plan.argtypes = [i64, i64, i64, i32, ctypes.POINTER(Plan)]
-        lib.gemm_f16_nn_plan.restype = ctypes.c_int
+        for lay in ("nn", "tn", "tt"):
+            f = getattr(lib, f"gemm_f16_{lay}")
+            f.argtypes = [i64, i64, i64, p, p, p, p]
+            f.restype = ctypes.c_int
+            f = getattr(lib, f"gemm_f16_{lay}_with_config")
+            f.argtypes = [i64, i64, i64, p, p, p, p, i32, i32, i32, i32]
+            f.restype = ctypes.c_int
+            f = getattr(lib, f"gemm_f16_{lay}_plan")
+            f.argtypes = [i64, i64, i64, i32, ctypes.POINTER(Plan)]
+            f.restype = ctypes.c_int
         lib.gemm_f16_nt_num_configs.argtypes = []
         lib.gemm_f16_nt_num_configs.restype = ctypes.c_int
         lib.gemm_f16_nt_config_info.argtypes = [i32, ctypes.POINTER(Plan)]
@@ -123,23 +132,30 @@ def gemm_f16_nt_plan(M: int, N: int, K: int, num_cus: int) -> Plan:
     return plan
 
 
-def gemm_f16_nn(M: int, N: int, K: int, A: int, B: int, C: int, stream: int = 0) -> None:
-    """C = A * B for device pointers A [M,K], B [K,N], C [M,N] (fp16)."""
-    _check(load().gemm_f16_nn(M, N, K, A, B, C, stream), "gemm_f16_nn")
+def _layout_fns(lay: str):
+    def call(M: int, N: int, K: int, A: int, B: int, C: int, stream: int = 0) -> None:
+        _check(getattr(load(), f"gemm_f16_{lay}")(M, N, K, A, B, C, stream), f"gemm_f16_{lay}")
+
+    def with_config(M: int, N: int, K: int, A: int, B: int, C: int, stream: int,
+                    config_id: int, swizzle: int = 0, grid: int = 0, epilogue: int = -1) -> None:
+        _check(getattr(load(), f"gemm_f16_{lay}_with_config")(M, N, K, A, B, C, stream, config_id,
+                                                              swizzle, grid, epilogue),
+               f"gemm_f16_{lay}_with_config")
+
+    def plan(M: int, N: int, K: int, num_cus: int) -> Plan:
+        out = Plan()
+        _check(getattr(load(), f"gemm_f16_{lay}_plan")(M, N, K, num_cus, ctypes.byref(out)),
+               f"gemm_f16_{lay}_plan")
+        return out
+
+    return call, with_config, plan
 
 
-def gemm_f16_nn_with_config(M: int, N: int, K: int, A: int, B: int, C: int, stream: int,
-                            config_id: int, swizzle: int = 0, grid: int = 0,
-                            epilogue: int = -1) -> None:
-    _check(load().gemm_f16_nn_with_config(M, N, K, A, B, C, stream, config_id, swizzle, grid,
-                                          epilogue),
-           "gemm_f16_nn_with_config")
-
-
-def gemm_f16_nn_plan(M: int, N: int, K: int, num_cus: int) -> Plan:
-    plan = Plan()
-    _check(load().gemm_f16_nn_plan(M, N, K, num_cus, ctypes.byref(plan)), "gemm_f16_nn_plan")
-    return plan
+# C = op(A) op(B) for the other layouts: nn (A [M,K], B [K,N]), tn (A [K,M],
+# B [K,N]), tt (A [K,M], B [N,K]); device pointers, fp16
+gemm_f16_nn, gemm_f16_nn_with_config, gemm_f16_nn_plan = _layout_fns("nn")
+gemm_f16_tn, gemm_f16_tn_with_config, gemm_f16_tn_plan = _layout_fns("tn")
+gemm_f16_tt, gemm_f16_tt_with_config, gemm_f16_tt_plan = _layout_fns("tt")
 
 
 def gemm_f16_nt_splitk_plan(M: int, N: int, K: int, num_cus: int,
@@ -260,30 +276,44 @@ def gemm_nt_splitk(a, b, splits: int = 0, out=None, workspace=None, config: int 
     return out
 
 
-def gemm_nn(a, b, out=None, config: int | None = None, swizzle: int = 0, grid: int = 0,
-            stream=None, epilogue: int = -1):
-    """C = a @ b for fp16 tensors a [M,K] and b [K,N] (gemm_f16_nn).  Same
-    checks as gemm_nt."""
+def gemm(a, b, layout: str = "nt", out=None, config: int | None = None, swizzle: int = 0,
+         grid: int = 0, stream=None, epilogue: int = -1):
+    """C = op(a) @ op(b) for fp16 tensors, by operand layout:
+    'nt': a [M,K], b [N,K] (C = a @ b.T);   'nn': a [M,K], b [K,N] (C = a @ b);
+    'tn': a [K,M], b [K,N] (C = a.T @ b);   'tt': a [K,M], b [N,K] (C = a.T @ b.T).
+    Same checks as gemm_nt."""
     import torch
 
+    if layout == "nt":
+        return gemm_nt(a, b, out=out, config=config, swizzle=swizzle, grid=grid, stream=stream,
+                       epilogue=epilogue)
+    if layout not in ("nn", "tn", "tt"):
+        raise ValueError(f"unknown layout {layout!r}")
     if a.dtype != torch.float16 or b.dtype != torch.float16:
         raise TypeError("a and b must be torch.float16")
-    if a.dim() != 2 or b.dim() != 2 or a.shape[1] != b.shape[0]:
-        raise ValueError(f"shape mismatch: a{tuple(a.shape)} b{tuple(b.shape)}")
+    if a.dim() != 2 or b.dim() != 2:
+        raise ValueError("a and b must be matrices")
+    m, k = (a.shape[1], a.shape[0]) if layout[0] == "t" else (a.shape[0], a.shape[1])
+    kb, n = (b.shape[0], b.shape[1]) if layout[1] == "n" else (b.shape[1], b.shape[0])
+    if k != kb:
+        raise ValueError(f"shape mismatch for {layout}: a{tuple(a.shape)} b{tuple(b.shape)}")
     if not (a.is_cuda and b.is_cuda) or a.device != b.device:
         raise ValueError("a and b must be on the same GPU")
     if not (a.is_contiguous() and b.is_contiguous()):
         raise ValueError("a and b must be contiguous (row-major)")
-    m, k = a.shape
-    n = b.shape[1]
     if out is None:
         out = torch.empty((m, n), dtype=torch.float16, device=a.device)
     elif (out.dtype != torch.float16 or tuple(out.shape) != (m, n) or not out.is_contiguous()
           or out.device != a.device):
         raise ValueError("out must be a contiguous float16 [M, N] tensor on a's device")
     s = stream if stream is not None else torch.cuda.current_stream(a.device)
+    fn = globals()[f"gemm_f16_{layout}_with_config"]
     with torch.cuda.device(a.device):
-        gemm_f16_nn_with_config(m, n, k, a.data_ptr(), b.data_ptr(), out.data_ptr(),
-                                s.cuda_stream, -1 if config is None else config, swizzle,
-                                grid, epilogue)
+        fn(m, n, k, a.data_ptr(), b.data_ptr(), out.data_ptr(), s.cuda_stream,
+           -1 if config is None else config, swizzle, grid, epilogue)
     return out
+
+
+def gemm_nn(a, b, **kw):
+    """C = a @ b for a [M,K], b [K,N] (gemm_f16_nn)."""
+    return gemm(a, b, "nn", **kw)

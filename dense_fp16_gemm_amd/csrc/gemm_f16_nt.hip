@@ -143,11 +143,13 @@ __host__ __device__ constexpr int kn_swizzle(int k)
 // ADB_: double-buffer the A fragments as well as the B fragments.
 // BL_: B's layout in memory: 0 = [N, K] (K contiguous, the pages' NT form),
 // 1 = [K, N] (N contiguous: C = A B with B row-major).
+// AL_: A's layout: 0 = [M, K] (K contiguous), 1 = [K, M] (M contiguous:
+// C = A^T B or A^T B^T with A row-major [K, M]).
 template <int BM_, int BN_, int BK_, int WM_, int WN_, int STAGES_, int MI_ = 32,
-          int DSTEPS_ = 0, int DX_ = 0, int ADB_ = 0, int BL_ = 0>
+          int DSTEPS_ = 0, int DX_ = 0, int ADB_ = 0, int BL_ = 0, int AL_ = 0>
 struct Cfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, STAGES = STAGES_;
-    static constexpr int BL = BL_;
+    static constexpr int BL = BL_, AL = AL_;
     static constexpr int MI = MI_;               // MFMA block edge (M and N)
     static constexpr int MK = 512 / MI;          // K per MFMA: 16 or 32
     static constexpr int ACC_N = MI * MI / 64;   // accumulators per lane per block
@@ -173,7 +175,15 @@ struct Cfg {
     static constexpr int B_BYTES = BN * ROW_BYTES;
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
     static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
-    static constexpr int A_LOADS = BM / DMA_ROWS / WAVES;    // DMA instructions per wave per stage
+    // the A tile in LDS: BM rows of BK halves (AL 0) or BK rows of BM halves
+    // (AL 1); DMA instructions per wave per stage
+    static constexpr int A_ROW_BYTES = AL ? BM * 2 : ROW_BYTES;
+    static constexpr int A_CHUNKS = A_ROW_BYTES / 16;
+    static constexpr int A_DMA_ROWS = DMA_BYTES / A_ROW_BYTES;
+    static constexpr int A_LOADS = (AL ? BK : BM) / A_DMA_ROWS / WAVES;
+    static constexpr int A_RB = WAVES * A_DMA_ROWS;
+    static constexpr int A_NB = (16 / (A_RB < 16 ? A_RB : 16)) < A_LOADS
+                                    ? (16 / (A_RB < 16 ? A_RB : 16)) : A_LOADS;
     // the B tile in LDS: BN rows of BK halves (BL 0, like A) or BK rows of
     // BN halves (BL 1)
     static constexpr int B_ROW_BYTES = BL ? BN * 2 : ROW_BYTES;
@@ -195,11 +205,13 @@ struct Cfg {
     static_assert(MI == 32 || MI == 16, "MFMA is 32x32x16 or 16x16x32");
     static_assert(MI == 32 || CHUNKS == 8, "16x16x32 fragments need 128-byte rows");
     static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be whole 32-row blocks");
-    static_assert(BM % (DMA_ROWS * WAVES) == 0 &&
+    static_assert((AL ? BK % (A_DMA_ROWS * WAVES) : BM % (DMA_ROWS * WAVES)) == 0 &&
                       (BL ? BK % (B_DMA_ROWS * WAVES) : BN % (DMA_ROWS * WAVES)) == 0,
                   "every wave issues the same number of DMA instructions");
     static_assert(BL == 0 || (MI == 16 && (BN == 128 || BN == 256) && BK % 32 == 0),
                   "[K, N] B: 16x16x32 fragments, 256- or 512-byte rows");
+    static_assert(AL == 0 || (MI == 16 && (BM == 128 || BM == 256) && BK % 32 == 0),
+                  "[K, M] A: 16x16x32 fragments, 256- or 512-byte rows");
     static_assert(STAGES >= 2, "need at least a double buffer");
     static_assert(LDS_BYTES <= LDS_LIMIT, "LDS ring exceeds 160 KB");
     static_assert((STAGES - 1) * LOADS <= 63, "vmcnt counts at most 63 loads");
@@ -298,8 +310,15 @@ __device__ __forceinline__ Tile make_tile(const Params &p, int32_t slot, uint32_
     // range are never addressed (they get an out-of-range offset)
     const int32_t rows_a = min(CF::BM, p.M - t.m0);
     const int32_t rows_b = min(CF::BN, p.N - t.n0);
-    t.rsrc_a = make_rsrc(p.A + static_cast<int64_t>(t.m0) * p.K + k0,
-                         static_cast<uint32_t>(rows_a) * row_pitch);
+    if constexpr (CF::AL == 0) {
+        t.rsrc_a = make_rsrc(p.A + static_cast<int64_t>(t.m0) * p.K + k0,
+                             static_cast<uint32_t>(rows_a) * row_pitch);
+    } else {
+        // [K, M]: rows are k, as for a [K, N] B (the host keeps K M 2 below 2^31)
+        t.rsrc_a = make_rsrc(p.A + static_cast<int64_t>(k0) * p.M + t.m0,
+                             static_cast<uint32_t>(t.klen) * static_cast<uint32_t>(p.M) * 2u -
+                                 static_cast<uint32_t>(t.m0) * 2u);
+    }
     if constexpr (CF::BL == 0) {
         t.rsrc_b = make_rsrc(p.B + static_cast<int64_t>(t.n0) * p.K + k0,
                              static_cast<uint32_t>(rows_b) * row_pitch);
@@ -327,18 +346,20 @@ __device__ __forceinline__ void dma_one(const Params &p, const Tile &t, int stag
     const uint32_t k0 = static_cast<uint32_t>(kt) * CF::BK;
     const bool is_a = i < CF::A_LOADS;
     const int rblk = (is_a ? i : i - CF::A_LOADS) * CF::WAVES + wave;
-    if constexpr (CF::BL == 1) {
-        if (!is_a) {
-            // row k0 + r of the [K, N] tile: lane l fetches logical chunk
-            // (l % B_CHUNKS) ^ kn_swizzle(r) of it (8 columns), zero past K or N
-            const int r = rblk * CF::B_DMA_ROWS + lane / CF::B_CHUNKS;
-            const int chunk = (lane % CF::B_CHUNKS) ^ kn_swizzle(r);
-            const uint32_t ldb = static_cast<uint32_t>(p.N) * 2u;
-            uint32_t v = (k0 + r) * ldb + chunk * 16;
-            if (k0 + r >= static_cast<uint32_t>(t.klen) || t.n0 + chunk * 8 >= p.N) v = OOB_OFFSET;
-            dma16(t.rsrc_b, v, lds0 + stage * CF::STAGE_BYTES + CF::A_BYTES + rblk * DMA_BYTES);
-            return;
-        }
+    if ((is_a && CF::AL == 1) || (!is_a && CF::BL == 1)) {
+        // row k0 + r of a [K, M] / [K, N] tile: lane l fetches logical chunk
+        // (l % chunks) ^ kn_swizzle(r) of it (8 columns), zero past K, M or N
+        const int dma_rows = is_a ? CF::A_DMA_ROWS : CF::B_DMA_ROWS;
+        const int chunks = is_a ? CF::A_CHUNKS : CF::B_CHUNKS;
+        const int32_t x0 = is_a ? t.m0 : t.n0, xn = is_a ? p.M : p.N;
+        const int r = rblk * dma_rows + lane / chunks;
+        const int chunk = (lane % chunks) ^ kn_swizzle(r);
+        const uint32_t ld = static_cast<uint32_t>(xn) * 2u;
+        uint32_t v = (k0 + r) * ld + chunk * 16;
+        if (k0 + r >= static_cast<uint32_t>(t.klen) || x0 + chunk * 8 >= xn) v = OOB_OFFSET;
+        dma16(is_a ? t.rsrc_a : t.rsrc_b, v,
+              lds0 + stage * CF::STAGE_BYTES + (is_a ? 0 : CF::A_BYTES) + rblk * DMA_BYTES);
+        return;
     }
     const int row = rblk * CF::DMA_ROWS + lane / CF::CHUNKS;
     const int chunk = (lane % CF::CHUNKS) ^ chunk_swizzle<CF::CHUNKS, CF::MI>(row);
@@ -368,14 +389,16 @@ __device__ __forceinline__ uint32_t dma_lane_offset(int ip, int wave, int lane, 
 // The same for the [K, N] B tile: fixed per tile (its columns past N get an
 // out-of-range offset), with the slice's row offset k0 N 2 in the scalar
 // offset.
-template <class CF>
-__device__ __forceinline__ uint32_t dma_lane_offset_kn(int ip, int wave, int lane, int32_t n0,
-                                                       int32_t N)
+template <class CF, bool IS_A>
+__device__ __forceinline__ uint32_t dma_lane_offset_kn(int ip, int wave, int lane, int32_t x0,
+                                                       int32_t xn)
 {
-    const int r = (ip * CF::WAVES + wave) * CF::B_DMA_ROWS + lane / CF::B_CHUNKS;
-    const int chunk = (lane % CF::B_CHUNKS) ^ kn_swizzle(r);
-    if (n0 + chunk * 8 >= N) return OOB_OFFSET;
-    return static_cast<uint32_t>(r) * static_cast<uint32_t>(N) * 2u + chunk * 16;
+    constexpr int DMA_ROWS_X = IS_A ? CF::A_DMA_ROWS : CF::B_DMA_ROWS;
+    constexpr int CHUNKS_X = IS_A ? CF::A_CHUNKS : CF::B_CHUNKS;
+    const int r = (ip * CF::WAVES + wave) * DMA_ROWS_X + lane / CHUNKS_X;
+    const int chunk = (lane % CHUNKS_X) ^ kn_swizzle(r);
+    if (x0 + chunk * 8 >= xn) return OOB_OFFSET;
+    return static_cast<uint32_t>(r) * static_cast<uint32_t>(xn) * 2u + chunk * 16;
 }
 
 template <class CF>
@@ -642,6 +665,8 @@ struct WaveCtx {
     // lane's own bits do not, so its offset is btr0 ^ 32 j.  Later steps and
     // the second read (4 rows on) keep the row's swizzle: constant offsets.
     uint32_t btr0;
+    // [K, M] A: the same, for block i of the wave's rows (atr0 ^ 32 i)
+    uint32_t atr0;
 
     __device__ __forceinline__ WaveCtx(const Params &p)
     {
@@ -664,11 +689,18 @@ struct WaveCtx {
         a_frag_base = wave_m * CF::TM * CF::ROW_BYTES;
         b_frag_base = CF::A_BYTES + wave_n * CF::TN * CF::ROW_BYTES;
         btr0 = 0;
+        atr0 = 0;
         if constexpr (CF::BL == 1) {
             static_assert(CF::TN % 128 == 0 || CF::TN == 64, "wave column offset clear of the XOR bits");
             const int r = 8 * (lane / 16) + (lane % 16) / 4;
             const int n = wave_n * CF::TN + 4 * (lane % 4);
             btr0 = r * CF::B_ROW_BYTES + (((n / 8) ^ kn_swizzle(r)) * 16) + (n % 8) * 2;
+        }
+        if constexpr (CF::AL == 1) {
+            static_assert(CF::TM % 128 == 0 || CF::TM == 64, "wave row offset clear of the XOR bits");
+            const int r = 8 * (lane / 16) + (lane % 16) / 4;
+            const int m = wave_m * CF::TM + 4 * (lane % 4);
+            atr0 = r * CF::A_ROW_BYTES + (((m / 8) ^ kn_swizzle(r)) * 16) + (m % 8) * 2;
         }
     }
 };
@@ -730,24 +762,35 @@ void gemm_f16_nt_kernel(Params p)
     // With two stages and the whole refill issued early, the refill of a
     // slice wholly inside K takes the fast form (dma_full).
     constexpr bool FAST_DMA = S == 2 && DX == L;
-    // fast-form lane offsets: shared by the A and B parts for [N, K] B; for
-    // [K, N] B the B part has its own, set per tile
-    constexpr int NVOFF = !FAST_DMA ? 1
-                          : CF::BL ? CF::A_LOADS
-                                   : (CF::A_LOADS > CF::B_LOADS ? CF::A_LOADS : CF::B_LOADS);
+    // fast-form lane offsets: one kernel-wide set for the K-contiguous
+    // operands (both parts use the same row pattern); an operand stored
+    // [K, M] / [K, N] has its own, set per tile
+    constexpr int NA_K = CF::AL ? 0 : CF::A_LOADS, NB_K = CF::BL ? 0 : CF::B_LOADS;
+    constexpr int NVOFF = !FAST_DMA ? 1 : (NA_K > NB_K ? NA_K : (NB_K > 0 ? NB_K : 1));
     uint32_t dvoff[NVOFF];
 #pragma unroll
     for (int i = 0; i < NVOFF; ++i) dvoff[i] = dma_lane_offset<CF>(i, w.wave, w.lane, w.row_pitch);
+    uint32_t dvoffa[FAST_DMA && CF::AL ? CF::A_NB : 1];
     uint32_t dvoffb[FAST_DMA && CF::BL ? CF::B_NB : 1];
+    const uint32_t lda = static_cast<uint32_t>(p.M) * 2u;   // [K, M] A row pitch
     const uint32_t ldb = static_cast<uint32_t>(p.N) * 2u;   // [K, N] B row pitch
     const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(smem));
 
     half8_t af[CF::ADB ? 2 : 1][CF::FM], bf[2][CF::FN];
     // A fragment i / B fragment j of step kk of `stage`, into buffer `buf`
     auto read_a = [&](int buf, int stage, int kk, int i) {
-        af[buf][i] = *reinterpret_cast<const half8_t *>(smem + stage * CF::STAGE_BYTES +
-                                                    w.frag_off[i & 1][kk] + w.a_frag_base +
-                                                    i * CF::MI * CF::ROW_BYTES);
+        if constexpr (CF::AL == 0) {
+            af[buf][i] = *reinterpret_cast<const half8_t *>(smem + stage * CF::STAGE_BYTES +
+                                                        w.frag_off[i & 1][kk] + w.a_frag_base +
+                                                        i * CF::MI * CF::ROW_BYTES);
+        } else {
+            uint32_t off;
+            asm volatile("v_xor_b32 %0, %2, %1" : "=v"(off) : "v"(w.atr0), "n"(32 * i));
+            const uint8_t *q = smem + stage * CF::STAGE_BYTES + off + kk * 32 * CF::A_ROW_BYTES;
+            const half4_t lo = lds_read_tr16(q);
+            const half4_t hi = lds_read_tr16(q + 4 * CF::A_ROW_BYTES);
+            af[buf][i] = half8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
     };
     auto read_b = [&](int buf, int stage, int kk, int j) {
         if constexpr (CF::BL == 0) {
@@ -780,10 +823,15 @@ void gemm_f16_nt_kernel(Params p)
 
     while (true) {
         const int KT = (cur.klen + CF::BK - 1) / CF::BK;   // slices of this unit
+        if constexpr (FAST_DMA && CF::AL == 1) {
+#pragma unroll
+            for (int i = 0; i < CF::A_NB; ++i)
+                dvoffa[i] = dma_lane_offset_kn<CF, true>(i, w.wave, w.lane, cur.m0, p.M);
+        }
         if constexpr (FAST_DMA && CF::BL == 1) {
 #pragma unroll
             for (int i = 0; i < CF::B_NB; ++i)
-                dvoffb[i] = dma_lane_offset_kn<CF>(i, w.wave, w.lane, cur.n0, p.N);
+                dvoffb[i] = dma_lane_offset_kn<CF, false>(i, w.wave, w.lane, cur.n0, p.N);
         }
         typename CF::Acc acc[CF::FM][CF::FN];
         zero_acc<CF>(acc);
@@ -834,21 +882,27 @@ void gemm_f16_nt_kernel(Params p)
                 // early part of slice kt + 2, into stage rd, which the barrier
                 // of this slice's last step has just freed
                 auto dma_early = [&](int d) {
-                    if constexpr (FAST && CF::BL == 1) {
-                        if (d < CF::A_LOADS)
-                            dma_full<CF>(cur, dvoff[d], static_cast<uint32_t>(kt + 2) * (CF::BK * 2),
-                                         rd, d, lds0, w.wave);
-                        else
-                            dma_full<CF>(cur, dvoffb[(d - CF::A_LOADS) % CF::B_NB],
-                                         (static_cast<uint32_t>(kt + 2) * CF::BK +
-                                          static_cast<uint32_t>((d - CF::A_LOADS) / CF::B_NB) *
-                                              CF::B_NB * CF::B_RB) * ldb,
-                                         rd, d, lds0, w.wave);
-                    } else if constexpr (FAST)
-                        dma_full<CF>(cur, dvoff[d < CF::A_LOADS ? d : d - CF::A_LOADS],
-                                     static_cast<uint32_t>(kt + 2) * (CF::BK * 2), rd, d, lds0,
-                                     w.wave);
-                    else
+                    if constexpr (FAST) {
+                        const uint32_t kslice = static_cast<uint32_t>(kt + 2) * CF::BK;
+                        if (d < CF::A_LOADS) {
+                            if constexpr (CF::AL == 1)
+                                dma_full<CF>(cur, dvoffa[d % CF::A_NB],
+                                             (kslice + static_cast<uint32_t>(d / CF::A_NB) *
+                                                           CF::A_NB * CF::A_RB) * lda,
+                                             rd, d, lds0, w.wave);
+                            else
+                                dma_full<CF>(cur, dvoff[d], kslice * 2, rd, d, lds0, w.wave);
+                        } else {
+                            const int db = d - CF::A_LOADS;
+                            if constexpr (CF::BL == 1)
+                                dma_full<CF>(cur, dvoffb[db % CF::B_NB],
+                                             (kslice + static_cast<uint32_t>(db / CF::B_NB) *
+                                                           CF::B_NB * CF::B_RB) * ldb,
+                                             rd, d, lds0, w.wave);
+                            else
+                                dma_full<CF>(cur, dvoff[db], kslice * 2, rd, d, lds0, w.wave);
+                        }
+                    } else
                         dma_one<CF>(p, cur, rd, kt + 2, d, lds0, w.wave, w.lane, w.row_pitch);
                 };
                 if (kk + 1 < KK) {
@@ -1106,13 +1160,13 @@ struct KernelEntry {
     int32_t staged_ok;
     int32_t general;  // the general kernel: any K, A and B at any 2-byte alignment
     int32_t per_cu;   // workgroups resident per CU (the persistent grid's multiple of the CUs)
-    int32_t layout;   // B in memory: 0 [N, K] (gemm_f16_nt), 1 [K, N] (gemm_f16_nn)
+    int32_t layout;   // operand layouts: 0 NT, 1 NN, 2 TT, 3 TN (2 * A's + B's, see Cfg)
 };
 
 template <class CF>
 const void *split_instance()
 {
-    if constexpr (CF::BL == 0)
+    if constexpr (CF::BL == 0 && CF::AL == 0)
         return reinterpret_cast<const void *>(&gemm_f16_nt_kernel<CF, true>);
     else
         return nullptr;
@@ -1123,7 +1177,7 @@ KernelEntry entry(int swizzle, float rate)
 {
     return KernelEntry{reinterpret_cast<const void *>(&gemm_f16_nt_kernel<CF, false>),
                        split_instance<CF>(), CF::BM, CF::BN, CF::BK, CF::WAVES, CF::STAGES, CF::LDS_BYTES, CF::THREADS,
-                       swizzle, rate, CF::STAGED_OK ? 1 : 0, 0, 1, CF::BL};
+                       swizzle, rate, CF::STAGED_OK ? 1 : 0, 0, 1, 2 * CF::AL + CF::BL};
 }
 
 template <class CF>
@@ -1178,7 +1232,15 @@ static const KernelEntry kKernels[] = {
     // 29: 28 with 6 stages, the refill spread over each slice: more of B in
     // flight for a small M (the streamed operand)
     entry<Cfg<64, 128, 64, 2, 2, 6, 16, 0, 0, 0, 1>>(8, 0.66f),
-    // 30: the general kernel, 4 waves of 64x64, two register-staged buffers of
+    // 30-32: A stored [K, M] and B [N, K] (gemm_f16_tt); 33-35: A [K, M] and
+    // B [K, N] (gemm_f16_tn): transposing fragment reads for A as well
+    entry<Cfg<256, 256, 64, 2, 2, 2, 16, 0, 16, 0, 0, 1>>(8, 1.06f),   // 30
+    entry<Cfg<256, 128, 64, 2, 2, 2, 16, 0, 12, 1, 0, 1>>(8, 0.85f),   // 31
+    entry<Cfg<128, 128, 64, 2, 2, 2, 16, 0, 8, 1, 0, 1>>(8, 0.75f),    // 32
+    entry<Cfg<256, 256, 64, 2, 2, 2, 16, 0, 16, 0, 1, 1>>(8, 1.06f),   // 33
+    entry<Cfg<256, 128, 64, 2, 2, 2, 16, 0, 12, 1, 1, 1>>(8, 0.85f),   // 34
+    entry<Cfg<128, 128, 64, 2, 2, 2, 16, 0, 8, 1, 1, 1>>(8, 0.75f),    // 35
+    // 36: the general kernel, 4 waves of 64x64, two register-staged buffers of
     // K 32; planned only when the direct-to-LDS path cannot run
     entry_general<Cfg<128, 128, 32, 2, 2, 2>>(8),
 };
@@ -1240,7 +1302,8 @@ static void fill_info(int id, gemm_f16_nt_plan_t *out)
     out->swizzle = e.default_swizzle;
     out->lds_bytes = e.lds_bytes;
     out->xcds = DEFAULT_XCDS;
-    out->b_layout = e.layout;
+    out->a_layout = e.layout >> 1;
+    out->b_layout = e.layout & 1;
 }
 
 // Epilogue policy: stage C through LDS whenever the configuration has room
@@ -1441,33 +1504,37 @@ static int run(int64_t M, int64_t N, int64_t K, const void *A, const void *B, vo
     return launch(plan, M, N, K, A, B, C, stream);
 }
 
-// C = A B with B stored [K, N] (N contiguous): only the direct-to-LDS
-// kernels of layout 1 take it.  Their preconditions: A's rows as for the
-// direct-to-LDS NT path (K a multiple of 8, at most 2^21, A 16-byte aligned),
-// B's rows 16-byte aligned (N a multiple of 8, B 16-byte aligned), and B's
-// byte offsets within 2^31 (K N 2 < 2^31).
-static bool nn_supported(int64_t N, int64_t K, const void *A, const void *B, bool check_pointers)
+// Layouts other than NT (layout = 2 * A's + B's: 1 NN, 2 TT, 3 TN): only the
+// direct-to-LDS kernels of that layout take them.  Each operand's rows must
+// be 16-byte aligned: a K-contiguous operand needs K a multiple of 8 and at
+// most 2^21 (as on the NT path), an M- or N-contiguous one M or N a multiple
+// of 8 and its K rows within 2^31 bytes of offsets; A and B 16-byte aligned.
+static bool layout_supported(int32_t layout, int64_t M, int64_t N, int64_t K, const void *A,
+                             const void *B, bool check_pointers)
 {
-    if (K % 8 != 0 || K > MAX_K || N % 8 != 0 || K * N * 2 > INT32_MAX) return false;
+    const bool a_kn = (layout >> 1) & 1, b_kn = layout & 1;
+    if (K > MAX_K) return false;
+    if (a_kn ? (M % 8 != 0 || K * M * 2 > INT32_MAX) : K % 8 != 0) return false;
+    if (b_kn ? (N % 8 != 0 || K * N * 2 > INT32_MAX) : K % 8 != 0) return false;
     if (!check_pointers) return true;
     return reinterpret_cast<uintptr_t>(A) % 16 == 0 && reinterpret_cast<uintptr_t>(B) % 16 == 0;
 }
 
-static int run_nn(int64_t M, int64_t N, int64_t K, const void *A, const void *B, void *C,
-                  hipStream_t stream, int32_t config_id, int32_t swizzle, int32_t grid,
-                  int32_t epilogue)
+static int run_layout(int32_t layout, int64_t M, int64_t N, int64_t K, const void *A,
+                      const void *B, void *C, hipStream_t stream, int32_t config_id,
+                      int32_t swizzle, int32_t grid, int32_t epilogue)
 {
-    const int v = validate(M, N, K, A, B, C);   // B holds K N elements either way
+    const int v = validate(M, N, K, A, B, C);   // A and B hold M K and K N elements either way
     if (v != GEMM_F16_OK) return v;
-    if (config_id >= kNumKernels || (config_id >= 0 && kKernels[config_id].layout != 1))
+    if (config_id >= kNumKernels || (config_id >= 0 && kKernels[config_id].layout != layout))
         return GEMM_F16_INVALID_ARG;
     if (M == 0 || N == 0) return GEMM_F16_OK;
-    if (K == 0) return run(M, N, 0, A, B, C, stream, -1, 0, 0, -1);   // the empty sum, B unread
-    if (!nn_supported(N, K, A, B, true)) return GEMM_F16_UNSUPPORTED;
+    if (K == 0) return run(M, N, 0, A, B, C, stream, -1, 0, 0, -1);   // the empty sum
+    if (!layout_supported(layout, M, N, K, A, B, true)) return GEMM_F16_UNSUPPORTED;
     int32_t cus = 0;
     const int s = current_cus(&cus);
     if (s != GEMM_F16_OK) return s;
-    const int id = config_id >= 0 ? config_id : choose_config(M, N, cus, 1);
+    const int id = config_id >= 0 ? config_id : choose_config(M, N, cus, layout);
     gemm_f16_nt_plan_t plan;
     make_plan(id, M, N, cus, swizzle, grid, &plan);
     if (epilogue < 0) {
@@ -1477,6 +1544,18 @@ static int run_nn(int64_t M, int64_t N, int64_t K, const void *A, const void *B,
         plan.epilogue = epilogue;
     }
     return launch(plan, M, N, K, A, B, C, stream);
+}
+
+static int plan_layout(int32_t layout, int64_t M, int64_t N, int64_t K, int32_t num_cus,
+                       gemm_f16_nt_plan_t *plan)
+{
+    if (!plan || M < 0 || N < 0 || K < 0 || num_cus <= 0) return GEMM_F16_INVALID_ARG;
+    if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX || cdiv(M, 64) * cdiv(N, 64) > INT32_MAX)
+        return GEMM_F16_UNSUPPORTED;
+    if (K == 0) return gemm_f16_nt_plan(M, N, K, num_cus, plan);
+    if (!layout_supported(layout, M, N, K, nullptr, nullptr, false)) return GEMM_F16_UNSUPPORTED;
+    make_plan(choose_config(M, N, num_cus, layout), M, N, num_cus, 0, 0, plan);
+    return GEMM_F16_OK;
 }
 
 static int run_splitk(int64_t M, int64_t N, int64_t K, const void *A, const void *B, void *C,
@@ -1627,7 +1706,7 @@ extern "C" int gemm_f16_nt_splitk_with_config(int64_t M, int64_t N, int64_t K, c
 extern "C" int gemm_f16_nn(int64_t M, int64_t N, int64_t K, const void *A, const void *B,
                            void *C, hipStream_t stream)
 {
-    return run_nn(M, N, K, A, B, C, stream, -1, 0, 0, -1);
+    return run_layout(1, M, N, K, A, B, C, stream, -1, 0, 0, -1);
 }
 
 extern "C" int gemm_f16_nn_with_config(int64_t M, int64_t N, int64_t K, const void *A,
@@ -1635,20 +1714,56 @@ extern "C" int gemm_f16_nn_with_config(int64_t M, int64_t N, int64_t K, const vo
                                        int32_t config_id, int32_t swizzle, int32_t grid,
                                        int32_t epilogue)
 {
-    return run_nn(M, N, K, A, B, C, stream, config_id < 0 ? -1 : config_id, swizzle, grid,
-                  epilogue);
+    return run_layout(1, M, N, K, A, B, C, stream, config_id < 0 ? -1 : config_id, swizzle,
+                      grid, epilogue);
 }
 
 extern "C" int gemm_f16_nn_plan(int64_t M, int64_t N, int64_t K, int32_t num_cus,
                                 gemm_f16_nt_plan_t *plan)
 {
-    if (!plan || M < 0 || N < 0 || K < 0 || num_cus <= 0) return GEMM_F16_INVALID_ARG;
-    if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX || cdiv(M, 64) * cdiv(N, 64) > INT32_MAX)
-        return GEMM_F16_UNSUPPORTED;
-    if (K == 0) return gemm_f16_nt_plan(M, N, K, num_cus, plan);
-    if (!nn_supported(N, K, nullptr, nullptr, false)) return GEMM_F16_UNSUPPORTED;
-    make_plan(choose_config(M, N, num_cus, 1), M, N, num_cus, 0, 0, plan);
-    return GEMM_F16_OK;
+    return plan_layout(1, M, N, K, num_cus, plan);
+}
+
+extern "C" int gemm_f16_tt(int64_t M, int64_t N, int64_t K, const void *A, const void *B,
+                           void *C, hipStream_t stream)
+{
+    return run_layout(2, M, N, K, A, B, C, stream, -1, 0, 0, -1);
+}
+
+extern "C" int gemm_f16_tt_with_config(int64_t M, int64_t N, int64_t K, const void *A,
+                                       const void *B, void *C, hipStream_t stream,
+                                       int32_t config_id, int32_t swizzle, int32_t grid,
+                                       int32_t epilogue)
+{
+    return run_layout(2, M, N, K, A, B, C, stream, config_id < 0 ? -1 : config_id, swizzle,
+                      grid, epilogue);
+}
+
+extern "C" int gemm_f16_tt_plan(int64_t M, int64_t N, int64_t K, int32_t num_cus,
+                                gemm_f16_nt_plan_t *plan)
+{
+    return plan_layout(2, M, N, K, num_cus, plan);
+}
+
+extern "C" int gemm_f16_tn(int64_t M, int64_t N, int64_t K, const void *A, const void *B,
+                           void *C, hipStream_t stream)
+{
+    return run_layout(3, M, N, K, A, B, C, stream, -1, 0, 0, -1);
+}
+
+extern "C" int gemm_f16_tn_with_config(int64_t M, int64_t N, int64_t K, const void *A,
+                                       const void *B, void *C, hipStream_t stream,
+                                       int32_t config_id, int32_t swizzle, int32_t grid,
+                                       int32_t epilogue)
+{
+    return run_layout(3, M, N, K, A, B, C, stream, config_id < 0 ? -1 : config_id, swizzle,
+                      grid, epilogue);
+}
+
+extern "C" int gemm_f16_tn_plan(int64_t M, int64_t N, int64_t K, int32_t num_cus,
+                                gemm_f16_nt_plan_t *plan)
+{
+    return plan_layout(3, M, N, K, num_cus, plan);
 }
 
 extern "C" int gemm_f16_nt_num_configs(void) { return kNumKernels; }

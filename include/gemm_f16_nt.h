@@ -104,8 +104,10 @@ typedef struct {
     int32_t xcds;        /* XCD count the tile order is arranged for       */
     int32_t epilogue;    /* 0: stores straight from the MFMA registers;
                             1: C staged through LDS for row-contiguous stores */
-    int32_t b_layout;    /* B in memory: 0 = [N, K] (gemm_f16_nt),
-                            1 = [K, N] (gemm_f16_nn) */
+    int32_t b_layout;    /* B in memory: 0 = [N, K] (gemm_f16_nt, gemm_f16_tt),
+                            1 = [K, N] (gemm_f16_nn, gemm_f16_tn) */
+    int32_t a_layout;    /* A in memory: 0 = [M, K] (gemm_f16_nt, gemm_f16_nn),
+                            1 = [K, M] (gemm_f16_tn, gemm_f16_tt) */
 } gemm_f16_nt_plan_t;
 
 int gemm_f16_nt_plan(int64_t M, int64_t N, int64_t K, int32_t num_cus,
@@ -138,23 +140,27 @@ int gemm_f16_nt_with_config(int64_t M, int64_t N, int64_t K,
                             int32_t swizzle, int32_t grid, int32_t epilogue);
 
 /*
- * C = A * B with B stored [K, N] row-major (N contiguous), the other operand
- * layout a GEMM library is asked for (the pages only build the NT form):
+ * The other operand layouts (the pages only build the NT form).  All four
+ * compute C[i][j] = fp16_rne( sum_k a(i, k) * b(k, j) ), accumulated in fp32,
+ * C fp16 [M, N] row-major, with
  *
- *     C[i][j] = fp16_rne( sum_k A[i][k] * B[k][j] )      (accumulated in fp32)
+ *   gemm_f16_nn:  a(i, k) = A[i][k], A [M, K];  b(k, j) = B[k][j], B [K, N]
+ *   gemm_f16_tn:  a(i, k) = A[k][i], A [K, M];  b(k, j) = B[k][j], B [K, N]
+ *   gemm_f16_tt:  a(i, k) = A[k][i], A [K, M];  b(k, j) = B[j][k], B [N, K]
  *
- *   A  fp16 [M, K] row-major, B fp16 [K, N] row-major, C fp16 [M, N] row-major.
- *
- * The same kernels as gemm_f16_nt with B's LDS tile kept in its [K, N] form
- * and the MFMA fragments read through gfx950's transposing LDS read; each
- * element's K order is the same as gemm_f16_nt's, so the result equals
- * gemm_f16_nt on the explicitly transposed B bit for bit.  Preconditions
- * (otherwise GEMM_F16_UNSUPPORTED): K a multiple of 8 and at most 2^21, N a
- * multiple of 8, A and B 16-byte aligned, K * N * 2 < 2^31.  K = 0 writes
- * +0 without reading B.  Ownership, asynchrony, threading and the other
- * status codes as for gemm_f16_nt; a configuration id of the other layout is
- * GEMM_F16_INVALID_ARG (each configuration's b_layout says which it is).
- * gemm_f16_nn_plan is the pure host planner (GEMM_F16_UNSUPPORTED where the
+ * (gemm_f16_nt: A [M, K], B [N, K]), every array row-major.  The same kernels
+ * as gemm_f16_nt, with a tile of an operand stored [K, M] or [K, N] kept in
+ * that form in LDS and its MFMA fragments read through gfx950's transposing
+ * LDS read.  Each element's K order is the same as gemm_f16_nt's, so each
+ * result equals gemm_f16_nt on the explicitly transposed operands bit for
+ * bit.  Preconditions (otherwise GEMM_F16_UNSUPPORTED): K at most 2^21; for an
+ * operand stored with K contiguous, K a multiple of 8; for one stored [K, M]
+ * or [K, N], M or N a multiple of 8 and K * M * 2 or K * N * 2 below 2^31;
+ * A and B 16-byte aligned.  K = 0 writes +0 without reading A or B.
+ * Ownership, asynchrony, threading and the other status codes as for
+ * gemm_f16_nt; a configuration id of another layout is GEMM_F16_INVALID_ARG
+ * (each configuration's a_layout and b_layout say which it is).  The _plan
+ * functions are the pure host planners (GEMM_F16_UNSUPPORTED where the
  * preconditions on sizes fail).
  */
 int gemm_f16_nn(int64_t M, int64_t N, int64_t K,
@@ -165,6 +171,24 @@ int gemm_f16_nn_with_config(int64_t M, int64_t N, int64_t K,
                             hipStream_t stream, int32_t config_id,
                             int32_t swizzle, int32_t grid, int32_t epilogue);
 int gemm_f16_nn_plan(int64_t M, int64_t N, int64_t K, int32_t num_cus,
+                     gemm_f16_nt_plan_t *plan);
+int gemm_f16_tn(int64_t M, int64_t N, int64_t K,
+                const void *A, const void *B, void *C,
+                hipStream_t stream);
+int gemm_f16_tn_with_config(int64_t M, int64_t N, int64_t K,
+                            const void *A, const void *B, void *C,
+                            hipStream_t stream, int32_t config_id,
+                            int32_t swizzle, int32_t grid, int32_t epilogue);
+int gemm_f16_tn_plan(int64_t M, int64_t N, int64_t K, int32_t num_cus,
+                     gemm_f16_nt_plan_t *plan);
+int gemm_f16_tt(int64_t M, int64_t N, int64_t K,
+                const void *A, const void *B, void *C,
+                hipStream_t stream);
+int gemm_f16_tt_with_config(int64_t M, int64_t N, int64_t K,
+                            const void *A, const void *B, void *C,
+                            hipStream_t stream, int32_t config_id,
+                            int32_t swizzle, int32_t grid, int32_t epilogue);
+int gemm_f16_tt_plan(int64_t M, int64_t N, int64_t K, int32_t num_cus,
                      gemm_f16_nt_plan_t *plan);
 
 /*

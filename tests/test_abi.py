@@ -283,18 +283,27 @@ def test_splitk_host_checks_before_any_device_access(g):
 # ---------------------------------------------------------------------------
 # B stored [K, N] (gemm_f16_nn): planner and host checks
 # ---------------------------------------------------------------------------
-def test_nn_configs_are_their_own(g):
-    nn = [c for c in range(g.gemm_f16_nt_num_configs()) if g.gemm_f16_nt_config_info(c).b_layout == 1]
-    assert nn, "no [K, N] configurations compiled"
-    for c in nn:
-        info = g.gemm_f16_nt_config_info(c)
-        assert info.block_n in (128, 256) and info.block_k == 64
-    # the NT planner never picks one, the NN planner always does
-    for shape in [(8192, 8192, 8192), (128, 16384, 16384), (4999, 7000, 4160), (300, 264, 200)]:
-        assert g.gemm_f16_nt_plan(*shape, 256).b_layout == 0
-        p = g.gemm_f16_nn_plan(*shape, 256)
-        assert p.b_layout == 1 and p.config_id in nn
+@pytest.mark.parametrize("lay", ["nn", "tn", "tt"])
+def test_layout_configs_are_their_own(g, lay):
+    ids = [c for c in range(g.gemm_f16_nt_num_configs())
+           if g.gemm_f16_nt_config_info(c).layout == lay]
+    assert ids, f"no {lay} configurations compiled"
+    plan_fn = getattr(g, f"gemm_f16_{lay}_plan")
+    # the NT planner never picks one, the layout's planner always does
+    for shape in [(8192, 8192, 8192), (4096, 4096, 4096), (4992, 7000, 4160), (304, 264, 200)]:
+        assert g.gemm_f16_nt_plan(*shape, 256).layout == "nt"
+        p = plan_fn(*shape, 256)
+        assert p.layout == lay and p.config_id in ids
         assert p.tiles == p.tiles_m * p.tiles_n and 1 <= p.grid <= min(256, p.tiles)
+
+
+@pytest.mark.parametrize("lay,shape", [("tn", (60, 64, 64)), ("tt", (60, 64, 64)),
+                                       ("tt", (64, 64, 60)), ("tn", (8, 64, 1 << 28)),
+                                       ("tn", (64, 64, (1 << 21) + 8))])
+def test_layout_plan_unsupported(g, lay, shape):
+    with pytest.raises(g.GemmError) as e:
+        getattr(g, f"gemm_f16_{lay}_plan")(*shape, 256)
+    assert e.value.status == 2
 
 
 @pytest.mark.parametrize("shape", [(64, 60, 64), (64, 64, 60), (64, 64, (1 << 21) + 8),
@@ -309,6 +318,8 @@ def test_nn_plan_unsupported(g, shape):
 def test_nn_host_checks_before_any_device_access(g):
     lib = g.load()
     nt_cfg = g.gemm_f16_nt_plan(64, 64, 64, 256).config_id
+    assert lib.gemm_f16_tn(64, 64, 64, A0 + 8, B0, C0, None) == 2        # A 8-byte aligned
+    assert lib.gemm_f16_tt(60, 64, 64, A0, B0, C0, None) == 2            # M % 8 with A [K, M]
     assert lib.gemm_f16_nn(0, 64, 64, A0, B0, C0, None) == 0
     assert lib.gemm_f16_nn(-1, 64, 64, A0, B0, C0, None) == 1
     assert lib.gemm_f16_nn(64, 60, 64, A0, B0, C0, None) == 2            # N % 8

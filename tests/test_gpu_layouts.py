@@ -1,0 +1,154 @@
+"""The other operand layouts (gemm_f16_nn, gemm_f16_tn, gemm_f16_tt) against
+the oracle.
+
+The oracle computes C = fp16_rne(sum_k a(i, k) b(k, j)) for A [M, K] and
+B [N, K]; the tests hand the layouts the same data transposed with numpy
+(pure data movement).  Every layout keeps each element's K order, so each
+must also equal gemm_f16_nt on the untransposed data bit for bit, for every
+configuration of that layout.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import workloads
+from parity import assert_bit_exact, assert_within_tolerance
+
+pytestmark = pytest.mark.gpu
+
+LAYOUTS = ["nn", "tn", "tt"]
+
+
+@pytest.fixture(scope="module")
+def g():
+    import torch
+
+    import dense_fp16_gemm_amd as lib
+
+    lib.load()
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return lib
+
+
+def _say(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def configs_of(g, lay):
+    return [c for c in range(g.gemm_f16_nt_num_configs())
+            if g.gemm_f16_nt_config_info(c).layout == lay]
+
+
+def operands(lay, a_mk, b_nk):
+    """The NT operands a [M, K], b [N, K] stored as the layout wants them."""
+    a = np.ascontiguousarray(a_mk.T) if lay[0] == "t" else a_mk
+    b = np.ascontiguousarray(b_nk.T) if lay[1] == "n" else b_nk
+    return a, b
+
+
+def run_layout(g, lay, a, b, config=None, epilogue=-1):
+    """C through the layout's entry point; C poisoned with NaN first."""
+    import torch
+
+    m = a.shape[1] if lay[0] == "t" else a.shape[0]
+    n = b.shape[1] if lay[1] == "n" else b.shape[0]
+    _say(f"  gpu gemm_{lay} {tuple(a.shape)} x {tuple(b.shape)} config={config} epilogue={epilogue}")
+    dev = torch.device("cuda:0")
+    ta = torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    tb = torch.from_numpy(np.ascontiguousarray(b)).to(dev)
+    flat = torch.full((m * n + 8,), float("nan"), dtype=torch.float16, device=dev)
+    out = flat[:m * n].view(m, n)
+    g.gemm(ta, tb, lay, out=out, config=config, epilogue=epilogue)
+    torch.cuda.synchronize()
+    host = flat.cpu().numpy()
+    assert np.isnan(host[m * n:].astype(np.float32)).all()
+    return host[:m * n].reshape(m, n)
+
+
+def run_nt(g, a_mk, b_nk):
+    import torch
+
+    c = g.gemm_nt(torch.from_numpy(np.ascontiguousarray(a_mk)).cuda(),
+                  torch.from_numpy(np.ascontiguousarray(b_nk)).cuda())
+    torch.cuda.synchronize()
+    return c.cpu().numpy()
+
+
+# M, N, K multiples of 8 (each layout needs them for its contiguous dimension)
+SHAPES = [(256, 256, 256), (304, 264, 200), (512, 392, 136), (32, 40, 24), (128, 64, 520),
+          (1000, 1000, 1000), (64, 1024, 2056), (776, 136, 72)]
+
+
+@pytest.mark.parametrize("lay", LAYOUTS)
+@pytest.mark.parametrize("shape", SHAPES)
+def test_layout_parity_every_config(g, oracle_mod, lay, shape):
+    m, n, k = shape
+    a_mk, b_nk = workloads.make_inputs(m, n, k, "normal", 1.0 / np.sqrt(k), seed=500 + m + n + k)
+    a, b = operands(lay, a_mk, b_nk)
+    ref = oracle_mod.gemm(a_mk, b_nk)
+    nt = run_nt(g, a_mk, b_nk)
+    for cid in configs_of(g, lay):
+        for epi in (0, 1):
+            got = run_layout(g, lay, a, b, config=cid, epilogue=epi)
+            assert_within_tolerance(got, ref, f"{lay} {shape} config {cid} epilogue {epi}")
+            assert_bit_exact(got, nt, f"{lay} {shape} config {cid} epilogue {epi} vs nt")
+
+
+@pytest.mark.parametrize("lay", LAYOUTS)
+def test_layout_integer_bit_exact(g, oracle_mod, lay):
+    a_mk, b_nk = workloads.make_inputs(704, 504, 1032, "int2", 1.0, seed=511)
+    a, b = operands(lay, a_mk, b_nk)
+    assert_bit_exact(run_layout(g, lay, a, b), oracle_mod.gemm(a_mk, b_nk), f"int2 {lay}")
+
+
+@pytest.mark.parametrize("lay", LAYOUTS)
+def test_layout_identity_and_permutation(g, lay):
+    rng = np.random.default_rng(512)
+    a_mk = rng.standard_normal((96, 256)).astype(np.float16)
+    eye = np.eye(256, dtype=np.float16)
+    perm = rng.permutation(256)
+    for b_nk, want, what in [(eye, a_mk, "B = I"), (eye[perm], a_mk[:, perm], "B = permutation")]:
+        a, b = operands(lay, a_mk, b_nk)
+        assert_bit_exact(run_layout(g, lay, a, b), want, f"{lay} {what}")
+
+
+@pytest.mark.parametrize("lay", LAYOUTS)
+def test_layout_k_zero(g, lay):
+    a, b = operands(lay, np.zeros((40, 0), np.float16), np.zeros((48, 0), np.float16))
+    got = run_layout(g, lay, a, b)
+    assert got.shape == (40, 48) and (got.view(np.uint16) == 0).all()
+
+
+def test_layout_unsupported_arguments(g):
+    import torch
+
+    a = torch.zeros((64, 64), dtype=torch.float16, device="cuda")
+    cases = [("nn", a, torch.zeros((64, 60), dtype=torch.float16, device="cuda"), "N % 8"),
+             ("tn", torch.zeros((64, 60), dtype=torch.float16, device="cuda"), a, "M % 8"),
+             ("nn", a, torch.zeros((1, 64 * 64 + 4), dtype=torch.float16, device="cuda")[0, 4:]
+              .view(64, 64), "B 8-byte aligned")]
+    for lay, x, y, why in cases:
+        with pytest.raises(g.GemmError) as e:
+            g.gemm(x, y, lay)
+        assert e.value.status == g.UNSUPPORTED, why
+
+
+@pytest.mark.parametrize("lay", LAYOUTS)
+@pytest.mark.parametrize("name", ["square8192", "skinny128x16384x16384", "square4096_int"])
+def test_layout_full_size_equals_nt(g, lay, name):
+    """At full size, in the launch configuration the planner picks, each
+    layout's result equals the NT result on the same data bit for bit (the NT
+    path is parity-tested against the oracle at these sizes)."""
+    import torch
+
+    a_mk, b_nk = workloads.workload_inputs(name)
+    ta = torch.from_numpy(a_mk).cuda()
+    tb = torch.from_numpy(b_nk).cuda()
+    nt = g.gemm_nt(ta, tb)
+    a = ta.t().contiguous() if lay[0] == "t" else ta
+    b = tb.t().contiguous() if lay[1] == "n" else tb
+    got = g.gemm(a, b, lay)
+    torch.cuda.synchronize()
+    assert torch.equal(got.view(torch.int16), nt.view(torch.int16)), f"{lay} {name}"

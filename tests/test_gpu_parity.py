@@ -96,8 +96,8 @@ def test_parity_every_config(g, oracle_mod, shape):
     ref = oracle_mod.gemm(a, b)
     first = None
     for cid in range(num_configs(g)):
-        if g.gemm_f16_nt_config_info(cid).b_layout != 0:
-            continue                                   # B stored [K, N]: gemm_f16_nn's
+        if g.gemm_f16_nt_config_info(cid).layout != "nt":
+            continue                                   # another operand layout's
         for epi in (0, 1):
             try:
                 got = run_gpu(g, a, b, config=cid, epilogue=epi)
@@ -417,7 +417,7 @@ def test_random_shapes_every_path(g, oracle_mod, case):
     general = g.gemm_f16_nt_num_configs() - 1
     fast_ok = k % 8 == 0 and a_off % 8 == 0 and b_off % 8 == 0
     nt_ids = [c for c in range(g.gemm_f16_nt_num_configs())
-              if g.gemm_f16_nt_config_info(c).b_layout == 0]
+              if g.gemm_f16_nt_config_info(c).layout == "nt"]
     cid = int(rng.choice(nt_ids)) if fast_ok else general
     a, b = workloads.make_inputs(m, n, k, "normal", 1.0 / np.sqrt(k), seed=case)
     got = run_gpu_offset(g, a, b, a_off, b_off, config=cid)
