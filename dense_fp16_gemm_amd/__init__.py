@@ -71,13 +71,17 @@ def load():
         lib.gemm_f16_nt_validate.restype = ctypes.c_int
         lib.gemm_f16_nt_plan.argtypes = [i64, i64, i64, i32, ctypes.POINTER(Plan)]
         lib.gemm_f16_nt_plan.restype = ctypes.c_int
-        lib.gemm_f16_nt_splitk_plan.argtypes = [i64, i64, i64, i32, i32, ctypes.POINTER(Plan),
-                                                ctypes.POINTER(i32), ctypes.POINTER(i64)]
-        lib.gemm_f16_nt_splitk_plan.restype = ctypes.c_int
-        lib.gemm_f16_nt_splitk.argtypes = [i64, i64, i64, p, p, p, i32, p, i64, p]
-        lib.gemm_f16_nt_splitk.restype = ctypes.c_int
-        lib.gemm_f16_nt_splitk_with_config.argtypes = [i64, i64, i64, p, p, p, i32, p, i64, p, i32]
-        lib.gemm_f16_nt_splitk_with_config.restype = ctypes.c_int
+        for lay in ("nt", "nn", "tn", "tt"):
+            f = getattr(lib, f"gemm_f16_{lay}_splitk_plan")
+            f.argtypes = [i64, i64, i64, i32, i32, ctypes.POINTER(Plan), ctypes.POINTER(i32),
+                          ctypes.POINTER(i64)]
+            f.restype = ctypes.c_int
+            f = getattr(lib, f"gemm_f16_{lay}_splitk")
+            f.argtypes = [i64, i64, i64, p, p, p, i32, p, i64, p]
+            f.restype = ctypes.c_int
+            f = getattr(lib, f"gemm_f16_{lay}_splitk_with_config")
+            f.argtypes = [i64, i64, i64, p, p, p, i32, p, i64, p, i32]
+            f.restype = ctypes.c_int
         for lay in ("nn", "tn", "tt"):
             f = getattr(lib, f"gemm_f16_{lay}")
             f.argtypes = [i64, i64, i64, p, p, p, p]
@@ -158,28 +162,35 @@ gemm_f16_tn, gemm_f16_tn_with_config, gemm_f16_tn_plan = _layout_fns("tn")
 gemm_f16_tt, gemm_f16_tt_with_config, gemm_f16_tt_plan = _layout_fns("tt")
 
 
-def gemm_f16_nt_splitk_plan(M: int, N: int, K: int, num_cus: int,
-                            splits: int = 0) -> tuple[Plan, int, int]:
-    """(plan, effective splits, workspace bytes) for the split-K entry point."""
-    plan, eff, wsb = Plan(), ctypes.c_int32(), ctypes.c_int64()
-    _check(load().gemm_f16_nt_splitk_plan(M, N, K, num_cus, splits, ctypes.byref(plan),
-                                          ctypes.byref(eff), ctypes.byref(wsb)),
-           "gemm_f16_nt_splitk_plan")
-    return plan, eff.value, wsb.value
+def _splitk_fns(lay: str):
+    def plan(M: int, N: int, K: int, num_cus: int, splits: int = 0) -> tuple[Plan, int, int]:
+        """(plan, effective splits, workspace bytes) for the split-K entry point."""
+        out, eff, wsb = Plan(), ctypes.c_int32(), ctypes.c_int64()
+        _check(getattr(load(), f"gemm_f16_{lay}_splitk_plan")(M, N, K, num_cus, splits,
+                                                              ctypes.byref(out), ctypes.byref(eff),
+                                                              ctypes.byref(wsb)),
+               f"gemm_f16_{lay}_splitk_plan")
+        return out, eff.value, wsb.value
+
+    def call(M: int, N: int, K: int, A: int, B: int, C: int, splits: int, workspace: int,
+             workspace_bytes: int, stream: int = 0) -> None:
+        _check(getattr(load(), f"gemm_f16_{lay}_splitk")(M, N, K, A, B, C, splits, workspace,
+                                                         workspace_bytes, stream),
+               f"gemm_f16_{lay}_splitk")
+
+    def with_config(M: int, N: int, K: int, A: int, B: int, C: int, splits: int, workspace: int,
+                    workspace_bytes: int, stream: int, config_id: int) -> None:
+        _check(getattr(load(), f"gemm_f16_{lay}_splitk_with_config")(
+            M, N, K, A, B, C, splits, workspace, workspace_bytes, stream, config_id),
+            f"gemm_f16_{lay}_splitk_with_config")
+
+    return plan, call, with_config
 
 
-def gemm_f16_nt_splitk(M: int, N: int, K: int, A: int, B: int, C: int, splits: int,
-                       workspace: int, workspace_bytes: int, stream: int = 0) -> None:
-    _check(load().gemm_f16_nt_splitk(M, N, K, A, B, C, splits, workspace, workspace_bytes,
-                                     stream), "gemm_f16_nt_splitk")
-
-
-def gemm_f16_nt_splitk_with_config(M: int, N: int, K: int, A: int, B: int, C: int,
-                                   splits: int, workspace: int, workspace_bytes: int,
-                                   stream: int, config_id: int) -> None:
-    _check(load().gemm_f16_nt_splitk_with_config(M, N, K, A, B, C, splits, workspace,
-                                                 workspace_bytes, stream, config_id),
-           "gemm_f16_nt_splitk_with_config")
+gemm_f16_nt_splitk_plan, gemm_f16_nt_splitk, gemm_f16_nt_splitk_with_config = _splitk_fns("nt")
+gemm_f16_nn_splitk_plan, gemm_f16_nn_splitk, gemm_f16_nn_splitk_with_config = _splitk_fns("nn")
+gemm_f16_tn_splitk_plan, gemm_f16_tn_splitk, gemm_f16_tn_splitk_with_config = _splitk_fns("tn")
+gemm_f16_tt_splitk_plan, gemm_f16_tt_splitk, gemm_f16_tt_splitk_with_config = _splitk_fns("tt")
 
 
 def gemm_f16_nt_num_configs() -> int:
@@ -236,33 +247,35 @@ def gemm_nt(a, b, out=None, config: int | None = None, swizzle: int = 0, grid: i
     return out
 
 
-def gemm_nt_splitk(a, b, splits: int = 0, out=None, workspace=None, config: int | None = None,
-                   stream=None):
-    """C = a @ b.T with K split (gemm_f16_nt_splitk) for fp16 tensors a [M,K], b [N,K].
-
-    splits <= 0: the library's choice.  The fp32 workspace is allocated with
-    torch unless `workspace` (a device tensor of at least the planned bytes)
-    is given.  Same checks as gemm_nt.
-    """
+def gemm_splitk(a, b, layout: str = "nt", splits: int = 0, out=None, workspace=None,
+                config: int | None = None, stream=None):
+    """C = op(a) @ op(b) with K split (gemm_f16_<layout>_splitk); operands as for
+    gemm().  splits <= 0: the library's choice.  The fp32 workspace is
+    allocated with torch unless `workspace` (a device tensor of at least the
+    planned bytes) is given."""
     import torch
 
+    if layout not in ("nt", "nn", "tn", "tt"):
+        raise ValueError(f"unknown layout {layout!r}")
     if a.dtype != torch.float16 or b.dtype != torch.float16:
         raise TypeError("a and b must be torch.float16")
-    if a.dim() != 2 or b.dim() != 2 or a.shape[1] != b.shape[1]:
-        raise ValueError(f"shape mismatch: a{tuple(a.shape)} b{tuple(b.shape)}")
+    if a.dim() != 2 or b.dim() != 2:
+        raise ValueError("a and b must be matrices")
+    m, k = (a.shape[1], a.shape[0]) if layout[0] == "t" else (a.shape[0], a.shape[1])
+    kb, n = (b.shape[0], b.shape[1]) if layout[1] == "n" else (b.shape[1], b.shape[0])
+    if k != kb:
+        raise ValueError(f"shape mismatch for {layout}: a{tuple(a.shape)} b{tuple(b.shape)}")
     if not (a.is_cuda and b.is_cuda) or a.device != b.device:
         raise ValueError("a and b must be on the same GPU")
     if not (a.is_contiguous() and b.is_contiguous()):
         raise ValueError("a and b must be contiguous (row-major)")
-    m, k = a.shape
-    n = b.shape[0]
     if out is None:
         out = torch.empty((m, n), dtype=torch.float16, device=a.device)
     elif (out.dtype != torch.float16 or tuple(out.shape) != (m, n) or not out.is_contiguous()
           or out.device != a.device):
         raise ValueError("out must be a contiguous float16 [M, N] tensor on a's device")
     cus = torch.cuda.get_device_properties(a.device).multi_processor_count
-    _, _, need = gemm_f16_nt_splitk_plan(m, n, k, cus, splits)
+    _, _, need = globals()[f"gemm_f16_{layout}_splitk_plan"](m, n, k, cus, splits)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=a.device)
     elif not workspace.is_cuda or workspace.device != a.device:
@@ -270,10 +283,17 @@ def gemm_nt_splitk(a, b, splits: int = 0, out=None, workspace=None, config: int 
     ws_bytes = workspace.numel() * workspace.element_size()
     s = stream if stream is not None else torch.cuda.current_stream(a.device)
     with torch.cuda.device(a.device):
-        gemm_f16_nt_splitk_with_config(m, n, k, a.data_ptr(), b.data_ptr(), out.data_ptr(),
-                                       splits, workspace.data_ptr(), ws_bytes, s.cuda_stream,
-                                       -1 if config is None else config)
+        globals()[f"gemm_f16_{layout}_splitk_with_config"](
+            m, n, k, a.data_ptr(), b.data_ptr(), out.data_ptr(), splits, workspace.data_ptr(),
+            ws_bytes, s.cuda_stream, -1 if config is None else config)
     return out
+
+
+def gemm_nt_splitk(a, b, splits: int = 0, out=None, workspace=None, config: int | None = None,
+                   stream=None):
+    """C = a @ b.T with K split (gemm_f16_nt_splitk) for fp16 tensors a [M,K], b [N,K]."""
+    return gemm_splitk(a, b, "nt", splits=splits, out=out, workspace=workspace, config=config,
+                       stream=stream)
 
 
 def gemm(a, b, layout: str = "nt", out=None, config: int | None = None, swizzle: int = 0,

@@ -1166,10 +1166,7 @@ struct KernelEntry {
 template <class CF>
 const void *split_instance()
 {
-    if constexpr (CF::BL == 0 && CF::AL == 0)
-        return reinterpret_cast<const void *>(&gemm_f16_nt_kernel<CF, true>);
-    else
-        return nullptr;
+    return reinterpret_cast<const void *>(&gemm_f16_nt_kernel<CF, true>);
 }
 
 template <class CF>
@@ -1418,14 +1415,14 @@ static double split_cost(int id, int64_t M, int64_t N, int64_t K, int32_t splits
 // config_id >= 0 the configuration; otherwise the cheapest by split_cost.
 // With one split this picks what choose_config picks.
 static void choose_split(int64_t M, int64_t N, int64_t K, int32_t cus, int32_t config_id,
-                         int32_t splits, int *id_out, int32_t *splits_out)
+                         int32_t splits, int *id_out, int32_t *splits_out, int32_t layout = 0)
 {
     double best = 0.0;
     int best_id = -1;
     int64_t best_eff = 1;
     for (int id = 0; id < kNumKernels; ++id) {
         if (config_id >= 0 ? id != config_id
-                           : (kKernels[id].rel_rate <= 0.0f || kKernels[id].layout != 0))
+                           : (kKernels[id].rel_rate <= 0.0f || kKernels[id].layout != layout))
             continue;
         const int32_t s_lo = splits > 0 ? splits : 1;
         const int32_t s_hi = splits > 0 ? splits : kMaxSplits;
@@ -1558,26 +1555,33 @@ static int plan_layout(int32_t layout, int64_t M, int64_t N, int64_t K, int32_t 
     return GEMM_F16_OK;
 }
 
-static int run_splitk(int64_t M, int64_t N, int64_t K, const void *A, const void *B, void *C,
-                      int32_t splits, void *workspace, int64_t workspace_bytes,
-                      hipStream_t stream, int32_t config_id)
+static int run_splitk(int32_t layout, int64_t M, int64_t N, int64_t K, const void *A,
+                      const void *B, void *C, int32_t splits, void *workspace,
+                      int64_t workspace_bytes, hipStream_t stream, int32_t config_id)
 {
     const int v = validate(M, N, K, A, B, C);
     if (v != GEMM_F16_OK) return v;
-    if (config_id >= kNumKernels || (config_id >= 0 && kKernels[config_id].layout != 0) ||
+    if (config_id >= kNumKernels || (config_id >= 0 && kKernels[config_id].layout != layout) ||
         splits > kMaxSplits || workspace_bytes < 0)
         return GEMM_F16_INVALID_ARG;
     if (M == 0 || N == 0) return GEMM_F16_OK;
-    // arguments only the general kernel takes, and K = 0: no split
-    if (K == 0 || needs_general(K, A, B, true) || (config_id >= 0 && kKernels[config_id].general))
-        return run(M, N, K, A, B, C, stream, config_id, 0, 0, -1);
+    if (K == 0) return run(M, N, 0, A, B, C, stream, -1, 0, 0, -1);   // the empty sum
+    if (layout == 0) {
+        // arguments only the general kernel takes: no split
+        if (needs_general(K, A, B, true) || (config_id >= 0 && kKernels[config_id].general))
+            return run(M, N, K, A, B, C, stream, config_id, 0, 0, -1);
+    } else if (!layout_supported(layout, M, N, K, A, B, true)) {
+        return GEMM_F16_UNSUPPORTED;
+    }
     int32_t cus = 0;
     const int s = current_cus(&cus);
     if (s != GEMM_F16_OK) return s;
     int id = -1;
     int32_t eff = 1;
-    choose_split(M, N, K, cus, config_id, splits, &id, &eff);
-    if (eff <= 1) return run(M, N, K, A, B, C, stream, id, 0, 0, -1);
+    choose_split(M, N, K, cus, config_id, splits, &id, &eff, layout);
+    if (eff <= 1)
+        return layout == 0 ? run(M, N, K, A, B, C, stream, id, 0, 0, -1)
+                           : run_layout(layout, M, N, K, A, B, C, stream, id, 0, 0, -1);
     gemm_f16_nt_plan_t plan;
     make_plan(id, M, N, cus, 0, 0, &plan);
     if (plan.tiles * eff > INT32_MAX) return GEMM_F16_UNSUPPORTED;
@@ -1658,51 +1662,6 @@ extern "C" int gemm_f16_nt_plan(int64_t M, int64_t N, int64_t K, int32_t num_cus
     return GEMM_F16_OK;
 }
 
-extern "C" int gemm_f16_nt_splitk_plan(int64_t M, int64_t N, int64_t K, int32_t num_cus,
-                                       int32_t splits, gemm_f16_nt_plan_t *plan,
-                                       int32_t *splits_out, int64_t *workspace_bytes)
-{
-    if (!plan || !splits_out || !workspace_bytes || M < 0 || N < 0 || K < 0 || num_cus <= 0 ||
-        splits > kMaxSplits)
-        return GEMM_F16_INVALID_ARG;
-    if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX || cdiv(M, 64) * cdiv(N, 64) > INT32_MAX)
-        return GEMM_F16_UNSUPPORTED;
-    *splits_out = 1;
-    *workspace_bytes = 0;
-    if (K == 0 || M == 0 || N == 0 || needs_general(K, nullptr, nullptr, false))
-        return gemm_f16_nt_plan(M, N, K, num_cus, plan);
-    int id = -1;
-    int32_t eff = 1;
-    choose_split(M, N, K, num_cus, -1, splits, &id, &eff);
-    make_plan(id, M, N, num_cus, 0, 0, plan);
-    if (eff > 1) {
-        if (plan->tiles * eff > INT32_MAX) return GEMM_F16_UNSUPPORTED;
-        const int64_t units = plan->tiles * eff;
-        const int64_t cap = int64_t(num_cus) * kKernels[id].per_cu;
-        plan->grid = static_cast<int32_t>(units < cap ? units : cap);
-        plan->epilogue = 0;
-        *splits_out = eff;
-        *workspace_bytes = eff * split_stride(M, N) * 4;
-    }
-    return GEMM_F16_OK;
-}
-
-extern "C" int gemm_f16_nt_splitk(int64_t M, int64_t N, int64_t K, const void *A, const void *B,
-                                  void *C, int32_t splits, void *workspace,
-                                  int64_t workspace_bytes, hipStream_t stream)
-{
-    return run_splitk(M, N, K, A, B, C, splits, workspace, workspace_bytes, stream, -1);
-}
-
-extern "C" int gemm_f16_nt_splitk_with_config(int64_t M, int64_t N, int64_t K, const void *A,
-                                              const void *B, void *C, int32_t splits,
-                                              void *workspace, int64_t workspace_bytes,
-                                              hipStream_t stream, int32_t config_id)
-{
-    return run_splitk(M, N, K, A, B, C, splits, workspace, workspace_bytes, stream,
-                      config_id < 0 ? -1 : config_id);
-}
-
 extern "C" int gemm_f16_nn(int64_t M, int64_t N, int64_t K, const void *A, const void *B,
                            void *C, hipStream_t stream)
 {
@@ -1764,6 +1723,130 @@ extern "C" int gemm_f16_tn_plan(int64_t M, int64_t N, int64_t K, int32_t num_cus
                                 gemm_f16_nt_plan_t *plan)
 {
     return plan_layout(3, M, N, K, num_cus, plan);
+}
+
+static int splitk_plan(int32_t layout, int64_t M, int64_t N, int64_t K, int32_t num_cus,
+                       int32_t splits, gemm_f16_nt_plan_t *plan, int32_t *splits_out,
+                       int64_t *workspace_bytes)
+{
+    if (!plan || !splits_out || !workspace_bytes || M < 0 || N < 0 || K < 0 || num_cus <= 0 ||
+        splits > kMaxSplits)
+        return GEMM_F16_INVALID_ARG;
+    if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX || cdiv(M, 64) * cdiv(N, 64) > INT32_MAX)
+        return GEMM_F16_UNSUPPORTED;
+    *splits_out = 1;
+    *workspace_bytes = 0;
+    if (K == 0 || M == 0 || N == 0) return gemm_f16_nt_plan(M, N, K, num_cus, plan);
+    if (layout == 0 && needs_general(K, nullptr, nullptr, false))
+        return gemm_f16_nt_plan(M, N, K, num_cus, plan);
+    if (layout != 0 && !layout_supported(layout, M, N, K, nullptr, nullptr, false))
+        return GEMM_F16_UNSUPPORTED;
+    int id = -1;
+    int32_t eff = 1;
+    choose_split(M, N, K, num_cus, -1, splits, &id, &eff, layout);
+    make_plan(id, M, N, num_cus, 0, 0, plan);
+    if (eff > 1) {
+        if (plan->tiles * eff > INT32_MAX) return GEMM_F16_UNSUPPORTED;
+        const int64_t units = plan->tiles * eff;
+        const int64_t cap = int64_t(num_cus) * kKernels[id].per_cu;
+        plan->grid = static_cast<int32_t>(units < cap ? units : cap);
+        plan->epilogue = 0;
+        *splits_out = eff;
+        *workspace_bytes = eff * split_stride(M, N) * 4;
+    }
+    return GEMM_F16_OK;
+}
+
+extern "C" int gemm_f16_nt_splitk_plan(int64_t M, int64_t N, int64_t K, int32_t num_cus,
+                                       int32_t splits, gemm_f16_nt_plan_t *plan,
+                                       int32_t *splits_out, int64_t *workspace_bytes)
+{
+    return splitk_plan(0, M, N, K, num_cus, splits, plan, splits_out, workspace_bytes);
+}
+
+extern "C" int gemm_f16_nt_splitk(int64_t M, int64_t N, int64_t K, const void *A, const void *B,
+                                  void *C, int32_t splits, void *workspace,
+                                  int64_t workspace_bytes, hipStream_t stream)
+{
+    return run_splitk(0, M, N, K, A, B, C, splits, workspace, workspace_bytes, stream, -1);
+}
+
+extern "C" int gemm_f16_nt_splitk_with_config(int64_t M, int64_t N, int64_t K, const void *A,
+                                              const void *B, void *C, int32_t splits,
+                                              void *workspace, int64_t workspace_bytes,
+                                              hipStream_t stream, int32_t config_id)
+{
+    return run_splitk(0, M, N, K, A, B, C, splits, workspace, workspace_bytes, stream,
+                      config_id < 0 ? -1 : config_id);
+}
+
+extern "C" int gemm_f16_nn_splitk_plan(int64_t M, int64_t N, int64_t K, int32_t num_cus,
+                                       int32_t splits, gemm_f16_nt_plan_t *plan,
+                                       int32_t *splits_out, int64_t *workspace_bytes)
+{
+    return splitk_plan(1, M, N, K, num_cus, splits, plan, splits_out, workspace_bytes);
+}
+
+extern "C" int gemm_f16_nn_splitk(int64_t M, int64_t N, int64_t K, const void *A, const void *B,
+                                  void *C, int32_t splits, void *workspace,
+                                  int64_t workspace_bytes, hipStream_t stream)
+{
+    return run_splitk(1, M, N, K, A, B, C, splits, workspace, workspace_bytes, stream, -1);
+}
+
+extern "C" int gemm_f16_nn_splitk_with_config(int64_t M, int64_t N, int64_t K, const void *A,
+                                              const void *B, void *C, int32_t splits,
+                                              void *workspace, int64_t workspace_bytes,
+                                              hipStream_t stream, int32_t config_id)
+{
+    return run_splitk(1, M, N, K, A, B, C, splits, workspace, workspace_bytes, stream,
+                      config_id < 0 ? -1 : config_id);
+}
+
+extern "C" int gemm_f16_tt_splitk_plan(int64_t M, int64_t N, int64_t K, int32_t num_cus,
+                                       int32_t splits, gemm_f16_nt_plan_t *plan,
+                                       int32_t *splits_out, int64_t *workspace_bytes)
+{
+    return splitk_plan(2, M, N, K, num_cus, splits, plan, splits_out, workspace_bytes);
+}
+
+extern "C" int gemm_f16_tt_splitk(int64_t M, int64_t N, int64_t K, const void *A, const void *B,
+                                  void *C, int32_t splits, void *workspace,
+                                  int64_t workspace_bytes, hipStream_t stream)
+{
+    return run_splitk(2, M, N, K, A, B, C, splits, workspace, workspace_bytes, stream, -1);
+}
+
+extern "C" int gemm_f16_tt_splitk_with_config(int64_t M, int64_t N, int64_t K, const void *A,
+                                              const void *B, void *C, int32_t splits,
+                                              void *workspace, int64_t workspace_bytes,
+                                              hipStream_t stream, int32_t config_id)
+{
+    return run_splitk(2, M, N, K, A, B, C, splits, workspace, workspace_bytes, stream,
+                      config_id < 0 ? -1 : config_id);
+}
+
+extern "C" int gemm_f16_tn_splitk_plan(int64_t M, int64_t N, int64_t K, int32_t num_cus,
+                                       int32_t splits, gemm_f16_nt_plan_t *plan,
+                                       int32_t *splits_out, int64_t *workspace_bytes)
+{
+    return splitk_plan(3, M, N, K, num_cus, splits, plan, splits_out, workspace_bytes);
+}
+
+extern "C" int gemm_f16_tn_splitk(int64_t M, int64_t N, int64_t K, const void *A, const void *B,
+                                  void *C, int32_t splits, void *workspace,
+                                  int64_t workspace_bytes, hipStream_t stream)
+{
+    return run_splitk(3, M, N, K, A, B, C, splits, workspace, workspace_bytes, stream, -1);
+}
+
+extern "C" int gemm_f16_tn_splitk_with_config(int64_t M, int64_t N, int64_t K, const void *A,
+                                              const void *B, void *C, int32_t splits,
+                                              void *workspace, int64_t workspace_bytes,
+                                              hipStream_t stream, int32_t config_id)
+{
+    return run_splitk(3, M, N, K, A, B, C, splits, workspace, workspace_bytes, stream,
+                      config_id < 0 ? -1 : config_id);
 }
 
 extern "C" int gemm_f16_nt_num_configs(void) { return kNumKernels; }

@@ -246,6 +246,50 @@ int gemm_f16_nt_splitk_with_config(int64_t M, int64_t N, int64_t K,
                                    int32_t config_id);
 
 /*
+ * The split over K for the other layouts: the same semantics, planner,
+ * workspace rules and status codes as the gemm_f16_nt_splitk functions
+ * above, for the operands stored as gemm_f16_nn, gemm_f16_tn and gemm_f16_tt
+ * take them (their preconditions apply; arguments outside them are
+ * GEMM_F16_UNSUPPORTED, and K = 0 writes +0).
+ */
+int gemm_f16_nn_splitk_plan(int64_t M, int64_t N, int64_t K, int32_t num_cus,
+                            int32_t splits, gemm_f16_nt_plan_t *plan,
+                            int32_t *splits_out, int64_t *workspace_bytes);
+int gemm_f16_nn_splitk(int64_t M, int64_t N, int64_t K,
+                       const void *A, const void *B, void *C,
+                       int32_t splits, void *workspace, int64_t workspace_bytes,
+                       hipStream_t stream);
+int gemm_f16_nn_splitk_with_config(int64_t M, int64_t N, int64_t K,
+                                   const void *A, const void *B, void *C,
+                                   int32_t splits, void *workspace,
+                                   int64_t workspace_bytes, hipStream_t stream,
+                                   int32_t config_id);
+int gemm_f16_tn_splitk_plan(int64_t M, int64_t N, int64_t K, int32_t num_cus,
+                            int32_t splits, gemm_f16_nt_plan_t *plan,
+                            int32_t *splits_out, int64_t *workspace_bytes);
+int gemm_f16_tn_splitk(int64_t M, int64_t N, int64_t K,
+                       const void *A, const void *B, void *C,
+                       int32_t splits, void *workspace, int64_t workspace_bytes,
+                       hipStream_t stream);
+int gemm_f16_tn_splitk_with_config(int64_t M, int64_t N, int64_t K,
+                                   const void *A, const void *B, void *C,
+                                   int32_t splits, void *workspace,
+                                   int64_t workspace_bytes, hipStream_t stream,
+                                   int32_t config_id);
+int gemm_f16_tt_splitk_plan(int64_t M, int64_t N, int64_t K, int32_t num_cus,
+                            int32_t splits, gemm_f16_nt_plan_t *plan,
+                            int32_t *splits_out, int64_t *workspace_bytes);
+int gemm_f16_tt_splitk(int64_t M, int64_t N, int64_t K,
+                       const void *A, const void *B, void *C,
+                       int32_t splits, void *workspace, int64_t workspace_bytes,
+                       hipStream_t stream);
+int gemm_f16_tt_splitk_with_config(int64_t M, int64_t N, int64_t K,
+                                   const void *A, const void *B, void *C,
+                                   int32_t splits, void *workspace,
+                                   int64_t workspace_bytes, hipStream_t stream,
+                                   int32_t config_id);
+
+/*
  * The tile order the kernel walks (Tilus tutorial "Hopper matmul", page
  * "4. Pipeline Abstraction and Two Consumer Warp Groups", Tile
  * Rasterization; page "6. ...", Persistent Tile Loop), exposed so that host

@@ -328,3 +328,19 @@ def test_nn_host_checks_before_any_device_access(g):
     assert lib.gemm_f16_nn_with_config(64, 64, 64, A0, B0, C0, None, nt_cfg, 0, 0, -1) == 1
     nn_cfg = g.gemm_f16_nn_plan(64, 64, 64, 256).config_id
     assert lib.gemm_f16_nt_with_config(64, 64, 64, A0, B0, C0, None, nn_cfg, 0, 0, -1) == 1
+
+
+@pytest.mark.parametrize("lay", ["nn", "tn", "tt"])
+def test_splitk_plan_layouts(g, lay):
+    plan_fn = getattr(g, f"gemm_f16_{lay}_splitk_plan")
+    plan, eff, ws = plan_fn(1024, 1024, 65536, 256)
+    assert eff > 1 and plan.layout == lay
+    assert ws == eff * _split_stride(1024, 1024) * 4
+    plan1, eff1, ws1 = plan_fn(8192, 8192, 8192, 256)
+    assert eff1 == 1 and ws1 == 0
+    assert plan1.as_dict() == getattr(g, f"gemm_f16_{lay}_plan")(8192, 8192, 8192, 256).as_dict()
+    with pytest.raises(g.GemmError) as e:
+        plan_fn(60, 64, 4096, 256)          # M or N % 8 (or K % 8) as the layout needs
+        plan_fn(64, 60, 4096, 256)
+        plan_fn(64, 64, 4092, 256)
+    assert e.value.status == 2

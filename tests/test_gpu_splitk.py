@@ -173,3 +173,41 @@ def test_full_size_underfilled_workload(g, oracle_mod, name):
     cols = [rng.integers(0, w.N, 4096), np.arange(w.N), np.arange(w.N), np.full(w.M, w.N - 1)]
     r, c = np.concatenate(rows), np.concatenate(cols)
     assert_within_tolerance(got[r, c], oracle_mod.gemm_sampled(a, b, r, c), name)
+
+
+# ---------------------------------------------------------------------------
+# the split over K for the other operand layouts
+# ---------------------------------------------------------------------------
+def _operands(lay, a_mk, b_nk):
+    a = np.ascontiguousarray(a_mk.T) if lay[0] == "t" else a_mk
+    b = np.ascontiguousarray(b_nk.T) if lay[1] == "n" else b_nk
+    return a, b
+
+
+@pytest.mark.parametrize("lay", ["nn", "tn", "tt"])
+@pytest.mark.parametrize("shape,splits", [((256, 256, 16384), 0), ((128, 136, 4104), 5),
+                                          ((384, 256, 40000), 7)])
+def test_splitk_layouts_parity(g, oracle_mod, lay, shape, splits):
+    import torch
+
+    m, n, k = shape
+    a_mk, b_nk = workloads.make_inputs(m, n, k, "normal", 1.0 / np.sqrt(k), seed=320 + k)
+    a, b = _operands(lay, a_mk, b_nk)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    _, eff, _ = getattr(g, f"gemm_f16_{lay}_splitk_plan")(m, n, k, cus, splits)
+    assert eff > 1, "the case must exercise the split path"
+    _say(f"  gpu splitk {lay} {shape} splits={splits}")
+    c = g.gemm_splitk(torch.from_numpy(a).cuda(), torch.from_numpy(b).cuda(), lay, splits=splits)
+    torch.cuda.synchronize()
+    assert_within_tolerance(c.cpu().numpy(), oracle_mod.gemm(a_mk, b_nk), f"splitk {lay} {shape}")
+
+
+@pytest.mark.parametrize("lay", ["nn", "tn", "tt"])
+def test_splitk_layouts_integer_bit_exact(g, oracle_mod, lay):
+    import torch
+
+    a_mk, b_nk = workloads.make_inputs(200, 304, 6152, "int2", 1.0, seed=331)
+    a, b = _operands(lay, a_mk, b_nk)
+    c = g.gemm_splitk(torch.from_numpy(a).cuda(), torch.from_numpy(b).cuda(), lay, splits=6)
+    torch.cuda.synchronize()
+    assert_bit_exact(c.cpu().numpy(), oracle_mod.gemm(a_mk, b_nk), f"int2 splitk {lay}")
