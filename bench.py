@@ -118,9 +118,10 @@ def main() -> int:
     ap.add_argument("--splitk", type=int, default=None,
                     help="time gemm_f16_nt_splitk with this many K splits (0: the library's "
                          "choice); a step is then the split GEMM and its reduction")
-    ap.add_argument("--nn", action="store_true",
-                    help="time gemm_f16_nn: B is handed over transposed, [K, N] row-major "
-                         "(transposed before anything is timed; same result bits as NT)")
+    ap.add_argument("--layout", default="nt", choices=("nt", "nn", "tn", "tt"),
+                    help="operand layout timed: A [K, M] for tn/tt, B [K, N] for nn/tn "
+                         "(transposed before anything is timed; same result bits as nt)")
+    ap.add_argument("--nn", action="store_true", help="the same as --layout nn")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -167,32 +168,34 @@ def main() -> int:
 
     stream = torch.cuda.current_stream(dev)
 
-    if args.nn and args.splitk is not None:
-        print("bench.py: --nn and --splitk do not combine", file=sys.stderr)
-        return 2
-    if args.nn:
-        b_kn = b.t().contiguous()
-        plan = g.gemm_f16_nn_plan(w.M, w.N, w.K, cus).as_dict()
+    lay = "nn" if args.nn else args.layout
+    # operands as the layout stores them, prepared before anything is timed
+    xa = a.t().contiguous() if lay[0] == "t" else a
+    xb = b.t().contiguous() if lay[1] == "n" else b
+    if lay != "nt" and args.splitk is None:
+        plan = getattr(g, f"gemm_f16_{lay}_plan")(w.M, w.N, w.K, cus).as_dict()
         if args.config is not None:
             info = g.gemm_f16_nt_config_info(args.config).as_dict()
             plan.update({k: info[k] for k in ("config_id", "block_m", "block_n", "block_k",
-                                              "waves", "stages", "lds_bytes", "b_layout")})
+                                              "waves", "stages", "lds_bytes", "a_layout",
+                                              "b_layout")})
 
         def launch():
-            g.gemm_nn(a, b_kn, out=c, config=args.config, swizzle=args.swizzle, grid=args.grid,
-                      stream=stream, epilogue=args.epilogue)
+            g.gemm(xa, xb, lay, out=c, config=args.config, swizzle=args.swizzle, grid=args.grid,
+                   stream=stream, epilogue=args.epilogue)
     elif args.splitk is not None:
         # the workspace is allocated once, before anything is timed
-        sk_plan, splits, ws_bytes = g.gemm_f16_nt_splitk_plan(w.M, w.N, w.K, cus, args.splitk)
+        sk_plan, splits, ws_bytes = getattr(g, f"gemm_f16_{lay}_splitk_plan")(
+            w.M, w.N, w.K, cus, args.splitk)
         plan = sk_plan.as_dict()
         plan.update({"splits": splits, "workspace_bytes": ws_bytes})
         ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+        split_fn = getattr(g, f"gemm_f16_{lay}_splitk_with_config")
 
         def launch():
-            g.gemm_f16_nt_splitk_with_config(w.M, w.N, w.K, a.data_ptr(), b.data_ptr(),
-                                             c.data_ptr(), args.splitk, ws.data_ptr(), ws_bytes,
-                                             stream.cuda_stream,
-                                             -1 if args.config is None else args.config)
+            split_fn(w.M, w.N, w.K, xa.data_ptr(), xb.data_ptr(), c.data_ptr(), args.splitk,
+                     ws.data_ptr(), ws_bytes, stream.cuda_stream,
+                     -1 if args.config is None else args.config)
     else:
         def launch():
             g.gemm_nt(a, b, out=c, config=args.config, swizzle=args.swizzle, grid=args.grid,
@@ -227,8 +230,8 @@ def main() -> int:
 
     tflops = w.flops / (ms_per_step * 1e-3) / 1e12
     compute_bound = w.flops / w.algorithmic_bytes > (PEAK_FP16_TFLOPS * 1e12) / (PEAK_HBM_GBS * 1e9)
-    traffic = measured_traffic(name + ("_splitk" if args.splitk is not None else
-                                       "_nn" if args.nn else ""))
+    traffic = measured_traffic(name + ("" if lay == "nt" else "_" + lay) +
+                               ("_splitk" if args.splitk is not None else ""))
     if compute_bound:
         achieved = w.flops / (kernel_avg_ms * 1e-3) / 1e12
         roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP16_TFLOPS,
@@ -252,11 +255,12 @@ def main() -> int:
         "scaling": "weak",
         # the pages' figure is for the NT form of the headline shape only
         "vs_baseline": (round(tflops / PAGES_H100_TFLOPS, 3)
-                        if name == workloads.HEADLINE and not args.nn and args.splitk is None
+                        if name == workloads.HEADLINE and lay == "nt" and args.splitk is None
                         else None),
         "dtype": "f16",
         "data": "synthetic",
-        "config": {"workload": name, "M": w.M, "N": w.N, "K": w.K, "inputs": w.note,
+        "config": {"workload": name, "M": w.M, "N": w.N, "K": w.K, "layout": lay,
+                   "inputs": w.note,
                    "seed": w.seed, "accumulate": "f32", "plan": plan,
                    "kernel_ms_avg": round(kernel_avg_ms, 5),
                    "kernel_ms_min": round(kernel_ms[0], 5),
