@@ -1048,7 +1048,26 @@ __device__ __forceinline__ half8_t load_chunk(const uint16_t *base, int32_t rows
     return v;
 }
 
-template <class CF>
+// An 8-k chunk of one row of an operand stored with k outermost ([K, M] or
+// [K, N], row pitch ld): element e is base[(k + e) ld + row], zero past the
+// valid rows or K.  Lanes take consecutive rows, so each of the 8 two-byte
+// loads of a wave reads one contiguous run.
+__device__ __forceinline__ half8_t load_chunk_kn(const uint16_t *base, int32_t rows_valid, int row,
+                                                 int64_t ld, int64_t K, int64_t k)
+{
+    half8_t v = {};
+    if (row < rows_valid) {
+        const _Float16 *src = reinterpret_cast<const _Float16 *>(base) + row;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if (k + e < K) v[e] = src[(k + e) * ld];
+    }
+    return v;
+}
+
+// LA, LB: A stored [K, M] / B stored [K, N] (see Cfg's AL and BL); the LDS
+// tiles keep the [rows][K] layout either way, so only the loads differ.
+template <class CF, int LA, int LB>
 __global__ __launch_bounds__(CF::THREADS)
 __attribute__((amdgpu_waves_per_eu(3)))
 void gemm_f16_nt_any_kernel(Params p)
@@ -1077,34 +1096,43 @@ void gemm_f16_nt_any_kernel(Params p)
         t.m0 = tile_m * CF::BM;
         t.n0 = tile_n * CF::BN;
         const int32_t rows_a = min(CF::BM, p.M - t.m0), rows_b = min(CF::BN, p.N - t.n0);
-        const uint16_t *a0 = p.A + static_cast<int64_t>(t.m0) * K;
-        const uint16_t *b0 = p.B + static_cast<int64_t>(t.n0) * K;
+        // a tile's first row (K-contiguous) or first column ([K, M] / [K, N])
+        const uint16_t *a0 = p.A + (LA ? static_cast<int64_t>(t.m0) : static_cast<int64_t>(t.m0) * K);
+        const uint16_t *b0 = p.B + (LB ? static_cast<int64_t>(t.n0) : static_cast<int64_t>(t.n0) * K);
+        // chunk c of a slice: K-contiguous operands walk a row's chunks with
+        // consecutive threads, k-outermost ones walk rows (coalesced loads)
+        auto row_of = [](int c, int rows, bool kn) { return kn ? c % rows : c / CF::CHUNKS; };
+        auto kchunk_of = [](int c, int rows, bool kn) { return kn ? c / rows : c % CF::CHUNKS; };
         auto load = [&](int kt) {
 #pragma unroll
             for (int q = 0; q < A_CH; ++q) {
                 const int c = q * CF::THREADS + tid;
-                ra[q] = load_chunk<CF>(a0, rows_a, c / CF::CHUNKS, K,
-                                       static_cast<int64_t>(kt) * CF::BK + (c % CF::CHUNKS) * 8);
+                const int row = row_of(c, CF::BM, LA);
+                const int64_t k = static_cast<int64_t>(kt) * CF::BK + kchunk_of(c, CF::BM, LA) * 8;
+                ra[q] = LA ? load_chunk_kn(a0, rows_a, row, p.M, K, k)
+                           : load_chunk<CF>(a0, rows_a, row, K, k);
             }
 #pragma unroll
             for (int q = 0; q < B_CH; ++q) {
                 const int c = q * CF::THREADS + tid;
-                rb[q] = load_chunk<CF>(b0, rows_b, c / CF::CHUNKS, K,
-                                       static_cast<int64_t>(kt) * CF::BK + (c % CF::CHUNKS) * 8);
+                const int row = row_of(c, CF::BN, LB);
+                const int64_t k = static_cast<int64_t>(kt) * CF::BK + kchunk_of(c, CF::BN, LB) * 8;
+                rb[q] = LB ? load_chunk_kn(b0, rows_b, row, p.N, K, k)
+                           : load_chunk<CF>(b0, rows_b, row, K, k);
             }
         };
         auto store = [&](int stage) {
 #pragma unroll
             for (int q = 0; q < A_CH; ++q) {
-                const int c = q * CF::THREADS + tid, row = c / CF::CHUNKS;
-                const int phys = (c % CF::CHUNKS) ^ chunk_swizzle<CF::CHUNKS, CF::MI>(row);
+                const int c = q * CF::THREADS + tid, row = row_of(c, CF::BM, LA);
+                const int phys = kchunk_of(c, CF::BM, LA) ^ chunk_swizzle<CF::CHUNKS, CF::MI>(row);
                 *reinterpret_cast<half8_t *>(smem + stage * CF::STAGE_BYTES + row * CF::ROW_BYTES +
                                              phys * 16) = ra[q];
             }
 #pragma unroll
             for (int q = 0; q < B_CH; ++q) {
-                const int c = q * CF::THREADS + tid, row = c / CF::CHUNKS;
-                const int phys = (c % CF::CHUNKS) ^ chunk_swizzle<CF::CHUNKS, CF::MI>(row);
+                const int c = q * CF::THREADS + tid, row = row_of(c, CF::BN, LB);
+                const int phys = kchunk_of(c, CF::BN, LB) ^ chunk_swizzle<CF::CHUNKS, CF::MI>(row);
                 *reinterpret_cast<half8_t *>(smem + stage * CF::STAGE_BYTES + CF::A_BYTES +
                                              row * CF::ROW_BYTES + phys * 16) = rb[q];
             }
@@ -1177,12 +1205,12 @@ KernelEntry entry(int swizzle, float rate)
                        swizzle, rate, CF::STAGED_OK ? 1 : 0, 0, 1, 2 * CF::AL + CF::BL};
 }
 
-template <class CF>
+template <class CF, int LA = 0, int LB = 0>
 KernelEntry entry_general(int swizzle)
 {
-    return KernelEntry{reinterpret_cast<const void *>(&gemm_f16_nt_any_kernel<CF>), nullptr,
-                       CF::BM, CF::BN, CF::BK, CF::WAVES, CF::STAGES, CF::LDS_BYTES, CF::THREADS,
-                       swizzle, 0.0f, 0, 1, 3, 0};
+    return KernelEntry{reinterpret_cast<const void *>(&gemm_f16_nt_any_kernel<CF, LA, LB>),
+                       nullptr, CF::BM, CF::BN, CF::BK, CF::WAVES, CF::STAGES, CF::LDS_BYTES,
+                       CF::THREADS, swizzle, 0.0f, 0, 1, 3, 2 * LA + LB};
 }
 
 static const KernelEntry kKernels[] = {
@@ -1237,7 +1265,13 @@ static const KernelEntry kKernels[] = {
     entry<Cfg<256, 256, 64, 2, 2, 2, 16, 0, 16, 0, 1, 1>>(8, 1.06f),   // 33
     entry<Cfg<256, 128, 64, 2, 2, 2, 16, 0, 12, 1, 1, 1>>(8, 0.85f),   // 34
     entry<Cfg<128, 128, 64, 2, 2, 2, 16, 0, 8, 1, 1, 1>>(8, 0.75f),    // 35
-    // 36: the general kernel, 4 waves of 64x64, two register-staged buffers of
+    // 36-38: the general kernel for NN, TT and TN (loads along the operand's
+    // contiguous dimension), for arguments the direct-to-LDS kernels of those
+    // layouts cannot take
+    entry_general<Cfg<128, 128, 32, 2, 2, 2>, 0, 1>(8),
+    entry_general<Cfg<128, 128, 32, 2, 2, 2>, 1, 0>(8),
+    entry_general<Cfg<128, 128, 32, 2, 2, 2>, 1, 1>(8),
+    // 39: the general kernel, 4 waves of 64x64, two register-staged buffers of
     // K 32; planned only when the direct-to-LDS path cannot run
     entry_general<Cfg<128, 128, 32, 2, 2, 2>>(8),
 };
@@ -1517,6 +1551,14 @@ static bool layout_supported(int32_t layout, int64_t M, int64_t N, int64_t K, co
     return reinterpret_cast<uintptr_t>(A) % 16 == 0 && reinterpret_cast<uintptr_t>(B) % 16 == 0;
 }
 
+// The general kernel of a layout (any sizes, any 2-byte alignment).
+static int general_config(int32_t layout)
+{
+    for (int id = 0; id < kNumKernels; ++id)
+        if (kKernels[id].general && kKernels[id].layout == layout) return id;
+    return kGeneralConfig;
+}
+
 static int run_layout(int32_t layout, int64_t M, int64_t N, int64_t K, const void *A,
                       const void *B, void *C, hipStream_t stream, int32_t config_id,
                       int32_t swizzle, int32_t grid, int32_t epilogue)
@@ -1527,11 +1569,15 @@ static int run_layout(int32_t layout, int64_t M, int64_t N, int64_t K, const voi
         return GEMM_F16_INVALID_ARG;
     if (M == 0 || N == 0) return GEMM_F16_OK;
     if (K == 0) return run(M, N, 0, A, B, C, stream, -1, 0, 0, -1);   // the empty sum
-    if (!layout_supported(layout, M, N, K, A, B, true)) return GEMM_F16_UNSUPPORTED;
+    // arguments the direct-to-LDS kernels of the layout cannot take run its
+    // general kernel
+    const bool fast = layout_supported(layout, M, N, K, A, B, true);
+    if (!fast && config_id >= 0 && !kKernels[config_id].general) return GEMM_F16_UNSUPPORTED;
     int32_t cus = 0;
     const int s = current_cus(&cus);
     if (s != GEMM_F16_OK) return s;
-    const int id = config_id >= 0 ? config_id : choose_config(M, N, cus, layout);
+    const int id = config_id >= 0 ? config_id
+                                  : (fast ? choose_config(M, N, cus, layout) : general_config(layout));
     gemm_f16_nt_plan_t plan;
     make_plan(id, M, N, cus, swizzle, grid, &plan);
     if (epilogue < 0) {
@@ -1550,8 +1596,9 @@ static int plan_layout(int32_t layout, int64_t M, int64_t N, int64_t K, int32_t 
     if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX || cdiv(M, 64) * cdiv(N, 64) > INT32_MAX)
         return GEMM_F16_UNSUPPORTED;
     if (K == 0) return gemm_f16_nt_plan(M, N, K, num_cus, plan);
-    if (!layout_supported(layout, M, N, K, nullptr, nullptr, false)) return GEMM_F16_UNSUPPORTED;
-    make_plan(choose_config(M, N, num_cus, layout), M, N, num_cus, 0, 0, plan);
+    const int id = layout_supported(layout, M, N, K, nullptr, nullptr, false)
+                       ? choose_config(M, N, num_cus, layout) : general_config(layout);
+    make_plan(id, M, N, num_cus, 0, 0, plan);
     return GEMM_F16_OK;
 }
 
@@ -1570,8 +1617,10 @@ static int run_splitk(int32_t layout, int64_t M, int64_t N, int64_t K, const voi
         // arguments only the general kernel takes: no split
         if (needs_general(K, A, B, true) || (config_id >= 0 && kKernels[config_id].general))
             return run(M, N, K, A, B, C, stream, config_id, 0, 0, -1);
-    } else if (!layout_supported(layout, M, N, K, A, B, true)) {
-        return GEMM_F16_UNSUPPORTED;
+    } else if (!layout_supported(layout, M, N, K, A, B, true) ||
+               (config_id >= 0 && kKernels[config_id].general)) {
+        // the layout's general kernel, without a split
+        return run_layout(layout, M, N, K, A, B, C, stream, config_id, 0, 0, -1);
     }
     int32_t cus = 0;
     const int s = current_cus(&cus);
@@ -1740,7 +1789,7 @@ static int splitk_plan(int32_t layout, int64_t M, int64_t N, int64_t K, int32_t 
     if (layout == 0 && needs_general(K, nullptr, nullptr, false))
         return gemm_f16_nt_plan(M, N, K, num_cus, plan);
     if (layout != 0 && !layout_supported(layout, M, N, K, nullptr, nullptr, false))
-        return GEMM_F16_UNSUPPORTED;
+        return plan_layout(layout, M, N, K, num_cus, plan);   // the general kernel, no split
     int id = -1;
     int32_t eff = 1;
     choose_split(M, N, K, num_cus, -1, splits, &id, &eff, layout);

@@ -153,15 +153,18 @@ int gemm_f16_nt_with_config(int64_t M, int64_t N, int64_t K,
  * that form in LDS and its MFMA fragments read through gfx950's transposing
  * LDS read.  Each element's K order is the same as gemm_f16_nt's, so each
  * result equals gemm_f16_nt on the explicitly transposed operands bit for
- * bit.  Preconditions (otherwise GEMM_F16_UNSUPPORTED): K at most 2^21; for an
- * operand stored with K contiguous, K a multiple of 8; for one stored [K, M]
- * or [K, N], M or N a multiple of 8 and K * M * 2 or K * N * 2 below 2^31;
- * A and B 16-byte aligned.  K = 0 writes +0 without reading A or B.
- * Ownership, asynchrony, threading and the other status codes as for
- * gemm_f16_nt; a configuration id of another layout is GEMM_F16_INVALID_ARG
- * (each configuration's a_layout and b_layout say which it is).  The _plan
- * functions are the pure host planners (GEMM_F16_UNSUPPORTED where the
- * preconditions on sizes fail).
+ * bit.  The direct-to-LDS kernels of these layouts need K at most 2^21; for
+ * an operand stored with K contiguous, K a multiple of 8; for one stored
+ * [K, M] or [K, N], M or N a multiple of 8 and K * M * 2 or K * N * 2 below
+ * 2^31; and A and B 16-byte aligned.  Other arguments run the layout's
+ * general kernel (register-staged loads along each operand's contiguous
+ * dimension, any sizes and 2-byte alignment), with the same results, more
+ * slowly; a forced direct-to-LDS configuration on such arguments is
+ * GEMM_F16_UNSUPPORTED.  K = 0 writes +0 without reading A or B.  Ownership,
+ * asynchrony, threading and the other status codes as for gemm_f16_nt; a
+ * configuration id of another layout is GEMM_F16_INVALID_ARG (each
+ * configuration's a_layout and b_layout say which it is).  The _plan
+ * functions are the pure host planners.
  */
 int gemm_f16_nn(int64_t M, int64_t N, int64_t K,
                 const void *A, const void *B, void *C,
@@ -249,8 +252,8 @@ int gemm_f16_nt_splitk_with_config(int64_t M, int64_t N, int64_t K,
  * The split over K for the other layouts: the same semantics, planner,
  * workspace rules and status codes as the gemm_f16_nt_splitk functions
  * above, for the operands stored as gemm_f16_nn, gemm_f16_tn and gemm_f16_tt
- * take them (their preconditions apply; arguments outside them are
- * GEMM_F16_UNSUPPORTED, and K = 0 writes +0).
+ * take them.  Arguments only the layout's general kernel takes run it
+ * without a split (as gemm_f16_nt_splitk does for NT), and K = 0 writes +0.
  */
 int gemm_f16_nn_splitk_plan(int64_t M, int64_t N, int64_t K, int32_t num_cus,
                             int32_t splits, gemm_f16_nt_plan_t *plan,

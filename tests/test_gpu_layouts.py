@@ -91,7 +91,11 @@ def test_layout_parity_every_config(g, oracle_mod, lay, shape):
     nt = run_nt(g, a_mk, b_nk)
     for cid in configs_of(g, lay):
         for epi in (0, 1):
-            got = run_layout(g, lay, a, b, config=cid, epilogue=epi)
+            try:
+                got = run_layout(g, lay, a, b, config=cid, epilogue=epi)
+            except g.GemmError as e:
+                assert epi == 1 and e.status == g.UNSUPPORTED   # no room to stage C
+                continue
             assert_within_tolerance(got, ref, f"{lay} {shape} config {cid} epilogue {epi}")
             assert_bit_exact(got, nt, f"{lay} {shape} config {cid} epilogue {epi} vs nt")
 
@@ -121,18 +125,54 @@ def test_layout_k_zero(g, lay):
     assert got.shape == (40, 48) and (got.view(np.uint16) == 0).all()
 
 
-def test_layout_unsupported_arguments(g):
+@pytest.mark.parametrize("lay", LAYOUTS)
+@pytest.mark.parametrize("shape", [(61, 70, 45), (33, 31, 24), (130, 257, 1001), (7, 9, 3),
+                                   (200, 136, 64), (129, 64, 520)])
+def test_layout_general_sizes(g, oracle_mod, lay, shape):
+    """M, N or K not multiples of 8 (and, for comparison, shapes that are):
+    the layout's general kernel where the direct-to-LDS ones cannot run."""
+    m, n, k = shape
+    a_mk, b_nk = workloads.make_inputs(m, n, k, "normal", 1.0 / np.sqrt(k), seed=600 + m + n + k)
+    a, b = operands(lay, a_mk, b_nk)
+    got = run_layout(g, lay, a, b)
+    assert_within_tolerance(got, oracle_mod.gemm(a_mk, b_nk), f"{lay} {shape}")
+    assert_bit_exact(got, run_nt(g, a_mk, b_nk), f"{lay} {shape} vs nt")
+
+
+@pytest.mark.parametrize("lay", LAYOUTS)
+@pytest.mark.parametrize("a_off,b_off", [(1, 0), (0, 3), (4, 4), (7, 2)])
+def test_layout_general_unaligned(g, oracle_mod, lay, a_off, b_off):
+    """A or B only 2-, 4- or 8-byte aligned: the layout's general kernel, with
+    the same bits as the aligned call."""
     import torch
 
-    a = torch.zeros((64, 64), dtype=torch.float16, device="cuda")
-    cases = [("nn", a, torch.zeros((64, 60), dtype=torch.float16, device="cuda"), "N % 8"),
-             ("tn", torch.zeros((64, 60), dtype=torch.float16, device="cuda"), a, "M % 8"),
-             ("nn", a, torch.zeros((1, 64 * 64 + 4), dtype=torch.float16, device="cuda")[0, 4:]
-              .view(64, 64), "B 8-byte aligned")]
-    for lay, x, y, why in cases:
-        with pytest.raises(g.GemmError) as e:
-            g.gemm(x, y, lay)
-        assert e.value.status == g.UNSUPPORTED, why
+    m, n, k = 136, 200, 264
+    a_mk, b_nk = workloads.make_inputs(m, n, k, "uniform", 1.0 / np.sqrt(k), seed=610)
+    a, b = operands(lay, a_mk, b_nk)
+    dev = torch.device("cuda:0")
+    fa = torch.zeros(a.size + 8, dtype=torch.float16, device=dev)
+    fb = torch.zeros(b.size + 8, dtype=torch.float16, device=dev)
+    fa[a_off:a_off + a.size] = torch.from_numpy(a.ravel()).to(dev)
+    fb[b_off:b_off + b.size] = torch.from_numpy(b.ravel()).to(dev)
+    ta = fa[a_off:a_off + a.size].view(a.shape)
+    tb = fb[b_off:b_off + b.size].view(b.shape)
+    _say(f"  gpu gemm_{lay} unaligned a_off={a_off} b_off={b_off}")
+    got = g.gemm(ta, tb, lay)
+    torch.cuda.synchronize()
+    got = got.cpu().numpy()
+    assert_within_tolerance(got, oracle_mod.gemm(a_mk, b_nk), f"{lay} offsets {a_off},{b_off}")
+    assert_bit_exact(got, run_layout(g, lay, a, b), f"{lay} offsets {a_off},{b_off} vs aligned")
+
+
+def test_layout_forced_fast_config_rejects_general_arguments(g):
+    import torch
+
+    a = torch.zeros((64, 60), dtype=torch.float16, device="cuda")     # K = 60 for nn
+    b = torch.zeros((60, 64), dtype=torch.float16, device="cuda")
+    fast = [c for c in configs_of(g, "nn") if g.gemm_f16_nt_config_info(c).block_k == 64][0]
+    with pytest.raises(g.GemmError) as e:
+        g.gemm(a, b, "nn", config=fast)
+    assert e.value.status == g.UNSUPPORTED
 
 
 @pytest.mark.parametrize("lay", LAYOUTS)
