@@ -48,6 +48,15 @@
 // chunk beyond K is given an offset past the resource, which also reads as
 // zero (the template needs K a multiple of 8, so chunks never straddle K;
 // other K, and A or B not 16-byte aligned, go to the general kernel).
+//
+// Beyond the pages' NT form, the same template covers
+//  * the other operand layouts (B stored [K, N], A stored [K, M]): such a
+//    tile keeps its memory layout in LDS and its fragments are read with the
+//    transposing LDS read, so each element's K order, and every result bit,
+//    stays that of the NT form (see kn_swizzle);
+//  * a split over K for tile counts that leave most CUs idle: a second
+//    instance of each configuration runs (range, tile) work units that store
+//    fp32 partials, and splitk_reduce_kernel sums them in range order.
 #include <hip/hip_runtime.h>
 
 #include <mutex>
