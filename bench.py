@@ -122,6 +122,12 @@ def main() -> int:
                     help="operand layout timed: A [K, M] for tn/tt, B [K, N] for nn/tn "
                          "(transposed before anything is timed; same result bits as nt)")
     ap.add_argument("--nn", action="store_true", help="the same as --layout nn")
+    ap.add_argument("--autotune", action="store_true",
+                    help="before anything is timed, time every configuration and split count "
+                         "of the layout on these operands (gemm_f16_autotune), then time the "
+                         "fastest")
+    ap.add_argument("--tune-iters", type=int, default=10,
+                    help="timed calls per autotuning candidate")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -169,10 +175,33 @@ def main() -> int:
     stream = torch.cuda.current_stream(dev)
 
     lay = "nn" if args.nn else args.layout
+    if args.autotune and (args.config is not None or args.splitk is not None):
+        print("bench.py: --autotune chooses the configuration and split itself", file=sys.stderr)
+        return 2
     # operands as the layout stores them, prepared before anything is timed
     xa = a.t().contiguous() if lay[0] == "t" else a
     xb = b.t().contiguous() if lay[1] == "n" else b
-    if lay != "nt" and args.splitk is None:
+    tune = None
+    if args.autotune:
+        # the search and its workspace come before anything is timed
+        code = g.LAYOUT_CODES[lay]
+        _, ws_bytes = g.gemm_f16_autotune_candidates(code, w.M, w.N, w.K, cus, True, 0)
+        ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+        t0 = time.perf_counter()
+        tuned = g.autotune(xa, xb, lay, iters=args.tune_iters, out=c, workspace=ws,
+                           stream=stream)
+        torch.cuda.synchronize()
+        tune = {"config_id": tuned.config, "splits": tuned.splits,
+                "tuned_ms": round(tuned.ms, 5), "candidates": len(tuned.entries),
+                "search_s": round(time.perf_counter() - t0, 2)}
+        plan = g.gemm_f16_nt_config_info(tuned.config).as_dict()
+        plan.update({"splits": tuned.splits, "workspace_bytes": ws_bytes})
+        split_fn = getattr(g, f"gemm_f16_{lay}_splitk_with_config")
+
+        def launch():
+            split_fn(w.M, w.N, w.K, xa.data_ptr(), xb.data_ptr(), c.data_ptr(), tuned.splits,
+                     ws.data_ptr(), ws_bytes, stream.cuda_stream, tuned.config)
+    elif lay != "nt" and args.splitk is None:
         plan = getattr(g, f"gemm_f16_{lay}_plan")(w.M, w.N, w.K, cus).as_dict()
         if args.config is not None:
             info = g.gemm_f16_nt_config_info(args.config).as_dict()
@@ -231,7 +260,8 @@ def main() -> int:
     tflops = w.flops / (ms_per_step * 1e-3) / 1e12
     compute_bound = w.flops / w.algorithmic_bytes > (PEAK_FP16_TFLOPS * 1e12) / (PEAK_HBM_GBS * 1e9)
     traffic = measured_traffic(name + ("" if lay == "nt" else "_" + lay) +
-                               ("_splitk" if args.splitk is not None else ""))
+                               ("_splitk" if args.splitk is not None else "") +
+                               ("_autotune" if args.autotune else ""))
     if compute_bound:
         achieved = w.flops / (kernel_avg_ms * 1e-3) / 1e12
         roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP16_TFLOPS,
@@ -256,12 +286,13 @@ def main() -> int:
         # the pages' figure is for the NT form of the headline shape only
         "vs_baseline": (round(tflops / PAGES_H100_TFLOPS, 3)
                         if name == workloads.HEADLINE and lay == "nt" and args.splitk is None
-                        else None),
+                        and not args.autotune else None),
         "dtype": "f16",
         "data": "synthetic",
         "config": {"workload": name, "M": w.M, "N": w.N, "K": w.K, "layout": lay,
                    "inputs": w.note,
                    "seed": w.seed, "accumulate": "f32", "plan": plan,
+                   "autotune": tune,
                    "kernel_ms_avg": round(kernel_avg_ms, 5),
                    "kernel_ms_min": round(kernel_ms[0], 5),
                    "kernel_ms_max": round(kernel_ms[-1], 5),

@@ -45,6 +45,19 @@ class Plan(ctypes.Structure):
         return {name: getattr(self, name) for name, _ in self._fields_}
 
 
+class TuneEntry(ctypes.Structure):
+    """One autotuning candidate: a configuration and an effective split count."""
+    _fields_ = [("config_id", ctypes.c_int32), ("splits", ctypes.c_int32),
+                ("status", ctypes.c_int32), ("ms", ctypes.c_float)]
+
+    def as_dict(self) -> dict:
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+# the library's layout codes: 2 * (A stored [K, M]) + (B stored [K, N])
+LAYOUT_CODES = {"nt": 0, "nn": 1, "tt": 2, "tn": 3}
+
+
 def library_path() -> str:
     return LIB_PATH
 
@@ -99,6 +112,13 @@ def load():
         lib.gemm_f16_nt_tile_of_slot.argtypes = [ctypes.POINTER(Plan), i64,
                                                  ctypes.POINTER(i32), ctypes.POINTER(i32)]
         lib.gemm_f16_nt_tile_of_slot.restype = ctypes.c_int
+        te = ctypes.POINTER(TuneEntry)
+        lib.gemm_f16_autotune_candidates.argtypes = [i32, i64, i64, i64, i32, i32, i64, te, i32,
+                                                     ctypes.POINTER(i32), ctypes.POINTER(i64)]
+        lib.gemm_f16_autotune_candidates.restype = ctypes.c_int
+        lib.gemm_f16_autotune.argtypes = [i32, i64, i64, i64, p, p, p, p, i64, i32, p, te, te,
+                                          i32, ctypes.POINTER(i32)]
+        lib.gemm_f16_autotune.restype = ctypes.c_int
         _lib = lib
         return lib
 
@@ -211,7 +231,61 @@ def gemm_f16_nt_tile_of_slot(plan: Plan, slot: int) -> tuple[int, int]:
     return tm.value, tn.value
 
 
+def gemm_f16_autotune_candidates(layout: int, M: int, N: int, K: int, num_cus: int,
+                                 aligned: bool = True,
+                                 workspace_bytes: int = 0) -> tuple[list[TuneEntry], int]:
+    """(candidates gemm_f16_autotune would time, workspace bytes the largest split needs)."""
+    lib, n, need = load(), ctypes.c_int32(), ctypes.c_int64()
+    _check(lib.gemm_f16_autotune_candidates(layout, M, N, K, num_cus, int(aligned),
+                                            workspace_bytes, None, 0, ctypes.byref(n),
+                                            ctypes.byref(need)), "gemm_f16_autotune_candidates")
+    buf = (TuneEntry * max(n.value, 1))()
+    _check(lib.gemm_f16_autotune_candidates(layout, M, N, K, num_cus, int(aligned),
+                                            workspace_bytes, buf, n.value, ctypes.byref(n),
+                                            ctypes.byref(need)), "gemm_f16_autotune_candidates")
+    return list(buf[:n.value]), need.value
+
+
+def gemm_f16_autotune(layout: int, M: int, N: int, K: int, A: int, B: int, C: int,
+                      workspace: int, workspace_bytes: int, iters: int,
+                      stream: int = 0, max_entries: int = 1024) -> tuple[TuneEntry, list[TuneEntry]]:
+    """(fastest candidate, every timed candidate) from gemm_f16_autotune."""
+    best, n = TuneEntry(), ctypes.c_int32()
+    buf = (TuneEntry * max_entries)()
+    _check(load().gemm_f16_autotune(layout, M, N, K, A, B, C, workspace, workspace_bytes, iters,
+                                    stream, ctypes.byref(best), buf, max_entries,
+                                    ctypes.byref(n)), "gemm_f16_autotune")
+    return best, list(buf[:min(n.value, max_entries)])
+
+
 # ---- torch convenience -------------------------------------------------------
+def _operands(a, b, layout: str, out):
+    """Check fp16 operands stored as `layout` says; return (M, N, K, out)."""
+    import torch
+
+    if layout not in LAYOUT_CODES:
+        raise ValueError(f"unknown layout {layout!r}")
+    if a.dtype != torch.float16 or b.dtype != torch.float16:
+        raise TypeError("a and b must be torch.float16")
+    if a.dim() != 2 or b.dim() != 2:
+        raise ValueError("a and b must be matrices")
+    m, k = (a.shape[1], a.shape[0]) if layout[0] == "t" else (a.shape[0], a.shape[1])
+    kb, n = (b.shape[0], b.shape[1]) if layout[1] == "n" else (b.shape[1], b.shape[0])
+    if k != kb:
+        raise ValueError(f"shape mismatch for {layout}: a{tuple(a.shape)} b{tuple(b.shape)}")
+    if not (a.is_cuda and b.is_cuda) or a.device != b.device:
+        raise ValueError("a and b must be on the same GPU")
+    if not (a.is_contiguous() and b.is_contiguous()):
+        raise ValueError("a and b must be contiguous (row-major)")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float16, device=a.device)
+    elif (out.dtype != torch.float16 or tuple(out.shape) != (m, n) or not out.is_contiguous()
+          or out.device != a.device):
+        raise ValueError("out must be a contiguous float16 [M, N] tensor on a's device")
+    return m, n, k, out
+
+
+
 def gemm_nt(a, b, out=None, config: int | None = None, swizzle: int = 0, grid: int = 0,
             stream=None, epilogue: int = -1):
     """C = a @ b.T for fp16 CUDA(HIP) tensors a [M,K] and b [N,K].
@@ -255,25 +329,7 @@ def gemm_splitk(a, b, layout: str = "nt", splits: int = 0, out=None, workspace=N
     planned bytes) is given."""
     import torch
 
-    if layout not in ("nt", "nn", "tn", "tt"):
-        raise ValueError(f"unknown layout {layout!r}")
-    if a.dtype != torch.float16 or b.dtype != torch.float16:
-        raise TypeError("a and b must be torch.float16")
-    if a.dim() != 2 or b.dim() != 2:
-        raise ValueError("a and b must be matrices")
-    m, k = (a.shape[1], a.shape[0]) if layout[0] == "t" else (a.shape[0], a.shape[1])
-    kb, n = (b.shape[0], b.shape[1]) if layout[1] == "n" else (b.shape[1], b.shape[0])
-    if k != kb:
-        raise ValueError(f"shape mismatch for {layout}: a{tuple(a.shape)} b{tuple(b.shape)}")
-    if not (a.is_cuda and b.is_cuda) or a.device != b.device:
-        raise ValueError("a and b must be on the same GPU")
-    if not (a.is_contiguous() and b.is_contiguous()):
-        raise ValueError("a and b must be contiguous (row-major)")
-    if out is None:
-        out = torch.empty((m, n), dtype=torch.float16, device=a.device)
-    elif (out.dtype != torch.float16 or tuple(out.shape) != (m, n) or not out.is_contiguous()
-          or out.device != a.device):
-        raise ValueError("out must be a contiguous float16 [M, N] tensor on a's device")
+    m, n, k, out = _operands(a, b, layout, out)
     cus = torch.cuda.get_device_properties(a.device).multi_processor_count
     _, _, need = globals()[f"gemm_f16_{layout}_splitk_plan"](m, n, k, cus, splits)
     if workspace is None:
@@ -307,25 +363,7 @@ def gemm(a, b, layout: str = "nt", out=None, config: int | None = None, swizzle:
     if layout == "nt":
         return gemm_nt(a, b, out=out, config=config, swizzle=swizzle, grid=grid, stream=stream,
                        epilogue=epilogue)
-    if layout not in ("nn", "tn", "tt"):
-        raise ValueError(f"unknown layout {layout!r}")
-    if a.dtype != torch.float16 or b.dtype != torch.float16:
-        raise TypeError("a and b must be torch.float16")
-    if a.dim() != 2 or b.dim() != 2:
-        raise ValueError("a and b must be matrices")
-    m, k = (a.shape[1], a.shape[0]) if layout[0] == "t" else (a.shape[0], a.shape[1])
-    kb, n = (b.shape[0], b.shape[1]) if layout[1] == "n" else (b.shape[1], b.shape[0])
-    if k != kb:
-        raise ValueError(f"shape mismatch for {layout}: a{tuple(a.shape)} b{tuple(b.shape)}")
-    if not (a.is_cuda and b.is_cuda) or a.device != b.device:
-        raise ValueError("a and b must be on the same GPU")
-    if not (a.is_contiguous() and b.is_contiguous()):
-        raise ValueError("a and b must be contiguous (row-major)")
-    if out is None:
-        out = torch.empty((m, n), dtype=torch.float16, device=a.device)
-    elif (out.dtype != torch.float16 or tuple(out.shape) != (m, n) or not out.is_contiguous()
-          or out.device != a.device):
-        raise ValueError("out must be a contiguous float16 [M, N] tensor on a's device")
+    m, n, k, out = _operands(a, b, layout, out)
     s = stream if stream is not None else torch.cuda.current_stream(a.device)
     fn = globals()[f"gemm_f16_{layout}_with_config"]
     with torch.cuda.device(a.device):
@@ -337,3 +375,51 @@ def gemm(a, b, layout: str = "nt", out=None, config: int | None = None, swizzle:
 def gemm_nn(a, b, **kw):
     """C = a @ b for a [M,K], b [K,N] (gemm_f16_nn)."""
     return gemm(a, b, "nn", **kw)
+
+
+class Tuned:
+    """Result of autotune(): the fastest (config, splits), its time, every
+    timed candidate, and the output tensor (which holds the fastest's C)."""
+
+    def __init__(self, layout: str, best: TuneEntry, entries: list[TuneEntry], out):
+        self.layout = layout
+        self.config = best.config_id
+        self.splits = best.splits
+        self.ms = best.ms
+        self.entries = [e.as_dict() for e in entries]
+        self.out = out
+
+    def __call__(self, a, b, out=None, workspace=None, stream=None):
+        """Run the tuned choice (gemm_f16_<layout>_splitk_with_config)."""
+        return gemm_splitk(a, b, self.layout, splits=self.splits, out=out, workspace=workspace,
+                           config=None if self.config < 0 else self.config, stream=stream)
+
+    def __repr__(self) -> str:
+        return (f"Tuned(layout={self.layout!r}, config={self.config}, splits={self.splits}, "
+                f"ms={self.ms:.4f}, candidates={len(self.entries)})")
+
+
+def autotune(a, b, layout: str = "nt", iters: int = 10, out=None, workspace=None, stream=None):
+    """Time every configuration of `layout` (and its split counts where the
+    grid is under-filled) on these operands with gemm_f16_autotune; blocks
+    until done.  The workspace the split candidates need (at most about 1 GiB)
+    is allocated with torch unless `workspace` is given; candidates that do
+    not fit it are not tried."""
+    import torch
+
+    m, n, k, out = _operands(a, b, layout, out)
+    code = LAYOUT_CODES[layout]
+    cus = torch.cuda.get_device_properties(a.device).multi_processor_count
+    aligned = a.data_ptr() % 16 == 0 and b.data_ptr() % 16 == 0
+    _, need = gemm_f16_autotune_candidates(code, m, n, k, cus, aligned, 0)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=a.device)
+    elif not workspace.is_cuda or workspace.device != a.device:
+        raise ValueError("workspace must be a tensor on a's device")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    s = stream if stream is not None else torch.cuda.current_stream(a.device)
+    with torch.cuda.device(a.device):
+        best, entries = gemm_f16_autotune(code, m, n, k, a.data_ptr(), b.data_ptr(),
+                                          out.data_ptr(), workspace.data_ptr(), ws_bytes, iters,
+                                          s.cuda_stream)
+    return Tuned(layout, best, entries, out)

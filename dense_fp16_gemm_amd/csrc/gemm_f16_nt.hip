@@ -61,6 +61,7 @@
 
 #include <mutex>
 #include <type_traits>
+#include <vector>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -1672,6 +1673,125 @@ static int run_splitk(int32_t layout, int64_t M, int64_t N, int64_t K, const voi
     return err == hipSuccess ? GEMM_F16_OK : GEMM_F16_LAUNCH_FAILED;
 }
 
+// ---------------------------------------------------------------------------
+// Autotuning: every configuration of a layout, with and without a split over K
+// ---------------------------------------------------------------------------
+// Requested split counts tried per configuration; each maps to an effective
+// count (ranges of whole K slices) and repeated effective counts are dropped.
+constexpr int32_t kTuneSplits[] = {2, 3, 4, 6, 8, 12, 16, 24, 32, 48, 64};
+constexpr int64_t kTuneMinSplitK = 256;   // K per range the tuner goes down to
+
+// The (configuration, split) pairs the tuner times for these arguments, in
+// configuration order, each configuration's unsplit run first.  Splits are
+// tried only while the unsplit grid would fill fewer than 4 rounds, up to 16
+// rounds of units, and only where their partials fit `workspace_bytes`
+// (*needed: the largest workspace any split candidate would use).  `fast`:
+// the arguments suit the layout's direct-to-LDS configurations; otherwise
+// only its general kernel is a candidate.
+static void tune_candidates(int32_t layout, int64_t M, int64_t N, int64_t K, int32_t cus,
+                            bool fast, int64_t workspace_bytes,
+                            std::vector<gemm_f16_tune_entry_t> &out, int64_t *needed)
+{
+    out.clear();
+    *needed = 0;
+    const int64_t stride_bytes = split_stride(M, N) * 4;
+    for (int id = 0; id < kNumKernels; ++id) {
+        const KernelEntry &e = kKernels[id];
+        if (e.layout != layout || (!fast && !e.general)) continue;
+        out.push_back(gemm_f16_tune_entry_t{id, 1, GEMM_F16_OK, -1.0f});
+        if (e.general || !e.fn_split || K <= 0) continue;
+        const int64_t tiles = cdiv(M, e.block_m) * cdiv(N, e.block_n);
+        if (tiles >= 4 * int64_t(cus)) continue;
+        int64_t last = 1;
+        for (int32_t sp : kTuneSplits) {
+            if (cdiv(K, sp) < kTuneMinSplitK) break;
+            const int64_t eff = cdiv(K, split_k_len(id, K, sp));
+            if (eff <= last) continue;
+            last = eff;
+            if (tiles * eff > 16 * int64_t(cus) || tiles * eff > INT32_MAX) break;
+            const int64_t bytes = eff * stride_bytes;
+            if (bytes > *needed) *needed = bytes;
+            if (bytes <= workspace_bytes)
+                out.push_back(gemm_f16_tune_entry_t{id, static_cast<int32_t>(eff), GEMM_F16_OK, -1.0f});
+        }
+    }
+}
+
+static bool fast_arguments(int32_t layout, int64_t M, int64_t N, int64_t K, const void *A,
+                           const void *B, bool check_pointers)
+{
+    return layout == 0 ? !needs_general(K, A, B, check_pointers)
+                       : layout_supported(layout, M, N, K, A, B, check_pointers);
+}
+
+// Times each candidate on the caller's buffers: one untimed call, then
+// `iters` back-to-back calls between two events on `stream`.  Candidates that
+// report GEMM_F16_UNSUPPORTED are recorded and skipped; any other failure
+// ends the search with that status.  The fastest is run once more at the end
+// so that C holds its result.
+static int autotune(int32_t layout, int64_t M, int64_t N, int64_t K, const void *A,
+                    const void *B, void *C, void *workspace, int64_t workspace_bytes,
+                    int32_t iters, hipStream_t stream, gemm_f16_tune_entry_t *best,
+                    gemm_f16_tune_entry_t *entries, int32_t max_entries, int32_t *n_entries)
+{
+    if (layout < 0 || layout > 3 || !best || iters < 1 || iters > 10000 || max_entries < 0 ||
+        (max_entries > 0 && !entries) || workspace_bytes < 0 || (workspace_bytes > 0 && !workspace))
+        return GEMM_F16_INVALID_ARG;
+    const int v = validate(M, N, K, A, B, C);
+    if (v != GEMM_F16_OK) return v;
+    *best = gemm_f16_tune_entry_t{-1, 1, GEMM_F16_OK, 0.0f};
+    if (n_entries) *n_entries = 0;
+    if (M == 0 || N == 0) return GEMM_F16_OK;
+    if (K == 0) return run(M, N, 0, A, B, C, stream, -1, 0, 0, -1);   // nothing to choose
+    int32_t cus = 0;
+    const int s = current_cus(&cus);
+    if (s != GEMM_F16_OK) return s;
+    std::vector<gemm_f16_tune_entry_t> cand;
+    int64_t needed = 0;
+    tune_candidates(layout, M, N, K, cus, fast_arguments(layout, M, N, K, A, B, true),
+                    workspace_bytes, cand, &needed);
+    hipEvent_t ev[2] = {nullptr, nullptr};
+    if (hipEventCreate(&ev[0]) != hipSuccess || hipEventCreate(&ev[1]) != hipSuccess) {
+        if (ev[0]) (void)hipEventDestroy(ev[0]);
+        return GEMM_F16_LAUNCH_FAILED;
+    }
+    int status = GEMM_F16_OK;
+    int best_i = -1;
+    for (size_t i = 0; i < cand.size() && status == GEMM_F16_OK; ++i) {
+        gemm_f16_tune_entry_t &c = cand[i];
+        auto call = [&] {
+            return run_splitk(layout, M, N, K, A, B, C, c.splits, workspace, workspace_bytes,
+                              stream, c.config_id);
+        };
+        c.status = call();
+        if (c.status == GEMM_F16_OK && hipEventRecord(ev[0], stream) != hipSuccess)
+            c.status = GEMM_F16_LAUNCH_FAILED;
+        for (int32_t it = 0; it < iters && c.status == GEMM_F16_OK; ++it) c.status = call();
+        if (c.status == GEMM_F16_OK) {
+            float ms = 0.0f;
+            if (hipEventRecord(ev[1], stream) != hipSuccess || hipEventSynchronize(ev[1]) != hipSuccess ||
+                hipEventElapsedTime(&ms, ev[0], ev[1]) != hipSuccess)
+                c.status = GEMM_F16_LAUNCH_FAILED;
+            c.ms = ms / iters;
+        }
+        if (c.status == GEMM_F16_OK) {
+            if (best_i < 0 || c.ms < cand[best_i].ms) best_i = static_cast<int>(i);
+        } else if (c.status != GEMM_F16_UNSUPPORTED) {
+            status = c.status;
+        }
+    }
+    (void)hipEventDestroy(ev[0]);
+    (void)hipEventDestroy(ev[1]);
+    const size_t n = cand.size() < size_t(max_entries) ? cand.size() : size_t(max_entries);
+    for (size_t i = 0; i < n; ++i) entries[i] = cand[i];
+    if (n_entries) *n_entries = static_cast<int32_t>(cand.size());
+    if (status != GEMM_F16_OK) return status;
+    if (best_i < 0) return GEMM_F16_UNSUPPORTED;
+    *best = cand[best_i];
+    return run_splitk(layout, M, N, K, A, B, C, best->splits, workspace, workspace_bytes, stream,
+                      best->config_id);
+}
+
 }  // namespace gemm_f16
 
 using namespace gemm_f16;
@@ -1929,4 +2049,38 @@ extern "C" int gemm_f16_nt_tile_of_slot(const gemm_f16_nt_plan_t *plan, int64_t 
     *tile_m = tm;
     *tile_n = tn;
     return GEMM_F16_OK;
+}
+
+extern "C" int gemm_f16_autotune_candidates(int32_t layout, int64_t M, int64_t N, int64_t K,
+                                            int32_t num_cus, int32_t aligned,
+                                            int64_t workspace_bytes,
+                                            gemm_f16_tune_entry_t *entries, int32_t max_entries,
+                                            int32_t *n_entries, int64_t *workspace_needed)
+{
+    if (layout < 0 || layout > 3 || M < 0 || N < 0 || K < 0 || num_cus <= 0 ||
+        workspace_bytes < 0 || max_entries < 0 || (max_entries > 0 && !entries) || !n_entries ||
+        !workspace_needed)
+        return GEMM_F16_INVALID_ARG;
+    if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX || cdiv(M, 64) * cdiv(N, 64) > INT32_MAX)
+        return GEMM_F16_UNSUPPORTED;
+    *n_entries = 0;
+    *workspace_needed = 0;
+    if (M == 0 || N == 0 || K == 0) return GEMM_F16_OK;
+    std::vector<gemm_f16_tune_entry_t> cand;
+    const bool fast = fast_arguments(layout, M, N, K, nullptr, nullptr, false) && aligned;
+    tune_candidates(layout, M, N, K, num_cus, fast, workspace_bytes, cand, workspace_needed);
+    const size_t n = cand.size() < size_t(max_entries) ? cand.size() : size_t(max_entries);
+    for (size_t i = 0; i < n; ++i) entries[i] = cand[i];
+    *n_entries = static_cast<int32_t>(cand.size());
+    return GEMM_F16_OK;
+}
+
+extern "C" int gemm_f16_autotune(int32_t layout, int64_t M, int64_t N, int64_t K, const void *A,
+                                 const void *B, void *C, void *workspace,
+                                 int64_t workspace_bytes, int32_t iters, hipStream_t stream,
+                                 gemm_f16_tune_entry_t *best, gemm_f16_tune_entry_t *entries,
+                                 int32_t max_entries, int32_t *n_entries)
+{
+    return autotune(layout, M, N, K, A, B, C, workspace, workspace_bytes, iters, stream, best,
+                    entries, max_entries, n_entries);
 }

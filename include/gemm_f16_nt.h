@@ -293,6 +293,77 @@ int gemm_f16_tt_splitk_with_config(int64_t M, int64_t N, int64_t K,
                                    int32_t config_id);
 
 /*
+ * Autotuning (the pages pick each kernel version's tile sizes, stage count
+ * and K depth by timing a search space of compile-time configurations:
+ * Tilus tutorial "Hopper matmul", page "2. Multi-Stage Software Pipelining",
+ * Multi-Stage Shared Memory and the results; page "3. Warp Specialization",
+ * the results; page "6. Register Reallocation, Multicast, and a Persistent
+ * Kernel", the closing caution on other shapes).  Here the search space
+ * is the library's compiled configurations of one operand layout, each run
+ * unsplit and, where the unsplit grid leaves the GPU under-filled, with K
+ * split several ways.
+ *
+ * `layout` = 2 * (A stored [K, M]) + (B stored [K, N]): 0 NT (gemm_f16_nt),
+ * 1 NN (gemm_f16_nn), 2 TT (gemm_f16_tt), 3 TN (gemm_f16_tn).
+ *
+ * One candidate: a configuration id and an effective split count (1 = no
+ * split).  Replaying it is gemm_f16_<layout>_splitk_with_config(M, N, K, A,
+ * B, C, splits, workspace, workspace_bytes, stream, config_id), whose result
+ * for one split equals that of gemm_f16_<layout>_with_config.
+ */
+typedef struct gemm_f16_tune_entry_t {
+    int32_t config_id;
+    int32_t splits;     /* effective split count, 1 = no split */
+    int32_t status;     /* status of the candidate's calls (gemm_f16_autotune) */
+    float ms;           /* average time per call in ms, -1 when not timed */
+} gemm_f16_tune_entry_t;
+
+/*
+ * gemm_f16_autotune_candidates: pure host function.  Lists the candidates
+ * gemm_f16_autotune would time for (M, N, K) on `num_cus` compute units, in
+ * the order it times them: every configuration of `layout` that can take the
+ * arguments (only the layout's general kernel when they do not suit the
+ * direct-to-LDS configurations; `aligned` != 0 says A and B are 16-byte
+ * aligned), each unsplit and then with each distinct effective split count
+ * (K per range at least 256) while the unsplit tiles fill fewer than 4 rounds
+ * of the grid, up to 16 rounds of work units, whose fp32 partials fit in
+ * `workspace_bytes`.  Writes the first min(count, max_entries) candidates to
+ * `entries` (status 0, ms -1), the count to *n_entries, and to
+ * *workspace_needed the workspace bytes that the largest split candidate
+ * needs regardless of `workspace_bytes` (0 without split candidates).
+ * M, N or K = 0: no candidates.  GEMM_F16_INVALID_ARG for a layout outside
+ * 0..3, negative sizes or workspace_bytes, num_cus <= 0, max_entries < 0,
+ * entries NULL with max_entries > 0, or NULL n_entries or workspace_needed.
+ *
+ * gemm_f16_autotune: times every candidate above on the caller's buffers and
+ * the current device, on `stream`: one untimed call, then `iters` calls
+ * between two HIP events; `ms` is the event time over `iters`.  It blocks
+ * until each candidate's events have completed (so it is not for graph
+ * capture).  `workspace` (caller-owned device memory, 16-byte aligned, not
+ * overlapping A, B or C; NULL when workspace_bytes = 0) bounds the split
+ * candidates as above.  Candidates that a layout's kernels reject record
+ * GEMM_F16_UNSUPPORTED and are skipped; any other failure stops the search
+ * and is returned.  On success *best is the fastest candidate and C holds its
+ * result (it is run once more last; C's contents are otherwise those of the
+ * last call).  `entries` receives up to max_entries timed candidates in
+ * order, *n_entries (may be NULL) their count.  M or N = 0: no call, *best =
+ * {-1, 1, 0, 0}; K = 0: C is filled with +0 and *best = {-1, 1, 0, 0}.
+ * GEMM_F16_INVALID_ARG for a layout outside 0..3, iters outside 1..10000,
+ * NULL best, entries NULL with max_entries > 0, or the arguments
+ * gemm_f16_<layout> rejects; the library allocates no device memory.
+ */
+int gemm_f16_autotune_candidates(int32_t layout, int64_t M, int64_t N, int64_t K,
+                                 int32_t num_cus, int32_t aligned, int64_t workspace_bytes,
+                                 gemm_f16_tune_entry_t *entries, int32_t max_entries,
+                                 int32_t *n_entries, int64_t *workspace_needed);
+int gemm_f16_autotune(int32_t layout, int64_t M, int64_t N, int64_t K,
+                      const void *A, const void *B, void *C,
+                      void *workspace, int64_t workspace_bytes, int32_t iters,
+                      hipStream_t stream, gemm_f16_tune_entry_t *best,
+                      gemm_f16_tune_entry_t *entries, int32_t max_entries,
+                      int32_t *n_entries);
+
+/*
  * The tile order the kernel walks (Tilus tutorial "Hopper matmul", page
  * "4. Pipeline Abstraction and Two Consumer Warp Groups", Tile
  * Rasterization; page "6. ...", Persistent Tile Loop), exposed so that host

@@ -29,12 +29,13 @@ def g():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(gemm_f16_nt\w*)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(gemm_f16_\w+)\s*\(", text)))
 
 
 def test_header_symbols_exported(g):
     names = declared_functions()
     assert "gemm_f16_nt" in names and "gemm_f16_nt_status_string" in names
+    assert {"gemm_f16_nn", "gemm_f16_tn_splitk", "gemm_f16_autotune"} <= set(names)
     lib = ctypes.CDLL(g.library_path())
     for name in names:
         assert hasattr(lib, name), f"{name} declared but not exported"
