@@ -4,11 +4,14 @@ One step = one GEMM over the workload's inputs (the whole hot path: one
 kernel launch through the C ABI).  Inputs are seeded synthetic fp16 matrices
 (workloads.py), resident in HBM before the timed region starts.
 
-Protocol (after the pages' benchmark: CUDA-event timing of 30 launches after a
-3-second cooldown; page 6, Performance and the Warning after it): W warm-up
-launches, a cooldown, then exactly K launches between two events on the
-launch stream, each launch also bracketed by its own event pair for the
-per-launch kernel duration used in the roofline.
+Protocol (after the pages' benchmark: event timing of back-to-back launches
+after a 3-second cooldown; page 6, Performance and the Warning after it): one
+launch, the cooldown, W untimed warm-up launches, then exactly K launches
+between two events on the launch stream, nothing else enqueued between them.
+The GPU's clock ramps up over the first ~50 ms of sustained work after idle,
+so by default W is sized from one launch's time to fill --warmup-ms (250 ms);
+an explicit --warmup is taken as given.  The per-launch time used in the
+roofline is the window over K.
 
 Prints ONE JSON line.  Fields beyond the common contract:
   roofline      the GEMM kernel against the MI355X dense fp16 MFMA peak
@@ -96,18 +99,21 @@ def copy_probe(args) -> int:
     src = torch.empty(n, dtype=torch.float16, device="cuda:0").fill_(1.0)
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
-    for _ in range(args.warmup + args.steps):
+    launches = (args.warmup or 0) + args.steps
+    for _ in range(launches):
         dst.copy_(src)
     torch.cuda.synchronize()
-    print(json.dumps({"copy_bytes": 2 * n, "launches": args.warmup + args.steps}), flush=True)
+    print(json.dumps({"copy_bytes": 2 * n, "launches": launches}), flush=True)
     return 0
 
 
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warm-up launches (default: enough to fill --warmup-ms)")
+    ap.add_argument("--warmup-ms", type=float, default=250.0)
     ap.add_argument("--cooldown", type=float, default=3.0)
     ap.add_argument("--workload", default=None, help="workload name (default: the 8192^3 one)")
     ap.add_argument("--config", type=int, default=None, help="force a kernel configuration")
@@ -236,26 +242,32 @@ def main() -> int:
     torch.cuda.synchronize()
     if args.cooldown > 0:
         time.sleep(args.cooldown)
-    for _ in range(args.warmup):
+    win0 = torch.cuda.Event(enable_timing=True)
+    win1 = torch.cuda.Event(enable_timing=True)
+    warmup = args.warmup
+    if warmup is None:
+        # one (cold) launch sizes the warm-up; it is a warm-up launch itself
+        win0.record(stream)
+        launch()
+        win1.record(stream)
+        torch.cuda.synchronize()
+        cold_ms = max(win0.elapsed_time(win1), 1e-3)
+        warmup = 1 + min(max(int(args.warmup_ms / cold_ms), 20), 20000)
+        todo = warmup - 1
+    else:
+        todo = warmup
+    for _ in range(todo):
         launch()
     torch.cuda.synchronize()
 
-    # timed region: exactly `steps` launches
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    win0 = torch.cuda.Event(enable_timing=True)
-    win1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
+    # timed region: exactly `steps` launches, back to back
     win0.record(stream)
-    for i in range(args.steps):
-        starts[i].record(stream)
+    for _ in range(args.steps):
         launch()
-        ends[i].record(stream)
     win1.record(stream)
     torch.cuda.synchronize()
     ms_per_step = win0.elapsed_time(win1) / args.steps
-    kernel_ms = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
-    kernel_avg_ms = sum(kernel_ms) / len(kernel_ms)
+    kernel_avg_ms = ms_per_step
 
     tflops = w.flops / (ms_per_step * 1e-3) / 1e12
     compute_bound = w.flops / w.algorithmic_bytes > (PEAK_FP16_TFLOPS * 1e12) / (PEAK_HBM_GBS * 1e9)
@@ -279,7 +291,7 @@ def main() -> int:
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": warmup,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -294,8 +306,6 @@ def main() -> int:
                    "seed": w.seed, "accumulate": "f32", "plan": plan,
                    "autotune": tune,
                    "kernel_ms_avg": round(kernel_avg_ms, 5),
-                   "kernel_ms_min": round(kernel_ms[0], 5),
-                   "kernel_ms_max": round(kernel_ms[-1], 5),
                    "source_digest": source_digest()},
         "roofline": roofline,
         "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_seconds),
