@@ -1058,28 +1058,51 @@ __device__ __forceinline__ half8_t load_chunk(const uint16_t *base, int32_t rows
     return v;
 }
 
-// An 8-k chunk of one row of an operand stored with k outermost ([K, M] or
-// [K, N], row pitch ld): element e is base[(k + e) ld + row], zero past the
-// valid rows or K.  Lanes take consecutive rows, so each of the 8 two-byte
-// loads of a wave reads one contiguous run.
-__device__ __forceinline__ half8_t load_chunk_kn(const uint16_t *base, int32_t rows_valid, int row,
-                                                 int64_t ld, int64_t K, int64_t k)
+// Eight consecutive rows at one k of an operand stored with k outermost
+// ([K, M] or [K, N], row pitch ld; base is the tile's first row): one 16-byte
+// run of the stored row at any 2-byte alignment, element by element for the
+// run that crosses the valid rows, zeros past them or past K.
+__device__ __forceinline__ half8_t load_run_kn(const uint16_t *base, int32_t rows_valid, int row0,
+                                               int64_t ld, int64_t K, int64_t k)
 {
     half8_t v = {};
-    if (row < rows_valid) {
-        const _Float16 *src = reinterpret_cast<const _Float16 *>(base) + row;
+    if (k < K && row0 < rows_valid) {
+        const _Float16 *src = reinterpret_cast<const _Float16 *>(base) + k * ld + row0;
+        if (row0 + 8 <= rows_valid) {
+            __builtin_memcpy(&v, src, 16);
+        } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            if (k + e < K) v[e] = src[(k + e) * ld];
+            for (int e = 0; e < 8; ++e)
+                if (row0 + e < rows_valid) v[e] = src[e];
+        }
     }
     return v;
 }
 
+// Position of run c of a k-outermost operand's slice (rows x BK): runs come
+// in groups of 64, 8 row-runs by 8 k, so one wave's loads cover 8 k of 128
+// contiguous bytes each.
+template <class CF, int ROWS>
+__device__ __forceinline__ void run_pos_kn(int c, int &row0, int &kl)
+{
+    constexpr int XG = ROWS / 64;   // groups of 8 runs along the rows
+    static_assert(ROWS % 64 == 0 && CF::BK % 8 == 0, "whole 8 x 8 groups of runs");
+    const int g = c / 64, l = c % 64;
+    row0 = ((g % XG) * 8 + l % 8) * 8;
+    kl = (g / XG) * 8 + l / 8;
+}
+
 // LA, LB: A stored [K, M] / B stored [K, N] (see Cfg's AL and BL); the LDS
 // tiles keep the [rows][K] layout either way, so only the loads differ.
+// Three workgroups per CU for NT; two when an operand is stored k-outermost,
+// whose chunks take eight 2-byte loads with their own addresses (at three,
+// the register budget would spill them).
+template <int LA, int LB>
+constexpr int any_kernel_per_cu() { return LA || LB ? 2 : 3; }
+
 template <class CF, int LA, int LB>
 __global__ __launch_bounds__(CF::THREADS)
-__attribute__((amdgpu_waves_per_eu(3)))
+__attribute__((amdgpu_waves_per_eu(any_kernel_per_cu<LA, LB>())))
 void gemm_f16_nt_any_kernel(Params p)
 {
     static_assert(CF::MI == 32 && CF::STAGES == 2, "general path: 32x32x16 MFMAs, 2 buffers");
@@ -1110,42 +1133,64 @@ void gemm_f16_nt_any_kernel(Params p)
         const uint16_t *a0 = p.A + (LA ? static_cast<int64_t>(t.m0) : static_cast<int64_t>(t.m0) * K);
         const uint16_t *b0 = p.B + (LB ? static_cast<int64_t>(t.n0) : static_cast<int64_t>(t.n0) * K);
         // chunk c of a slice: K-contiguous operands walk a row's chunks with
-        // consecutive threads, k-outermost ones walk rows (coalesced loads)
-        auto row_of = [](int c, int rows, bool kn) { return kn ? c % rows : c / CF::CHUNKS; };
-        auto kchunk_of = [](int c, int rows, bool kn) { return kn ? c / rows : c % CF::CHUNKS; };
-        auto load = [&](int kt) {
+        // consecutive threads; k-outermost ones load 8-row runs along their
+        // stored rows (run_pos_kn), both coalesced
+        // one operand's runs of slice kt into registers
+        auto load_op = [&](half8_t *r, int n_ch, const uint16_t *base, int32_t rows_valid,
+                           auto rows_c, auto kn_c, int64_t ld, int kt) {
+            constexpr int ROWS = decltype(rows_c)::value;
+            constexpr bool KN = decltype(kn_c)::value;
 #pragma unroll
-            for (int q = 0; q < A_CH; ++q) {
+            for (int q = 0; q < n_ch; ++q) {
                 const int c = q * CF::THREADS + tid;
-                const int row = row_of(c, CF::BM, LA);
-                const int64_t k = static_cast<int64_t>(kt) * CF::BK + kchunk_of(c, CF::BM, LA) * 8;
-                ra[q] = LA ? load_chunk_kn(a0, rows_a, row, p.M, K, k)
-                           : load_chunk<CF>(a0, rows_a, row, K, k);
-            }
-#pragma unroll
-            for (int q = 0; q < B_CH; ++q) {
-                const int c = q * CF::THREADS + tid;
-                const int row = row_of(c, CF::BN, LB);
-                const int64_t k = static_cast<int64_t>(kt) * CF::BK + kchunk_of(c, CF::BN, LB) * 8;
-                rb[q] = LB ? load_chunk_kn(b0, rows_b, row, p.N, K, k)
-                           : load_chunk<CF>(b0, rows_b, row, K, k);
+                if constexpr (KN) {
+                    int row0, kl;
+                    run_pos_kn<CF, ROWS>(c, row0, kl);
+                    r[q] = load_run_kn(base, rows_valid, row0, ld, K,
+                                       static_cast<int64_t>(kt) * CF::BK + kl);
+                } else {
+                    r[q] = load_chunk<CF>(base, rows_valid, c / CF::CHUNKS, K,
+                                          static_cast<int64_t>(kt) * CF::BK + (c % CF::CHUNKS) * 8);
+                }
             }
         };
+        // ... and from registers into a stage's [rows][K] swizzled tile: a
+        // K-contiguous chunk is one 16-byte write, a k-outermost run eight
+        // 2-byte writes down its rows
+        auto store_op = [&](const half8_t *r, int n_ch, uint8_t *tile, auto rows_c, auto kn_c) {
+            constexpr int ROWS = decltype(rows_c)::value;
+            constexpr bool KN = decltype(kn_c)::value;
+#pragma unroll
+            for (int q = 0; q < n_ch; ++q) {
+                const int c = q * CF::THREADS + tid;
+                if constexpr (KN) {
+                    int row0, kl;
+                    run_pos_kn<CF, ROWS>(c, row0, kl);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int row = row0 + e;
+                        const int phys = (kl / 8) ^ chunk_swizzle<CF::CHUNKS, CF::MI>(row);
+                        *reinterpret_cast<_Float16 *>(tile + row * CF::ROW_BYTES + phys * 16 +
+                                                      (kl % 8) * 2) = r[q][e];
+                    }
+                } else {
+                    const int row = c / CF::CHUNKS;
+                    const int phys = (c % CF::CHUNKS) ^ chunk_swizzle<CF::CHUNKS, CF::MI>(row);
+                    *reinterpret_cast<half8_t *>(tile + row * CF::ROW_BYTES + phys * 16) = r[q];
+                }
+            }
+        };
+        using BMc = std::integral_constant<int, CF::BM>;
+        using BNc = std::integral_constant<int, CF::BN>;
+        using LAc = std::integral_constant<bool, LA != 0>;
+        using LBc = std::integral_constant<bool, LB != 0>;
+        auto load = [&](int kt) {
+            load_op(ra, A_CH, a0, rows_a, BMc{}, LAc{}, p.M, kt);
+            load_op(rb, B_CH, b0, rows_b, BNc{}, LBc{}, p.N, kt);
+        };
         auto store = [&](int stage) {
-#pragma unroll
-            for (int q = 0; q < A_CH; ++q) {
-                const int c = q * CF::THREADS + tid, row = row_of(c, CF::BM, LA);
-                const int phys = kchunk_of(c, CF::BM, LA) ^ chunk_swizzle<CF::CHUNKS, CF::MI>(row);
-                *reinterpret_cast<half8_t *>(smem + stage * CF::STAGE_BYTES + row * CF::ROW_BYTES +
-                                             phys * 16) = ra[q];
-            }
-#pragma unroll
-            for (int q = 0; q < B_CH; ++q) {
-                const int c = q * CF::THREADS + tid, row = row_of(c, CF::BN, LB);
-                const int phys = kchunk_of(c, CF::BN, LB) ^ chunk_swizzle<CF::CHUNKS, CF::MI>(row);
-                *reinterpret_cast<half8_t *>(smem + stage * CF::STAGE_BYTES + CF::A_BYTES +
-                                             row * CF::ROW_BYTES + phys * 16) = rb[q];
-            }
+            store_op(ra, A_CH, smem + stage * CF::STAGE_BYTES, BMc{}, LAc{});
+            store_op(rb, B_CH, smem + stage * CF::STAGE_BYTES + CF::A_BYTES, BNc{}, LBc{});
         };
 
         typename CF::Acc acc[CF::FM][CF::FN];
@@ -1220,7 +1265,8 @@ KernelEntry entry_general(int swizzle)
 {
     return KernelEntry{reinterpret_cast<const void *>(&gemm_f16_nt_any_kernel<CF, LA, LB>),
                        nullptr, CF::BM, CF::BN, CF::BK, CF::WAVES, CF::STAGES, CF::LDS_BYTES,
-                       CF::THREADS, swizzle, 0.0f, 0, 1, 3, 2 * LA + LB};
+                       CF::THREADS, swizzle, 0.0f, 0, 1, any_kernel_per_cu<LA, LB>(),
+                       2 * LA + LB};
 }
 
 static const KernelEntry kKernels[] = {
@@ -1275,13 +1321,19 @@ static const KernelEntry kKernels[] = {
     entry<Cfg<256, 256, 64, 2, 2, 2, 16, 0, 16, 0, 1, 1>>(8, 1.06f),   // 33
     entry<Cfg<256, 128, 64, 2, 2, 2, 16, 0, 12, 1, 1, 1>>(8, 0.85f),   // 34
     entry<Cfg<128, 128, 64, 2, 2, 2, 16, 0, 8, 1, 1, 1>>(8, 0.75f),    // 35
-    // 36-38: the general kernel for NN, TT and TN (loads along the operand's
+    // 36-37: TT with a 64-wide B side (B [N, K] takes any multiple of 32
+    // rows; A [K, M] needs 128): 4 waves of 64x32, twice the tiles of 32 for
+    // a small M.  36 keeps 6 stages with the refill spread over each slice,
+    // as 29 does for NN; 37 is the two-stage early-refill scheme.
+    entry<Cfg<128, 64, 64, 2, 2, 6, 16, 0, 0, 0, 0, 1>>(8, 0.66f),     // 36
+    entry<Cfg<128, 64, 64, 2, 2, 2, 16, 0, 6, 1, 0, 1>>(8, 0.00f),     // 37
+    // 38-40: the general kernel for NN, TT and TN (loads along the operand's
     // contiguous dimension), for arguments the direct-to-LDS kernels of those
     // layouts cannot take
     entry_general<Cfg<128, 128, 32, 2, 2, 2>, 0, 1>(8),
     entry_general<Cfg<128, 128, 32, 2, 2, 2>, 1, 0>(8),
     entry_general<Cfg<128, 128, 32, 2, 2, 2>, 1, 1>(8),
-    // 39: the general kernel, 4 waves of 64x64, two register-staged buffers of
+    // 41: the general kernel, 4 waves of 64x64, two register-staged buffers of
     // K 32; planned only when the direct-to-LDS path cannot run
     entry_general<Cfg<128, 128, 32, 2, 2, 2>>(8),
 };
