@@ -139,8 +139,16 @@ __host__ __device__ constexpr int chunk_swizzle(int r)
 // those 16 rows over 8 distinct 32-byte windows (two rows per window, the
 // minimum for 512 bytes):
 //   chunk ^ 2 ((k & 3) | ((k >> 3) & 1) << 2)
+// Rows of 128 bytes (a 64-wide tile) alternate between the two halves of the
+// 256-byte bank window, so only the four even (odd) rows of each half-wave's
+// eight need distinct 32-byte windows within their half, from k's bits 1 and
+// 3 (for the second read, 4 rows on, as well):
+//   chunk ^ 2 (((k >> 1) & 1) | ((k >> 3) & 1) << 1)
+template <int ROW_BYTES>
 __host__ __device__ constexpr int kn_swizzle(int k)
 {
+    static_assert(ROW_BYTES == 128 || ROW_BYTES == 256 || ROW_BYTES == 512, "[K, X] tile rows");
+    if (ROW_BYTES == 128) return 2 * (((k >> 1) & 1) | (((k >> 3) & 1) << 1));
     return 2 * ((k & 3) | (((k >> 3) & 1) << 2));
 }
 
@@ -218,10 +226,10 @@ struct Cfg {
     static_assert((AL ? BK % (A_DMA_ROWS * WAVES) : BM % (DMA_ROWS * WAVES)) == 0 &&
                       (BL ? BK % (B_DMA_ROWS * WAVES) : BN % (DMA_ROWS * WAVES)) == 0,
                   "every wave issues the same number of DMA instructions");
-    static_assert(BL == 0 || (MI == 16 && (BN == 128 || BN == 256) && BK % 32 == 0),
-                  "[K, N] B: 16x16x32 fragments, 256- or 512-byte rows");
-    static_assert(AL == 0 || (MI == 16 && (BM == 128 || BM == 256) && BK % 32 == 0),
-                  "[K, M] A: 16x16x32 fragments, 256- or 512-byte rows");
+    static_assert(BL == 0 || (MI == 16 && (BN == 64 || BN == 128 || BN == 256) && BK % 32 == 0),
+                  "[K, N] B: 16x16x32 fragments, 128-, 256- or 512-byte rows");
+    static_assert(AL == 0 || (MI == 16 && (BM == 64 || BM == 128 || BM == 256) && BK % 32 == 0),
+                  "[K, M] A: 16x16x32 fragments, 128-, 256- or 512-byte rows");
     static_assert(STAGES >= 2, "need at least a double buffer");
     static_assert(LDS_BYTES <= LDS_LIMIT, "LDS ring exceeds 160 KB");
     static_assert((STAGES - 1) * LOADS <= 63, "vmcnt counts at most 63 loads");
@@ -343,6 +351,16 @@ __device__ __forceinline__ Tile make_tile(const Params &p, int32_t slot, uint32_
     return t;
 }
 
+// kn_swizzle of the A (IS_A) or B tile when that operand is stored k-outermost
+template <class CF, bool IS_A>
+__device__ __forceinline__ int kn_swizzle_of(int r)
+{
+    if constexpr (IS_A ? CF::AL == 1 : CF::BL == 1)
+        return kn_swizzle<IS_A ? CF::A_ROW_BYTES : CF::B_ROW_BYTES>(r);
+    else
+        return 0;
+}
+
 // One of this wave's DMA instructions for K-slice `kt` of tile `t`, into ring
 // stage `stage`.  Instruction i fills rows R = (i' * WAVES + wave) * DMA_ROWS
 // .. R + DMA_ROWS - 1 of the A tile (i < A_LOADS, i' = i) or of the B tile
@@ -363,7 +381,8 @@ __device__ __forceinline__ void dma_one(const Params &p, const Tile &t, int stag
         const int chunks = is_a ? CF::A_CHUNKS : CF::B_CHUNKS;
         const int32_t x0 = is_a ? t.m0 : t.n0, xn = is_a ? p.M : p.N;
         const int r = rblk * dma_rows + lane / chunks;
-        const int chunk = (lane % chunks) ^ kn_swizzle(r);
+        const int chunk = (lane % chunks) ^ (is_a ? kn_swizzle_of<CF, true>(r)
+                                                  : kn_swizzle_of<CF, false>(r));
         const uint32_t ld = static_cast<uint32_t>(xn) * 2u;
         uint32_t v = (k0 + r) * ld + chunk * 16;
         if (k0 + r >= static_cast<uint32_t>(t.klen) || x0 + chunk * 8 >= xn) v = OOB_OFFSET;
@@ -406,7 +425,7 @@ __device__ __forceinline__ uint32_t dma_lane_offset_kn(int ip, int wave, int lan
     constexpr int DMA_ROWS_X = IS_A ? CF::A_DMA_ROWS : CF::B_DMA_ROWS;
     constexpr int CHUNKS_X = IS_A ? CF::A_CHUNKS : CF::B_CHUNKS;
     const int r = (ip * CF::WAVES + wave) * DMA_ROWS_X + lane / CHUNKS_X;
-    const int chunk = (lane % CHUNKS_X) ^ kn_swizzle(r);
+    const int chunk = (lane % CHUNKS_X) ^ kn_swizzle<CHUNKS_X * 16>(r);
     if (x0 + chunk * 8 >= xn) return OOB_OFFSET;
     return static_cast<uint32_t>(r) * static_cast<uint32_t>(xn) * 2u + chunk * 16;
 }
@@ -700,17 +719,24 @@ struct WaveCtx {
         b_frag_base = CF::A_BYTES + wave_n * CF::TN * CF::ROW_BYTES;
         btr0 = 0;
         atr0 = 0;
+        // the fragment XOR 32 j (j < TN / 16) touches chunk bits below
+        // log2(TN / 8); the wave's offset, a multiple of TN / 8 chunks, lies
+        // above them when TN is a power of two
         if constexpr (CF::BL == 1) {
-            static_assert(CF::TN % 128 == 0 || CF::TN == 64, "wave column offset clear of the XOR bits");
+            static_assert(CF::TN >= 32 && (CF::TN & (CF::TN - 1)) == 0,
+                          "wave column offset clear of the XOR bits");
             const int r = 8 * (lane / 16) + (lane % 16) / 4;
             const int n = wave_n * CF::TN + 4 * (lane % 4);
-            btr0 = r * CF::B_ROW_BYTES + (((n / 8) ^ kn_swizzle(r)) * 16) + (n % 8) * 2;
+            btr0 = r * CF::B_ROW_BYTES + (((n / 8) ^ kn_swizzle<CF::B_ROW_BYTES>(r)) * 16) +
+                   (n % 8) * 2;
         }
         if constexpr (CF::AL == 1) {
-            static_assert(CF::TM % 128 == 0 || CF::TM == 64, "wave row offset clear of the XOR bits");
+            static_assert(CF::TM >= 32 && (CF::TM & (CF::TM - 1)) == 0,
+                          "wave row offset clear of the XOR bits");
             const int r = 8 * (lane / 16) + (lane % 16) / 4;
             const int m = wave_m * CF::TM + 4 * (lane % 4);
-            atr0 = r * CF::A_ROW_BYTES + (((m / 8) ^ kn_swizzle(r)) * 16) + (m % 8) * 2;
+            atr0 = r * CF::A_ROW_BYTES + (((m / 8) ^ kn_swizzle<CF::A_ROW_BYTES>(r)) * 16) +
+                   (m % 8) * 2;
         }
     }
 };
@@ -1327,13 +1353,21 @@ static const KernelEntry kKernels[] = {
     // as 29 does for NN; 37 is the two-stage early-refill scheme.
     entry<Cfg<128, 64, 64, 2, 2, 6, 16, 0, 0, 0, 0, 1>>(8, 0.66f),     // 36
     entry<Cfg<128, 64, 64, 2, 2, 2, 16, 0, 6, 1, 0, 1>>(8, 0.00f),     // 37
-    // 38-40: the general kernel for NN, TT and TN (loads along the operand's
+    // 38-41: 64-wide tiles on a k-outermost side (128-byte LDS rows), 6
+    // stages with the refill spread over each slice, for a small M or N:
+    // 38 NN 128x64 (B [K, N]), 39 TT 64x128 (A [K, M]), 40 TN 64x128, 41 TN
+    // 128x64
+    entry<Cfg<128, 64, 64, 2, 2, 6, 16, 0, 0, 0, 1, 0>>(8, 0.66f),     // 38
+    entry<Cfg<64, 128, 64, 2, 2, 6, 16, 0, 0, 0, 0, 1>>(8, 0.66f),     // 39
+    entry<Cfg<64, 128, 64, 2, 2, 6, 16, 0, 0, 0, 1, 1>>(8, 0.66f),     // 40
+    entry<Cfg<128, 64, 64, 2, 2, 6, 16, 0, 0, 0, 1, 1>>(8, 0.66f),     // 41
+    // 42-44: the general kernel for NN, TT and TN (loads along the operand's
     // contiguous dimension), for arguments the direct-to-LDS kernels of those
     // layouts cannot take
     entry_general<Cfg<128, 128, 32, 2, 2, 2>, 0, 1>(8),
     entry_general<Cfg<128, 128, 32, 2, 2, 2>, 1, 0>(8),
     entry_general<Cfg<128, 128, 32, 2, 2, 2>, 1, 1>(8),
-    // 41: the general kernel, 4 waves of 64x64, two register-staged buffers of
+    // 45: the general kernel, 4 waves of 64x64, two register-staged buffers of
     // K 32; planned only when the direct-to-LDS path cannot run
     entry_general<Cfg<128, 128, 32, 2, 2, 2>>(8),
 };
@@ -1420,7 +1454,10 @@ static void make_plan(int id, int64_t M, int64_t N, int32_t num_cus, int32_t swi
 
 // Cost model: rounds of the persistent grid times the time one tile takes,
 // which scales with its area over the configuration's relative MFMA rate.
-// Entries with rel_rate 0 are compiled for sweeps but never planned.
+// Entries with rel_rate 0 are compiled for sweeps but never planned.  Between
+// tiles of equal cost, one whose long side lies along the longer of M and N
+// is preferred (1%): its strip of the larger operand, the one streamed from
+// HBM, then fills most of each LDS stage.
 static int choose_config(int64_t M, int64_t N, int32_t num_cus, int32_t layout = 0)
 {
     int best = -1;
@@ -1430,7 +1467,9 @@ static int choose_config(int64_t M, int64_t N, int32_t num_cus, int32_t layout =
         if (e.rel_rate <= 0.0f || e.layout != layout) continue;
         const int64_t tiles = cdiv(M, e.block_m) * cdiv(N, e.block_n);
         const int64_t rounds = cdiv(tiles, num_cus > 0 ? num_cus : 1);
-        const double cost = static_cast<double>(rounds) * e.block_m * e.block_n / e.rel_rate;
+        const bool along = (N > M && e.block_n > e.block_m) || (M > N && e.block_m > e.block_n);
+        const double cost = static_cast<double>(rounds) * e.block_m * e.block_n / e.rel_rate *
+                            (along ? 0.99 : 1.0);
         if (best < 0 || cost < best_cost) {
             best = id;
             best_cost = cost;
