@@ -423,3 +423,37 @@ def autotune(a, b, layout: str = "nt", iters: int = 10, out=None, workspace=None
                                           out.data_ptr(), workspace.data_ptr(), ws_bytes, iters,
                                           s.cuda_stream)
     return Tuned(layout, best, entries, out)
+
+
+def matmul_layout(a, b):
+    """How matmul() runs a @ b: (layout, A as stored, B as stored).
+
+    Each operand must be row-major or the transposed view of a row-major
+    matrix: a [M,K] row-major is A stored [M,K] ('n'); a.t() of a row-major
+    [K,M] is A stored [K,M] ('t'); b [K,N] row-major is B stored [K,N] ('n');
+    b.t() of a row-major [N,K] is B stored [N,K] ('t').  Pure function of the
+    shapes and strides."""
+    if a.dim() != 2 or b.dim() != 2:
+        raise ValueError("a and b must be matrices")
+
+    def stored(x):
+        if x.is_contiguous():
+            return "n", x
+        if x.t().is_contiguous():
+            return "t", x.t()
+        raise ValueError("each operand must be row-major or a transposed view of a "
+                         f"row-major matrix (strides {tuple(x.stride())})")
+
+    la, xa = stored(a)
+    lb, xb = stored(b)
+    return la + lb, xa, xb
+
+
+def matmul(a, b, out=None, stream=None):
+    """C = a @ b for fp16 GPU matrices a [M,K] and b [K,N], each row-major or
+    a transposed view of a row-major matrix (see matmul_layout): the storage
+    picks gemm_f16_nn, gemm_f16_nt, gemm_f16_tn or gemm_f16_tt, with no copy."""
+    lay, xa, xb = matmul_layout(a, b)
+    if a.shape[1] != b.shape[0]:
+        raise ValueError(f"shape mismatch: a{tuple(a.shape)} b{tuple(b.shape)}")
+    return gemm(xa, xb, lay, out=out, stream=stream)

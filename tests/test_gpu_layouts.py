@@ -192,3 +192,19 @@ def test_layout_full_size_equals_nt(g, lay, name):
     got = g.gemm(a, b, lay)
     torch.cuda.synchronize()
     assert torch.equal(got.view(torch.int16), nt.view(torch.int16)), f"{lay} {name}"
+
+
+@pytest.mark.parametrize("ta,tb", [(False, False), (False, True), (True, False), (True, True)])
+def test_matmul_picks_the_layout_from_strides(g, oracle_mod, ta, tb):
+    """matmul(a, b) on row-major operands and transposed views: bit-exact on
+    integer inputs, in every layout."""
+    import torch
+
+    m, n, k = 200, 304, 520
+    a_mk, b_nk = workloads.make_inputs(m, n, k, "int2", 1.0, seed=361)
+    ga = torch.from_numpy(a_mk.T.copy()).cuda().t() if ta else torch.from_numpy(a_mk).cuda()
+    gb = torch.from_numpy(b_nk.copy()).cuda().t() if tb else torch.from_numpy(b_nk.T.copy()).cuda()
+    _say(f"  gpu matmul ta={ta} tb={tb}")
+    c = g.matmul(ga, gb)
+    torch.cuda.synchronize()
+    assert_bit_exact(c.cpu().numpy(), oracle_mod.gemm(a_mk, b_nk), f"matmul ta={ta} tb={tb}")
