@@ -1,0 +1,62 @@
+"""Seeded random shapes in every layout, through the planner's entry points
+(plain and split over K), on integer inputs: every partial sum is exact in
+fp32, so each result must equal the oracle bit for bit, whichever
+configuration, split count and tail handling the planner picks.  The output
+is NaN-poisoned first, so an element left unwritten fails too."""
+import sys
+
+import numpy as np
+import pytest
+
+import workloads
+from parity import assert_bit_exact
+
+pytestmark = pytest.mark.gpu
+
+LAYOUTS = ["nt", "nn", "tn", "tt"]
+
+
+def _shapes(seed, count):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(count):
+        m, n, k = (int(x) for x in rng.integers(1, 700, 3))
+        if i % 4 == 1:   # larger outputs: the 128- and 256-wide tiles
+            m, n = 3 * m, 3 * n
+        if i % 2 == 0:   # half with every dimension a multiple of 8: the fast kernels
+            m, n, k = (max(8, x // 8 * 8) for x in (m, n, k))
+        out.append((m, n, 8 * k if i % 3 == 0 else k))   # some long K for the splits
+    return out
+
+
+@pytest.fixture(scope="module")
+def g():
+    import torch
+
+    import dense_fp16_gemm_amd as lib
+
+    lib.load()
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return lib
+
+
+@pytest.mark.parametrize("lay", LAYOUTS)
+@pytest.mark.parametrize("split", [False, True])
+def test_random_shapes_bit_exact(g, oracle_mod, lay, split):
+    import torch
+
+    for idx, (m, n, k) in enumerate(_shapes(410 + LAYOUTS.index(lay), 16)):
+        a_mk, b_nk = workloads.make_inputs(m, n, k, "int2", 1.0, seed=420 + idx)
+        a = np.ascontiguousarray(a_mk.T) if lay[0] == "t" else a_mk
+        b = np.ascontiguousarray(b_nk.T) if lay[1] == "n" else b_nk
+        print(f"  gpu random {lay} split={split} {m}x{n}x{k}", file=sys.stderr, flush=True)
+        ta, tb = torch.from_numpy(a).cuda(), torch.from_numpy(b).cuda()
+        out = torch.full((m, n), float("nan"), dtype=torch.float16, device="cuda")
+        if split:
+            g.gemm_splitk(ta, tb, lay, out=out)
+        else:
+            g.gemm(ta, tb, lay, out=out)
+        torch.cuda.synchronize()
+        assert_bit_exact(out.cpu().numpy(), oracle_mod.gemm(a_mk, b_nk),
+                         f"{lay} split={split} {m}x{n}x{k}")
