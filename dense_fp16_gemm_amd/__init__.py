@@ -119,6 +119,8 @@ def load():
         lib.gemm_f16_autotune.argtypes = [i32, i64, i64, i64, p, p, p, p, i64, i32, p, te, te,
                                           i32, ctypes.POINTER(i32)]
         lib.gemm_f16_autotune.restype = ctypes.c_int
+        lib.gemm_f16_splitk_workspace_bytes.argtypes = [i64, i64, i32, ctypes.POINTER(i64)]
+        lib.gemm_f16_splitk_workspace_bytes.restype = ctypes.c_int
         _lib = lib
         return lib
 
@@ -211,6 +213,14 @@ gemm_f16_nt_splitk_plan, gemm_f16_nt_splitk, gemm_f16_nt_splitk_with_config = _s
 gemm_f16_nn_splitk_plan, gemm_f16_nn_splitk, gemm_f16_nn_splitk_with_config = _splitk_fns("nn")
 gemm_f16_tn_splitk_plan, gemm_f16_tn_splitk, gemm_f16_tn_splitk_with_config = _splitk_fns("tn")
 gemm_f16_tt_splitk_plan, gemm_f16_tt_splitk, gemm_f16_tt_splitk_with_config = _splitk_fns("tt")
+
+
+def gemm_f16_splitk_workspace_bytes(M: int, N: int, splits: int) -> int:
+    """Workspace bytes any configuration needs for at most `splits` ranges."""
+    out = ctypes.c_int64()
+    _check(load().gemm_f16_splitk_workspace_bytes(M, N, splits, ctypes.byref(out)),
+           "gemm_f16_splitk_workspace_bytes")
+    return out.value
 
 
 def gemm_f16_nt_num_configs() -> int:
@@ -332,6 +342,9 @@ def gemm_splitk(a, b, layout: str = "nt", splits: int = 0, out=None, workspace=N
     m, n, k, out = _operands(a, b, layout, out)
     cus = torch.cuda.get_device_properties(a.device).multi_processor_count
     _, _, need = globals()[f"gemm_f16_{layout}_splitk_plan"](m, n, k, cus, splits)
+    if config is not None and splits > 1:
+        # a forced configuration may split into more ranges than the planner's
+        need = max(need, gemm_f16_splitk_workspace_bytes(m, n, splits))
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=a.device)
     elif not workspace.is_cuda or workspace.device != a.device:

@@ -2026,6 +2026,16 @@ static int splitk_plan(int32_t layout, int64_t M, int64_t N, int64_t K, int32_t 
     return GEMM_F16_OK;
 }
 
+extern "C" int gemm_f16_splitk_workspace_bytes(int64_t M, int64_t N, int32_t splits,
+                                               int64_t *workspace_bytes)
+{
+    if (!workspace_bytes || M < 0 || N < 0 || splits < 0 || splits > kMaxSplits)
+        return GEMM_F16_INVALID_ARG;
+    if (M > INT32_MAX || N > INT32_MAX) return GEMM_F16_UNSUPPORTED;
+    *workspace_bytes = splits > 1 ? int64_t(splits) * split_stride(M, N) * 4 : 0;
+    return GEMM_F16_OK;
+}
+
 extern "C" int gemm_f16_nt_splitk_plan(int64_t M, int64_t N, int64_t K, int32_t num_cus,
                                        int32_t splits, gemm_f16_nt_plan_t *plan,
                                        int32_t *splits_out, int64_t *workspace_bytes)

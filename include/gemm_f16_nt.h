@@ -233,8 +233,20 @@ int gemm_f16_tt_plan(int64_t M, int64_t N, int64_t K, int32_t num_cus,
  * GEMM_F16_INVALID_ARG for splits > 64.
  *
  * gemm_f16_nt_splitk_with_config: the same with the kernel configuration
- * fixed (config_id < 0: the planner's choice), for tests and sweeps.
+ * fixed (config_id < 0: the planner's choice), for tests and sweeps.  Its
+ * effective split count follows the forced configuration's K slice, so the
+ * workspace the plan above reports may not suffice for it;
+ * gemm_f16_splitk_workspace_bytes gives a size that does.
+ *
+ * gemm_f16_splitk_workspace_bytes: pure host function.  The workspace bytes
+ * that any configuration of any layout needs for at most `splits` ranges of
+ * an M x N output: splits slices of M N fp32 partials, each rounded up to 64
+ * elements (0 for splits <= 1).  GEMM_F16_INVALID_ARG for NULL output,
+ * negative sizes or splits outside 0..64; GEMM_F16_UNSUPPORTED for M or N
+ * above 2^31 - 1.
  */
+int gemm_f16_splitk_workspace_bytes(int64_t M, int64_t N, int32_t splits,
+                                    int64_t *workspace_bytes);
 int gemm_f16_nt_splitk_plan(int64_t M, int64_t N, int64_t K, int32_t num_cus,
                             int32_t splits, gemm_f16_nt_plan_t *plan,
                             int32_t *splits_out, int64_t *workspace_bytes);

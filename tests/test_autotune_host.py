@@ -160,3 +160,22 @@ def test_autotune_rejects_bad_arguments_without_a_device():
     # a workspace size without a workspace
     assert lib.gemm_f16_autotune(0, 64, 64, 64, A, B, C, None, 1024, 10, None,
                                  ctypes.byref(best), None, 0, ctypes.byref(n)) == g.INVALID_ARG
+
+
+def test_splitk_workspace_bytes_bounds_every_configuration():
+    """The bound covers the effective split count of every configuration of
+    every layout (each splits K into ranges of its own K slice)."""
+    for (m, n, k) in ((1024, 1024, 65536), (300, 200, 1000), (64, 64, 1048576), (8, 8, 520)):
+        for splits in (2, 3, 5, 7, 16, 64):
+            bound = g.gemm_f16_splitk_workspace_bytes(m, n, splits)
+            assert bound == splits * cdiv(m * n, 64) * 64 * 4
+            for c in configs():
+                if c.block_k == 32:
+                    continue
+                ks = cdiv(cdiv(k, splits), c.block_k) * c.block_k
+                assert cdiv(k, ks) * cdiv(m * n, 64) * 64 * 4 <= bound
+    assert g.gemm_f16_splitk_workspace_bytes(100, 100, 1) == 0
+    assert g.gemm_f16_splitk_workspace_bytes(100, 100, 0) == 0
+    for bad in ((-1, 4, 2), (4, 4, 65), (4, 4, -1)):
+        with pytest.raises(g.GemmError):
+            g.gemm_f16_splitk_workspace_bytes(*bad)

@@ -211,3 +211,21 @@ def test_splitk_layouts_integer_bit_exact(g, oracle_mod, lay):
     c = g.gemm_splitk(torch.from_numpy(a).cuda(), torch.from_numpy(b).cuda(), lay, splits=6)
     torch.cuda.synchronize()
     assert_bit_exact(c.cpu().numpy(), oracle_mod.gemm(a_mk, b_nk), f"int2 splitk {lay}")
+
+
+def test_splitk_forced_config_default_workspace(g, oracle_mod):
+    """A forced configuration whose K slice differs from the planner's splits
+    into more ranges than the planner's plan (here 6 against 5): the torch
+    wrapper's default workspace must still cover it."""
+    import torch
+
+    m, n, k = 64, 64, 1040
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    plan, eff, _ = g.gemm_f16_nt_splitk_plan(m, n, k, cus, 8)
+    assert plan.block_k == 128 and eff == 5, "the case needs a K-128 plan"
+    a, b = workloads.make_inputs(m, n, k, "int2", 1.0, seed=351)
+    _say(f"  gpu splitk forced config 11 {m}x{n}x{k} splits=8")
+    c = g.gemm_nt_splitk(torch.from_numpy(a).cuda(), torch.from_numpy(b).cuda(), splits=8,
+                         config=11)
+    torch.cuda.synchronize()
+    assert_bit_exact(c.cpu().numpy(), oracle_mod.gemm(a, b), "forced config 11, 8 splits")
