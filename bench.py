@@ -11,7 +11,11 @@ between two events on the launch stream, nothing else enqueued between them.
 The GPU's clock ramps up over the first ~50 ms of sustained work after idle,
 so by default W is sized from one launch's time to fill --warmup-ms (250 ms);
 an explicit --warmup is taken as given.  The per-launch time used in the
-roofline is the window over K.
+roofline is the window over K.  As the pages report the median of three fresh
+processes, the whole protocol runs in --repeat (3) fresh processes, one after
+another; this process only starts them (it touches no GPU) and prints the
+line of the median one, with every process's value, and times the CPU
+baseline itself.
 
 Prints ONE JSON line.  Fields beyond the common contract:
   roofline      the GEMM kernel against the MI355X dense fp16 MFMA peak
@@ -107,6 +111,40 @@ def copy_probe(args) -> int:
     return 0
 
 
+def run_repeats(args) -> int:
+    """The protocol in args.repeat fresh processes, one after another; prints
+    the median process's line (the middle value; the upper middle for an even
+    count) with every value, and the CPU baseline timed here."""
+    import subprocess
+
+    import workloads
+
+    cmd = [sys.executable, os.path.abspath(__file__)] + sys.argv[1:] + [
+        "--repeat", "1", "--child", "--no-cpu-baseline"]
+    lines = []
+    for r in range(args.repeat):
+        res = subprocess.run(cmd, stdout=subprocess.PIPE, text=True)
+        if res.returncode != 0:
+            sys.stdout.write(res.stdout)
+            return res.returncode
+        found = [ln for ln in res.stdout.splitlines() if ln.startswith('{"metric"')]
+        if not found:
+            print("bench.py: a measuring process printed no result line", file=sys.stderr)
+            return 1
+        lines.append(json.loads(found[-1]))
+        print(f"bench.py: process {r + 1}/{args.repeat}: {lines[-1]['value']} "
+              f"{lines[-1]['unit']}", file=sys.stderr, flush=True)
+    values = [d["value"] for d in lines]
+    out = sorted(lines, key=lambda d: d["value"])[len(lines) // 2]
+    out["repeat"] = {"processes": len(lines), "values": values, "median": out["value"],
+                     "min": min(values), "max": max(values)}
+    name = args.workload or workloads.HEADLINE
+    out["cpu_baseline"] = (None if args.no_cpu_baseline else
+                           cpu_baseline(workloads.ALL_WORKLOADS[name], args.cpu_seconds))
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -136,6 +174,10 @@ def main() -> int:
                     help="timed calls per autotuning candidate")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--repeat", type=int, default=3,
+                    help="fresh processes, one after another, each running the whole "
+                         "protocol; the line is the median one's (1: measure in this process)")
+    ap.add_argument("--child", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead of the GEMM, run a plain device copy of this many bytes "
                          "(calibrates the HBM byte counters)")
@@ -146,6 +188,8 @@ def main() -> int:
               "the GEMM shards into independent output tiles, see the design notes.",
               file=sys.stderr)
         return 2
+    if args.repeat > 1 and not args.child and args.copy_bytes <= 0:
+        return run_repeats(args)
 
     import numpy as np
     import torch
