@@ -97,6 +97,14 @@ def draw(rng: np.random.Generator, shape, dist: str, scale: float) -> np.ndarray
     return x.astype(np.float16)
 
 
+def int2_matrix(shape, seed: int) -> np.ndarray:
+    """Integers in {-2..2} as fp16, drawn through int8: for matrices of more
+    than 2^31 bytes, where draw()'s fp64 intermediate would take 4x the
+    memory.  Its own stream (not draw(..., "int2"))."""
+    rng = np.random.default_rng(seed)
+    return rng.integers(-2, 3, size=shape, dtype=np.int8).astype(np.float16)
+
+
 def make_inputs(M: int, N: int, K: int, dist: str = "uniform", scale: float = 1.0,
                 seed: int = 0):
     """A [M, K] and B [N, K] as fp16 numpy arrays; A is drawn before B."""
