@@ -612,11 +612,12 @@ __device__ __forceinline__ void store_tile_f32(const Params &p, const Tile &t,
 }
 
 // Epilogue staged through LDS (the stage the next tile's prefill leaves
-// free).  Block row i of every wave -- WM * MI tile rows -- is written to LDS
-// as fp16, rows padded by 16 bytes so that the 32 rows one write instruction
-// touches fall in distinct banks; after a barrier every thread stores 16-byte
-// row segments, a wave covering 512 consecutive columns.  Masked at M and N.
-// A barrier ends each block row before the buffer is reused.
+// free).  Block rows of every wave -- WM * MI tile rows each -- are written to
+// LDS as fp16, as many as the stage holds per round, rows padded by 16 bytes
+// so that the 32 rows one write instruction touches fall in distinct banks;
+// after a barrier every thread stores 16-byte row segments, a wave covering
+// 512 consecutive columns.  Masked at M and N.  A barrier ends each round
+// before the buffer is reused.
 template <class CF>
 __device__ __forceinline__ void store_tile_staged(const Params &p, const Tile &t,
                                                   typename CF::Acc (&acc)[CF::FM][CF::FN],
@@ -624,54 +625,72 @@ __device__ __forceinline__ void store_tile_staged(const Params &p, const Tile &t
 {
     constexpr int PITCH = CF::BN * 2 + 16;     // bytes per staged row
     constexpr int CROWS = CF::WM * CF::MI;     // tile rows per block row
+    constexpr int BROW = CROWS * PITCH;        // bytes per staged block row
     static_assert(CF::STAGED_OK, "staged block row fits one stage");
+    // block rows per round: as many as one stage holds
+    constexpr int R = CF::STAGE_BYTES / BROW < CF::FM ? CF::STAGE_BYTES / BROW : CF::FM;
+    static_assert(R >= 1, "one block row per round at least");
     uint8_t *buf = smem + (CF::STAGES - 1) * CF::STAGE_BYTES;
     const int lrow = lane % CF::MI;
     const int lq = lane / CF::MI;
     const int tid = threadIdx.x;
+    constexpr int SEGS = CF::BN / 8;           // 8-column segments per row
 #pragma unroll
-    for (int i = 0; i < CF::FM; ++i) {
-        const int srow = wave_m * CF::MI + lrow;   // staged row of this lane
+    for (int i0 = 0; i0 < CF::FM; i0 += R) {
+        const int nr = CF::FM - i0 < R ? CF::FM - i0 : R;   // block rows this round
 #pragma unroll
-        for (int j = 0; j < CF::FN; ++j) {
-            acc_fence<CF>(acc[i][j]);
+        for (int r = 0; r < R; ++r) {
+            if (r < nr) {
+                const int i = i0 + r;
+                const int srow = wave_m * CF::MI + lrow;   // staged row of this lane
 #pragma unroll
-            for (int g = 0; g < CF::ACC_N / 4; ++g) {
-                const int ncol = wave_n * CF::TN + j * CF::MI + (CF::MI == 32 ? g * 8 + lq * 4 : lq * 4);
-                f32x4_t v;
-                v.x = acc[i][j][4 * g + 0];
-                v.y = acc[i][j][4 * g + 1];
-                v.z = acc[i][j][4 * g + 2];
-                v.w = acc[i][j][4 * g + 3];
-                *reinterpret_cast<half4_t *>(buf + srow * PITCH + ncol * 2) =
-                    __builtin_convertvector(v, half4_t);
+                for (int j = 0; j < CF::FN; ++j) {
+                    acc_fence<CF>(acc[i][j]);
+#pragma unroll
+                    for (int g = 0; g < CF::ACC_N / 4; ++g) {
+                        const int ncol = wave_n * CF::TN + j * CF::MI +
+                                         (CF::MI == 32 ? g * 8 + lq * 4 : lq * 4);
+                        f32x4_t v;
+                        v.x = acc[i][j][4 * g + 0];
+                        v.y = acc[i][j][4 * g + 1];
+                        v.z = acc[i][j][4 * g + 2];
+                        v.w = acc[i][j][4 * g + 3];
+                        *reinterpret_cast<half4_t *>(buf + r * BROW + srow * PITCH + ncol * 2) =
+                            __builtin_convertvector(v, half4_t);
+                    }
+                }
             }
         }
         lds_barrier();
         // 16 bytes per lane at any 2-byte alignment: memcpy lets the compiler
         // emit one 16-byte store, which the target's unaligned-access mode
         // allows; only the segment crossing N is stored element by element.
-        constexpr int SEGS = CF::BN / 8;           // 8-column segments per row
-        constexpr int ITEMS = CROWS * SEGS;
+        // one block row's items at a time (a scheduling barrier between
+        // them keeps only those in registers)
+        constexpr int ITEMS_R = CROWS * SEGS;   // items per block row
 #pragma unroll
-        for (int it = 0; it < (ITEMS + CF::THREADS - 1) / CF::THREADS; ++it) {
-            const int c = it * CF::THREADS + tid;
-            if (c < ITEMS) {
-                const int sr = c / SEGS, sc = c % SEGS;
-                const int32_t m = t.m0 + (sr / CF::MI) * CF::TM + i * CF::MI + sr % CF::MI;
+        for (int r = 0; r < R; ++r) {
+            if (r >= nr) break;
+#pragma unroll
+            for (int it = 0; it < (ITEMS_R + CF::THREADS - 1) / CF::THREADS; ++it) {
+                const int cr = it * CF::THREADS + tid;
+                if (cr >= ITEMS_R) continue;
+                const int sr = cr / SEGS, sc = cr % SEGS;
+                const int32_t m = t.m0 + (sr / CF::MI) * CF::TM + (i0 + r) * CF::MI + sr % CF::MI;
                 const int32_t n = t.n0 + sc * 8;
-                if (m < p.M && n < p.N) {
-                    const half8_t h = *reinterpret_cast<const half8_t *>(buf + sr * PITCH + sc * 16);
-                    _Float16 *dst = reinterpret_cast<_Float16 *>(p.C) + static_cast<int64_t>(m) * p.N + n;
-                    if (n + 8 <= p.N) {
-                        __builtin_memcpy(dst, &h, 16);
-                    } else {
+                if (m >= p.M || n >= p.N) continue;
+                const half8_t h =
+                    *reinterpret_cast<const half8_t *>(buf + r * BROW + sr * PITCH + sc * 16);
+                _Float16 *dst = reinterpret_cast<_Float16 *>(p.C) + static_cast<int64_t>(m) * p.N + n;
+                if (n + 8 <= p.N) {
+                    __builtin_memcpy(dst, &h, 16);
+                } else {
 #pragma unroll
-                        for (int e = 0; e < 8; ++e)
-                            if (n + e < p.N) dst[e] = h[e];
-                    }
+                    for (int e = 0; e < 8; ++e)
+                        if (n + e < p.N) dst[e] = h[e];
                 }
             }
+            __builtin_amdgcn_sched_barrier(0);
         }
         lds_barrier();
     }
