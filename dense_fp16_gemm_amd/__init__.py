@@ -121,6 +121,8 @@ def load():
         lib.gemm_f16_autotune.restype = ctypes.c_int
         lib.gemm_f16_splitk_workspace_bytes.argtypes = [i64, i64, i32, ctypes.POINTER(i64)]
         lib.gemm_f16_splitk_workspace_bytes.restype = ctypes.c_int
+        lib.gemm_f16_device_cus.argtypes = [ctypes.POINTER(i32)]
+        lib.gemm_f16_device_cus.restype = ctypes.c_int
         _lib = lib
         return lib
 
@@ -213,6 +215,13 @@ gemm_f16_nt_splitk_plan, gemm_f16_nt_splitk, gemm_f16_nt_splitk_with_config = _s
 gemm_f16_nn_splitk_plan, gemm_f16_nn_splitk, gemm_f16_nn_splitk_with_config = _splitk_fns("nn")
 gemm_f16_tn_splitk_plan, gemm_f16_tn_splitk, gemm_f16_tn_splitk_with_config = _splitk_fns("tn")
 gemm_f16_tt_splitk_plan, gemm_f16_tt_splitk, gemm_f16_tt_splitk_with_config = _splitk_fns("tt")
+
+
+def gemm_f16_device_cus() -> int:
+    """The current device's compute-unit count, from the library's cache."""
+    out = ctypes.c_int32()
+    _check(load().gemm_f16_device_cus(ctypes.byref(out)), "gemm_f16_device_cus")
+    return out.value
 
 
 def gemm_f16_splitk_workspace_bytes(M: int, N: int, splits: int) -> int:
@@ -340,7 +349,8 @@ def gemm_splitk(a, b, layout: str = "nt", splits: int = 0, out=None, workspace=N
     import torch
 
     m, n, k, out = _operands(a, b, layout, out)
-    cus = torch.cuda.get_device_properties(a.device).multi_processor_count
+    with torch.cuda.device(a.device):
+        cus = gemm_f16_device_cus()
     _, _, need = globals()[f"gemm_f16_{layout}_splitk_plan"](m, n, k, cus, splits)
     if config is not None and splits > 1:
         # a forced configuration may split into more ranges than the planner's
@@ -422,7 +432,8 @@ def autotune(a, b, layout: str = "nt", iters: int = 10, out=None, workspace=None
 
     m, n, k, out = _operands(a, b, layout, out)
     code = LAYOUT_CODES[layout]
-    cus = torch.cuda.get_device_properties(a.device).multi_processor_count
+    with torch.cuda.device(a.device):
+        cus = gemm_f16_device_cus()
     aligned = a.data_ptr() % 16 == 0 and b.data_ptr() % 16 == 0
     _, need = gemm_f16_autotune_candidates(code, m, n, k, cus, aligned, 0)
     if workspace is None:

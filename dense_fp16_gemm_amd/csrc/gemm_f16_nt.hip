@@ -2045,6 +2045,12 @@ static int splitk_plan(int32_t layout, int64_t M, int64_t N, int64_t K, int32_t 
     return GEMM_F16_OK;
 }
 
+extern "C" int gemm_f16_device_cus(int32_t *cus)
+{
+    if (!cus) return GEMM_F16_INVALID_ARG;
+    return current_cus(cus);
+}
+
 extern "C" int gemm_f16_splitk_workspace_bytes(int64_t M, int64_t N, int32_t splits,
                                                int64_t *workspace_bytes)
 {

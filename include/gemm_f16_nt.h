@@ -76,6 +76,14 @@ int gemm_f16_nt(int64_t M, int64_t N, int64_t K,
 const char *gemm_f16_nt_status_string(int status);
 
 /*
+ * The current HIP device's compute-unit count, as the planners of the
+ * launching entry points use it (read once per device and cached; safe from
+ * any thread).  GEMM_F16_INVALID_ARG for NULL; GEMM_F16_LAUNCH_FAILED if the
+ * HIP runtime cannot report it.
+ */
+int gemm_f16_device_cus(int32_t *cus);
+
+/*
  * Argument check used by every GEMM entry point; pure host function, touches
  * no device and dereferences nothing.  Returns a status code.
  */
