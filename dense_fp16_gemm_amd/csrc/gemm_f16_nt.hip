@@ -611,6 +611,16 @@ __device__ __forceinline__ void store_tile_f32(const Params &p, const Tile &t,
     }
 }
 
+// Store instructions each wave issues, at least, in the staged epilogue of a
+// tile wholly inside M x N: one 16-byte segment per item with every lane
+// live, counting only the item rounds in which every thread has an item.
+template <class CF>
+constexpr int staged_stores()
+{
+    constexpr int ITEMS_R = CF::WM * CF::MI * (CF::BN / 8);
+    return CF::FM * (ITEMS_R / CF::THREADS);
+}
+
 // Epilogue staged through LDS (the stage the next tile's prefill leaves
 // free).  Block rows of every wave -- WM * MI tile rows each -- are written to
 // LDS as fp16, as many as the stage holds per round, rows padded by 16 bytes
@@ -870,6 +880,9 @@ void gemm_f16_nt_kernel(Params p)
     int32_t slot = blockIdx.x;
     if (slot >= p.tiles) return;
     Tile cur = make_tile<CF, SPLIT>(p, slot, w.row_pitch);
+    // the previous tile was an interior one whose C went out through the
+    // staged epilogue (see the first wait of a tile)
+    bool prev_interior = false;
     // Prefill: slices 0 .. S-2 into stages 0 .. S-2; stage S-1 is refilled
     // while slice 0 is computed.  Issued even when K has fewer slices (those
     // move no data), so every wait below counts the same instructions.
@@ -900,20 +913,34 @@ void gemm_f16_nt_kernel(Params p)
             asm volatile("s_nop 4");
         }
         if (KT > 0) {
-            // slice 0 landed (slices 1 .. S-2 may still be in flight)
-            wait_vmcnt<(S - 2) * L>();
-            lds_barrier();
-#pragma unroll
-            for (int i = 0; i < CF::FM; ++i) read_a(0, 0, 0, i);
-#pragma unroll
-            for (int j = 0; j < CF::FN; ++j) read_b(0, 0, 0, j);
             // early part of slice 1, into stage 1: free, since the previous
-            // tile's epilogue ended with a barrier
+            // tile's epilogue ended with a barrier.  Issued before the wait for
+            // slice 0, which (vmcnt also counting stores) drains that
+            // epilogue's C stores as well: its latency overlaps theirs.
             if constexpr (DX > 0) {
 #pragma unroll
                 for (int d = 0; d < DX; ++d)
                     dma_one<CF>(p, cur, 1, 1, d, lds0, w.wave, w.lane, w.row_pitch);
             }
+            // slice 0 landed (slices 1 .. S-2, and slice 1's early part, may
+            // still be in flight).  After the staged epilogue of an interior
+            // tile, the C stores it issued (at least staged_stores<CF>() per
+            // wave, all younger than the prefill; vmcnt counts stores) stay in
+            // flight too: C drains behind this tile's MFMAs.
+            if constexpr (CF::STAGED_OK && !SPLIT) {
+                static_assert((S - 2) * L + DX + staged_stores<CF>() <= 63, "vmcnt holds at most 63");
+                if (__builtin_amdgcn_readfirstlane(prev_interior ? 1 : 0))
+                    wait_vmcnt<(S - 2) * L + DX + staged_stores<CF>()>();
+                else
+                    wait_vmcnt<(S - 2) * L + DX>();
+            } else {
+                wait_vmcnt<(S - 2) * L + DX>();
+            }
+            lds_barrier();
+#pragma unroll
+            for (int i = 0; i < CF::FM; ++i) read_a(0, 0, 0, i);
+#pragma unroll
+            for (int j = 0; j < CF::FN; ++j) read_b(0, 0, 0, j);
         }
 
         // One branch-free loop over the slices.  Slice kt streams in the refill
@@ -1033,6 +1060,7 @@ void gemm_f16_nt_kernel(Params p)
                 store_tile_staged<CF>(p, cur, acc, w.wave_m, w.wave_n, w.lane, smem);
             else
                 store_tile<CF>(p, cur, acc, w.wave_m, w.wave_n, w.lane);
+            prev_interior = p.staged && cur.m0 + CF::BM <= p.M && cur.n0 + CF::BN <= p.N;
         } else {
             store_tile<CF>(p, cur, acc, w.wave_m, w.wave_n, w.lane);
         }
