@@ -75,6 +75,8 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
+// 16 bytes at any 2-byte alignment (the target's unaligned-access mode)
+typedef _Float16 half8_u_t __attribute__((ext_vector_type(8), aligned(2)));
 
 template <int N>
 struct AccVec;
@@ -693,7 +695,9 @@ __device__ __forceinline__ void store_tile_staged(const Params &p, const Tile &t
                     *reinterpret_cast<const half8_t *>(buf + r * BROW + sr * PITCH + sc * 16);
                 _Float16 *dst = reinterpret_cast<_Float16 *>(p.C) + static_cast<int64_t>(m) * p.N + n;
                 if (n + 8 <= p.N) {
-                    __builtin_memcpy(dst, &h, 16);
+                    // non-temporal: C is written once, and left out of L2 it
+                    // does not evict the A and B strips the XCD's tiles share
+                    __builtin_nontemporal_store(h, reinterpret_cast<half8_u_t *>(dst));
                 } else {
 #pragma unroll
                     for (int e = 0; e < 8; ++e)
