@@ -77,6 +77,8 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
 // 16 bytes at any 2-byte alignment (the target's unaligned-access mode)
 typedef _Float16 half8_u_t __attribute__((ext_vector_type(8), aligned(2)));
+typedef _Float16 half4_u_t __attribute__((ext_vector_type(4), aligned(2)));
+typedef float f32x4_u_t __attribute__((ext_vector_type(4), aligned(4)));
 
 template <int N>
 struct AccVec;
@@ -257,6 +259,7 @@ struct Params {
     int32_t splits, k_split;
     int64_t split_stride;
     float *W;
+    int32_t nt_w;   // store the partials non-temporally (they exceed the L2s)
 };
 
 // Buffer resource (V#) for raw byte addressing of `bytes` bytes at `base`:
@@ -601,7 +604,14 @@ __device__ __forceinline__ void store_tile_f32(const Params &p, const Tile &t,
                     v.z = acc[i][j][4 * g + 2];
                     v.w = acc[i][j][4 * g + 3];
                     if (n + 3 < p.N) {
-                        __builtin_memcpy(wrow + n, &v, 16);   // rows are 4-byte aligned
+                        // rows are 4-byte aligned.  Partials larger than the
+                        // L2s are stored non-temporally, so they do not evict
+                        // the A and B strips; smaller ones stay in L2 for the
+                        // reduction.
+                        if (p.nt_w)
+                            __builtin_nontemporal_store(v, reinterpret_cast<f32x4_u_t *>(wrow + n));
+                        else
+                            __builtin_memcpy(wrow + n, &v, 16);
                     } else {
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
@@ -1082,6 +1092,7 @@ void gemm_f16_nt_kernel(Params p)
 // C, so both are walked as flat arrays: four elements per thread and step
 // (each partial starts 256-byte aligned, so the fp32 loads are 16-byte
 // aligned), then the last M N mod 4 elements one by one.
+template <bool NT>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restrict__ W,
                                                             int32_t splits, int64_t stride,
                                                             int64_t count, uint16_t *__restrict__ C)
@@ -1090,9 +1101,15 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
     const int64_t step = static_cast<int64_t>(gridDim.x) * blockDim.x;
     for (int64_t v = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; v < nvec;
          v += step) {
-        f32x4_t sum = *reinterpret_cast<const f32x4_t *>(W + 4 * v);
-        for (int32_t s = 1; s < splits; ++s)
-            sum += *reinterpret_cast<const f32x4_t *>(W + s * stride + 4 * v);
+        // every partial is read once: non-temporally when they exceed the L2s
+        auto ld = [&](const float *q) {
+            if constexpr (NT)
+                return __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(q));
+            else
+                return *reinterpret_cast<const f32x4_t *>(q);
+        };
+        f32x4_t sum = ld(W + 4 * v);
+        for (int32_t s = 1; s < splits; ++s) sum += ld(W + s * stride + 4 * v);
         const half4_t h = __builtin_convertvector(sum, half4_t);
         __builtin_memcpy(C + 4 * v, &h, 8);   // C is only 2-byte aligned
     }
@@ -1559,6 +1576,16 @@ static int current_cus(int32_t *cus)
 constexpr int32_t kMaxSplits = 64;
 constexpr int64_t kMinSplitK = 512;   // K per unit the planner goes down to
 
+// Partials of more bytes than the L2s hold together (8 XCDs of 4 MB) are
+// written and read back non-temporally: they would only evict the GEMM's
+// A and B strips.  Smaller ones stay in L2 for the reduction (measured both
+// ways: 1024 x 1024 x 65536, 64 MB of partials, +22% non-temporal; 256 x 256
+// x 65536, 4 MB, -14%).
+static bool nt_partials(int64_t splits, int64_t M, int64_t N)
+{
+    return splits * M * N * 4 > (int64_t(32) << 20);
+}
+
 // fp32 elements between the partials of consecutive splits: M N rounded up to
 // 64, so each partial starts 256-byte aligned when the workspace does
 static int64_t split_stride(int64_t M, int64_t N) { return cdiv(M * N, 64) * 64; }
@@ -1649,6 +1676,7 @@ static int launch(const gemm_f16_nt_plan_t &plan, int64_t M, int64_t N, int64_t 
     p.k_split = static_cast<int32_t>(splits > 1 ? k_split : K);
     p.split_stride = splits > 1 ? split_stride(M, N) : 0;
     p.W = W;
+    p.nt_w = splits > 1 && nt_partials(splits, M, N) ? 1 : 0;
     if (splits > 1) p.tiles = static_cast<int32_t>(plan.tiles * splits);
     const KernelEntry &e = kKernels[plan.config_id];
     void *args[] = {&p};
@@ -1809,7 +1837,10 @@ static int run_splitk(int32_t layout, int64_t M, int64_t N, int64_t K, const voi
     const float *w_arg = W;
     uint16_t *c_arg = static_cast<uint16_t *>(C);
     void *args[] = {&w_arg, &splits_arg, &stride_arg, &count_arg, &c_arg};
-    const hipError_t err = hipLaunchKernel(reinterpret_cast<const void *>(&splitk_reduce_kernel),
+    const void *reduce = nt_partials(eff, M, N)
+                             ? reinterpret_cast<const void *>(&splitk_reduce_kernel<true>)
+                             : reinterpret_cast<const void *>(&splitk_reduce_kernel<false>);
+    const hipError_t err = hipLaunchKernel(reduce,
                                            dim3(static_cast<uint32_t>(rgrid)), dim3(256), args, 0,
                                            stream);
     return err == hipSuccess ? GEMM_F16_OK : GEMM_F16_LAUNCH_FAILED;
