@@ -5,7 +5,8 @@
 //
 // One kernel template, every workgroup doing every job (the pages' V2 shape,
 // which suits CDNA's in-order waves sharing one barrier), plus a general
-// kernel for the arguments the template's loads cannot take:
+// kernel for the arguments the template's loads cannot take (per operand
+// layout):
 //
 //  * persistent tile loop: grid = min(tiles, CUs); workgroup wg walks slots
 //    wg, wg + grid, ... through the grouped, XCD-aware order of
@@ -36,7 +37,10 @@
 //  * epilogue: round-to-nearest-even fp32 -> fp16 (v_cvt_f16_f32 under the
 //    default MODE), staged through a free ring stage for 16-byte row stores
 //    at any 2-byte alignment (page 6 "Shared-Memory Epilogue"), or stored
-//    straight from the MFMA layout; masked M/N tails.
+//    straight from the MFMA layout; masked M/N tails.  The staged stores are
+//    non-temporal, keeping C out of L2 and the shared A and B strips in it,
+//    and after an interior tile the next tile's first wait leaves them in
+//    flight (vmcnt counts stores too).
 //
 // Operand roles: the MFMA's first operand (rows of its result block) takes
 // rows of the B tile and the second operand (columns) rows of the A tile, so
@@ -56,7 +60,8 @@
 //    stays that of the NT form (see kn_swizzle);
 //  * a split over K for tile counts that leave most CUs idle: a second
 //    instance of each configuration runs (range, tile) work units that store
-//    fp32 partials, and splitk_reduce_kernel sums them in range order.
+//    fp32 partials (non-temporally when they exceed the L2s), and
+//    splitk_reduce_kernel sums them in range order.
 #include <hip/hip_runtime.h>
 
 #include <mutex>
