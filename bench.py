@@ -39,11 +39,19 @@ PAGES_H100_TFLOPS = 756.0      # the pages' best kernel at 8192^3 on H100 SXM (c
 SOURCE = os.path.join(ROOT, "dense_fp16_gemm_amd", "csrc", "gemm_f16_nt.hip")
 
 
-def source_digest() -> str:
+def source_digest(paths=None) -> str:
+    """Digest of the kernel sources with comments removed and whitespace
+    collapsed: what the recorded HBM traffic belongs to (editing a comment
+    does not change it)."""
+    import re
+
     h = hashlib.sha256()
-    for path in (SOURCE, os.path.join(ROOT, "dense_fp16_gemm_amd", "csrc", "tile_schedule.h")):
-        with open(path, "rb") as f:
-            h.update(f.read())
+    for path in paths or (SOURCE, os.path.join(ROOT, "dense_fp16_gemm_amd", "csrc", "tile_schedule.h")):
+        with open(path, encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update(" ".join(text.split()).encode())   # and layout
     return h.hexdigest()[:16]
 
 
