@@ -357,7 +357,9 @@ typedef struct gemm_f16_tune_entry_t {
  *
  * gemm_f16_autotune: times every candidate above on the caller's buffers and
  * the current device, on `stream`: one untimed call, then `iters` calls
- * between two HIP events; `ms` is the event time over `iters`.  It blocks
+ * between two HIP events; `ms` is the event time over `iters`.  Before the
+ * first candidate is timed, it runs for about 50 ms (in batches of `iters`),
+ * so that the GPU's clock has ramped up from idle.  It blocks
  * until each candidate's events have completed (so it is not for graph
  * capture).  `workspace` (caller-owned device memory, 16-byte aligned, not
  * overlapping A, B or C; NULL when workspace_bytes = 0) bounds the split
