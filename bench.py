@@ -119,6 +119,50 @@ def copy_probe(args) -> int:
     return 0
 
 
+def power_sampler_loop() -> int:
+    """Print `time power_w gfx_clock_mhz` from `amd-smi metric -p -c` every
+    0.5 s until stopped.  Runs as its own process, started before the
+    measuring process touches the GPU."""
+    import re
+    import subprocess
+
+    parent = os.getppid()
+    while os.getppid() == parent:   # ends with the measuring process
+        try:
+            out = subprocess.run(["amd-smi", "metric", "-p", "-c"], capture_output=True,
+                                 text=True, timeout=10).stdout
+        except (OSError, subprocess.SubprocessError):
+            return 1
+        pw = re.search(r"SOCKET_POWER:\s*([0-9.]+)\s*W", out)
+        clk = re.search(r"GFX_0:\s*\n\s*CLK:\s*([0-9.]+)\s*MHz", out)
+        if pw and clk:
+            print(f"{time.time():.3f} {pw.group(1)} {clk.group(1)}", flush=True)
+        time.sleep(0.5)
+    return 0
+
+
+def power_summary(proc, t0: float, t1: float):
+    """Stop the sampler process and summarise its samples taken in [t0, t1]."""
+    proc.terminate()
+    try:
+        out, _ = proc.communicate(timeout=15)
+    except Exception:
+        proc.kill()
+        out, _ = proc.communicate()
+    pw, ck = [], []
+    for line in out.splitlines():
+        parts = line.split()
+        if len(parts) == 3 and t0 <= float(parts[0]) <= t1:
+            pw.append(float(parts[1]))
+            ck.append(float(parts[2]))
+    if not pw:
+        return None
+    return {"samples": len(pw), "socket_power_w_avg": round(sum(pw) / len(pw), 1),
+            "socket_power_w_min": min(pw), "socket_power_w_max": max(pw),
+            "gfx_clock_mhz_avg": round(sum(ck) / len(ck), 1), "gfx_clock_mhz_min": min(ck),
+            "gfx_clock_mhz_max": max(ck), "source": "amd-smi metric -p -c, every 0.5 s"}
+
+
 def run_repeats(args) -> int:
     """The protocol in args.repeat fresh processes, one after another; prints
     the median process's line (the middle value; the upper middle for an even
@@ -182,10 +226,14 @@ def main() -> int:
                     help="timed calls per autotuning candidate")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--power-sample", action="store_true",
+                    help="sample socket power and the GFX clock with amd-smi every 0.5 s during "
+                         "the timed window (give it a window of several seconds via --steps)")
     ap.add_argument("--repeat", type=int, default=3,
                     help="fresh processes, one after another, each running the whole "
                          "protocol; the line is the median one's (1: measure in this process)")
     ap.add_argument("--child", action="store_true", help=argparse.SUPPRESS)
+    ap.add_argument("--power-sampler-loop", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead of the GEMM, run a plain device copy of this many bytes "
                          "(calibrates the HBM byte counters)")
@@ -196,8 +244,20 @@ def main() -> int:
               "the GEMM shards into independent output tiles, see the design notes.",
               file=sys.stderr)
         return 2
+    if args.power_sampler_loop:
+        return power_sampler_loop()
     if args.repeat > 1 and not args.child and args.copy_bytes <= 0:
         return run_repeats(args)
+    sampler = None
+    if args.power_sample:
+        # its own process, started before this one touches the GPU
+        import subprocess
+
+        import atexit
+
+        sampler = subprocess.Popen([sys.executable, os.path.abspath(__file__),
+                                    "--power-sampler-loop"], stdout=subprocess.PIPE, text=True)
+        atexit.register(sampler.terminate)   # whatever path this process leaves by
 
     import numpy as np
     import torch
@@ -313,11 +373,13 @@ def main() -> int:
     torch.cuda.synchronize()
 
     # timed region: exactly `steps` launches, back to back
+    t_start = time.time()
     win0.record(stream)
     for _ in range(args.steps):
         launch()
     win1.record(stream)
     torch.cuda.synchronize()
+    power = power_summary(sampler, t_start, time.time()) if sampler is not None else None
     ms_per_step = win0.elapsed_time(win1) / args.steps
     kernel_avg_ms = ms_per_step
 
@@ -357,6 +419,7 @@ def main() -> int:
                    "inputs": w.note,
                    "seed": w.seed, "accumulate": "f32", "plan": plan,
                    "autotune": tune,
+                   "power": power,
                    "kernel_ms_avg": round(kernel_avg_ms, 5),
                    "source_digest": source_digest()},
         "roofline": roofline,
