@@ -157,8 +157,12 @@ def power_summary(proc, t0: float, t1: float):
             ck.append(float(parts[2]))
     if not pw:
         return None
-    return {"samples": len(pw), "socket_power_w_avg": round(sum(pw) / len(pw), 1),
+    import statistics
+
+    return {"samples": len(pw), "socket_power_w_median": statistics.median(pw),
+            "socket_power_w_avg": round(sum(pw) / len(pw), 1),
             "socket_power_w_min": min(pw), "socket_power_w_max": max(pw),
+            "gfx_clock_mhz_median": statistics.median(ck),
             "gfx_clock_mhz_avg": round(sum(ck) / len(ck), 1), "gfx_clock_mhz_min": min(ck),
             "gfx_clock_mhz_max": max(ck), "source": "amd-smi metric -p -c, every 0.5 s"}
 
