@@ -64,6 +64,9 @@
 //    splitk_reduce_kernel sums them in range order.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <array>
+#include <cmath>
 #include <mutex>
 #include <type_traits>
 #include <vector>
@@ -1339,6 +1342,7 @@ struct KernelEntry {
     int32_t block_m, block_n, block_k, waves, stages, lds_bytes, threads;
     int32_t default_swizzle;
     float rel_rate;   // relative MFMA rate per tile area, for the plan cost model
+    float split_rate; // fraction of one CU's dense fp16 peak, fitted to measured times; split planner
     int32_t staged_ok;
     int32_t general;  // the general kernel: any K, A and B at any 2-byte alignment
     int32_t per_cu;   // workgroups resident per CU (the persistent grid's multiple of the CUs)
@@ -1352,11 +1356,11 @@ const void *split_instance()
 }
 
 template <class CF>
-KernelEntry entry(int swizzle, float rate)
+KernelEntry entry(int swizzle, float rate, float split_rate)
 {
     return KernelEntry{reinterpret_cast<const void *>(&gemm_f16_nt_kernel<CF, false>),
                        split_instance<CF>(), CF::BM, CF::BN, CF::BK, CF::WAVES, CF::STAGES, CF::LDS_BYTES, CF::THREADS,
-                       swizzle, rate, CF::STAGED_OK ? 1 : 0, 0, 1, 2 * CF::AL + CF::BL};
+                       swizzle, rate, split_rate, CF::STAGED_OK ? 1 : 0, 0, 1, 2 * CF::AL + CF::BL};
 }
 
 template <class CF, int LA = 0, int LB = 0>
@@ -1364,76 +1368,76 @@ KernelEntry entry_general(int swizzle)
 {
     return KernelEntry{reinterpret_cast<const void *>(&gemm_f16_nt_any_kernel<CF, LA, LB>),
                        nullptr, CF::BM, CF::BN, CF::BK, CF::WAVES, CF::STAGES, CF::LDS_BYTES,
-                       CF::THREADS, swizzle, 0.0f, 0, 1, any_kernel_per_cu<LA, LB>(),
+                       CF::THREADS, swizzle, 0.0f, 0.0f, 0, 1, any_kernel_per_cu<LA, LB>(),
                        2 * LA + LB};
 }
 
 static const KernelEntry kKernels[] = {
-    entry<Cfg<256, 256, 32, 2, 2, 4>>(8, 0.00f),   // 0: 4 waves of 128x128, 4 stages of K 32
-    entry<Cfg<256, 256, 32, 2, 2, 5>>(8, 0.00f),   // 1: the same, 5 stages
-    entry<Cfg<256, 128, 64, 2, 2, 3>>(8, 0.85f),   // 2: 4 waves of 128x64, 3 stages of K 64
-    entry<Cfg<256, 128, 32, 2, 2, 6>>(8, 0.00f),   // 3: the same tile, 6 stages of K 32
-    entry<Cfg<128, 128, 64, 2, 2, 4>>(8, 0.75f),   // 4: 4 waves of 64x64, 4 stages
-    entry<Cfg<128, 64, 64, 2, 1, 6>>(8, 0.60f),    // 5: 2 waves of 64x64, 6 stages
-    entry<Cfg<256, 256, 32, 2, 4, 4>>(8, 0.00f),   // 6: 8 waves of 128x64, 4 stages of K 32
-    entry<Cfg<256, 256, 32, 4, 2, 4>>(8, 0.00f),   // 7: 8 waves of 64x128, 4 stages of K 32
-    entry<Cfg<256, 256, 32, 2, 4, 5>>(8, 0.00f),   // 8: 8 waves of 128x64, 5 stages of K 32
-    entry<Cfg<256, 256, 64, 2, 2, 2>>(8, 1.00f),   // 9: 4 waves of 128x128, 2 stages of K 64
-    entry<Cfg<256, 256, 64, 2, 4, 2>>(8, 0.00f),   // 10: 8 waves of 128x64, 2 stages of K 64
+    entry<Cfg<256, 256, 32, 2, 2, 4>>(8, 0.00f, 0.751f),   // 0: 4 waves of 128x128, 4 stages of K 32
+    entry<Cfg<256, 256, 32, 2, 2, 5>>(8, 0.00f, 0.746f),   // 1: the same, 5 stages
+    entry<Cfg<256, 128, 64, 2, 2, 3>>(8, 0.85f, 0.711f),   // 2: 4 waves of 128x64, 3 stages of K 64
+    entry<Cfg<256, 128, 32, 2, 2, 6>>(8, 0.00f, 0.555f),   // 3: the same tile, 6 stages of K 32
+    entry<Cfg<128, 128, 64, 2, 2, 4>>(8, 0.75f, 0.558f),   // 4: 4 waves of 64x64, 4 stages
+    entry<Cfg<128, 64, 64, 2, 1, 6>>(8, 0.60f, 0.287f),    // 5: 2 waves of 64x64, 6 stages
+    entry<Cfg<256, 256, 32, 2, 4, 4>>(8, 0.00f, 0.748f),   // 6: 8 waves of 128x64, 4 stages of K 32
+    entry<Cfg<256, 256, 32, 4, 2, 4>>(8, 0.00f, 0.750f),   // 7: 8 waves of 64x128, 4 stages of K 32
+    entry<Cfg<256, 256, 32, 2, 4, 5>>(8, 0.00f, 0.745f),   // 8: 8 waves of 128x64, 5 stages of K 32
+    entry<Cfg<256, 256, 64, 2, 2, 2>>(8, 1.00f, 0.723f),   // 9: 4 waves of 128x128, 2 stages of K 64
+    entry<Cfg<256, 256, 64, 2, 4, 2>>(8, 0.00f, 0.718f),   // 10: 8 waves of 128x64, 2 stages of K 64
     // 11: as 9 with 16x16x32 MFMAs, the whole refill issued early, A double-buffered
-    entry<Cfg<256, 256, 64, 2, 2, 2, 16, 0, 16, 1>>(8, 1.06f),
-    entry<Cfg<256, 128, 64, 2, 2, 3, 16>>(8, 0.00f),   // 12: as 2 with 16x16x32 MFMAs
-    entry<Cfg<192, 256, 64, 2, 2, 2>>(8, 0.80f),   // 13: 4 waves of 96x128, 2 stages of K 64
-    entry<Cfg<256, 192, 64, 2, 2, 2>>(8, 0.82f),   // 14: 4 waves of 128x96, 2 stages of K 64
-    entry<Cfg<192, 256, 32, 2, 2, 5>>(8, 0.00f),   // 15: 4 waves of 96x128, 5 stages of K 32
-    entry<Cfg<256, 192, 32, 2, 2, 5>>(8, 0.00f),   // 16: 4 waves of 128x96, 5 stages of K 32
+    entry<Cfg<256, 256, 64, 2, 2, 2, 16, 0, 16, 1>>(8, 1.06f, 0.792f),
+    entry<Cfg<256, 128, 64, 2, 2, 3, 16>>(8, 0.00f, 0.652f),   // 12: as 2 with 16x16x32 MFMAs
+    entry<Cfg<192, 256, 64, 2, 2, 2>>(8, 0.80f, 0.635f),   // 13: 4 waves of 96x128, 2 stages of K 64
+    entry<Cfg<256, 192, 64, 2, 2, 2>>(8, 0.82f, 0.636f),   // 14: 4 waves of 128x96, 2 stages of K 64
+    entry<Cfg<192, 256, 32, 2, 2, 5>>(8, 0.00f, 0.684f),   // 15: 4 waves of 96x128, 5 stages of K 32
+    entry<Cfg<256, 192, 32, 2, 2, 5>>(8, 0.00f, 0.702f),   // 16: 4 waves of 128x96, 5 stages of K 32
     // 17-20: the scheme of 11 on smaller tiles
-    entry<Cfg<256, 192, 64, 2, 2, 2, 16, 0, 14, 1>>(8, 0.94f),   // 17: 4 waves of 128x96
-    entry<Cfg<192, 256, 64, 2, 2, 2, 16, 0, 14, 1>>(8, 0.97f),   // 18: 4 waves of 96x128
-    entry<Cfg<256, 128, 64, 2, 2, 2, 16, 0, 12, 1>>(8, 0.00f),   // 19: 4 waves of 128x64
-    entry<Cfg<128, 128, 64, 2, 2, 2, 16, 0, 8, 1>>(8, 0.00f),    // 20: 4 waves of 64x64
+    entry<Cfg<256, 192, 64, 2, 2, 2, 16, 0, 14, 1>>(8, 0.94f, 0.760f),   // 17: 4 waves of 128x96
+    entry<Cfg<192, 256, 64, 2, 2, 2, 16, 0, 14, 1>>(8, 0.97f, 0.752f),   // 18: 4 waves of 96x128
+    entry<Cfg<256, 128, 64, 2, 2, 2, 16, 0, 12, 1>>(8, 0.00f, 0.570f),   // 19: 4 waves of 128x64
+    entry<Cfg<128, 128, 64, 2, 2, 2, 16, 0, 8, 1>>(8, 0.00f, 0.384f),    // 20: 4 waves of 64x64
     // 21: 4 waves of 32x64.  For a small M the two tile rows that share a B
     // strip run together on one XCD, and B, the operand streamed from HBM,
     // holds two thirds of every stage (a 128x64 tile gives it one third).
-    entry<Cfg<64, 128, 64, 2, 2, 6>>(8, 0.65f),
+    entry<Cfg<64, 128, 64, 2, 2, 6>>(8, 0.65f, 0.357f),
     // 22: 21 with K 128 per stage (256-byte rows): twice the contiguous bytes
     // per row and DMA instruction, which the HBM stream of B prefers
-    entry<Cfg<64, 128, 128, 2, 2, 3>>(8, 0.66f),
+    entry<Cfg<64, 128, 128, 2, 2, 3>>(8, 0.66f, 0.366f),
     // 23: 4 waves of 32x32, five stages of K 128: more tiles for a small M
     // whose 64x128 tiles would leave CUs idle (M <= 256, N of a few thousand)
-    entry<Cfg<64, 64, 128, 2, 2, 5>>(8, 0.62f),
+    entry<Cfg<64, 64, 128, 2, 2, 5>>(8, 0.62f, 0.259f),
     // 24-29: B stored [K, N] (gemm_f16_nn), the schemes of 11 and 18-21 with
     // transposing fragment reads of B
-    entry<Cfg<256, 256, 64, 2, 2, 2, 16, 0, 16, 0, 1>>(8, 1.06f),   // 24: as 11, A single-buffered
-    entry<Cfg<192, 256, 64, 2, 2, 2, 16, 0, 14, 1, 1>>(8, 0.97f),   // 25: as 18
-    entry<Cfg<256, 128, 64, 2, 2, 2, 16, 0, 12, 1, 1>>(8, 0.85f),   // 26: as 19
-    entry<Cfg<128, 128, 64, 2, 2, 2, 16, 0, 8, 1, 1>>(8, 0.75f),    // 27: as 20
-    entry<Cfg<64, 128, 64, 2, 2, 2, 16, 0, 6, 1, 1>>(8, 0.62f),     // 28: 4 waves of 32x64
+    entry<Cfg<256, 256, 64, 2, 2, 2, 16, 0, 16, 0, 1>>(8, 1.06f, 0.736f),   // 24: as 11, A single-buffered
+    entry<Cfg<192, 256, 64, 2, 2, 2, 16, 0, 14, 1, 1>>(8, 0.97f, 0.706f),   // 25: as 18
+    entry<Cfg<256, 128, 64, 2, 2, 2, 16, 0, 12, 1, 1>>(8, 0.85f, 0.568f),   // 26: as 19
+    entry<Cfg<128, 128, 64, 2, 2, 2, 16, 0, 8, 1, 1>>(8, 0.75f, 0.377f),    // 27: as 20
+    entry<Cfg<64, 128, 64, 2, 2, 2, 16, 0, 6, 1, 1>>(8, 0.62f, 0.218f),     // 28: 4 waves of 32x64
     // 29: 28 with 6 stages, the refill spread over each slice: more of B in
     // flight for a small M (the streamed operand)
-    entry<Cfg<64, 128, 64, 2, 2, 6, 16, 0, 0, 0, 1>>(8, 0.66f),
+    entry<Cfg<64, 128, 64, 2, 2, 6, 16, 0, 0, 0, 1>>(8, 0.66f, 0.243f),
     // 30-32: A stored [K, M] and B [N, K] (gemm_f16_tt); 33-35: A [K, M] and
     // B [K, N] (gemm_f16_tn): transposing fragment reads for A as well
-    entry<Cfg<256, 256, 64, 2, 2, 2, 16, 0, 16, 0, 0, 1>>(8, 1.06f),   // 30
-    entry<Cfg<256, 128, 64, 2, 2, 2, 16, 0, 12, 1, 0, 1>>(8, 0.85f),   // 31
-    entry<Cfg<128, 128, 64, 2, 2, 2, 16, 0, 8, 1, 0, 1>>(8, 0.75f),    // 32
-    entry<Cfg<256, 256, 64, 2, 2, 2, 16, 0, 16, 0, 1, 1>>(8, 1.06f),   // 33
-    entry<Cfg<256, 128, 64, 2, 2, 2, 16, 0, 12, 1, 1, 1>>(8, 0.85f),   // 34
-    entry<Cfg<128, 128, 64, 2, 2, 2, 16, 0, 8, 1, 1, 1>>(8, 0.75f),    // 35
+    entry<Cfg<256, 256, 64, 2, 2, 2, 16, 0, 16, 0, 0, 1>>(8, 1.06f, 0.728f),   // 30
+    entry<Cfg<256, 128, 64, 2, 2, 2, 16, 0, 12, 1, 0, 1>>(8, 0.85f, 0.558f),   // 31
+    entry<Cfg<128, 128, 64, 2, 2, 2, 16, 0, 8, 1, 0, 1>>(8, 0.75f, 0.375f),    // 32
+    entry<Cfg<256, 256, 64, 2, 2, 2, 16, 0, 16, 0, 1, 1>>(8, 1.06f, 0.676f),   // 33
+    entry<Cfg<256, 128, 64, 2, 2, 2, 16, 0, 12, 1, 1, 1>>(8, 0.85f, 0.558f),   // 34
+    entry<Cfg<128, 128, 64, 2, 2, 2, 16, 0, 8, 1, 1, 1>>(8, 0.75f, 0.374f),    // 35
     // 36-37: TT with a 64-wide B side (B [N, K] takes any multiple of 32
     // rows; A [K, M] needs 128): 4 waves of 64x32, twice the tiles of 32 for
     // a small M.  36 keeps 6 stages with the refill spread over each slice,
     // as 29 does for NN; 37 is the two-stage early-refill scheme.
-    entry<Cfg<128, 64, 64, 2, 2, 6, 16, 0, 0, 0, 0, 1>>(8, 0.66f),     // 36
-    entry<Cfg<128, 64, 64, 2, 2, 2, 16, 0, 6, 1, 0, 1>>(8, 0.00f),     // 37
+    entry<Cfg<128, 64, 64, 2, 2, 6, 16, 0, 0, 0, 0, 1>>(8, 0.66f, 0.254f),     // 36
+    entry<Cfg<128, 64, 64, 2, 2, 2, 16, 0, 6, 1, 0, 1>>(8, 0.00f, 0.222f),     // 37
     // 38-41: 64-wide tiles on a k-outermost side (128-byte LDS rows), 6
     // stages with the refill spread over each slice, for a small M or N:
     // 38 NN 128x64 (B [K, N]), 39 TT 64x128 (A [K, M]), 40 TN 64x128, 41 TN
     // 128x64
-    entry<Cfg<128, 64, 64, 2, 2, 6, 16, 0, 0, 0, 1, 0>>(8, 0.66f),     // 38
-    entry<Cfg<64, 128, 64, 2, 2, 6, 16, 0, 0, 0, 0, 1>>(8, 0.66f),     // 39
-    entry<Cfg<64, 128, 64, 2, 2, 6, 16, 0, 0, 0, 1, 1>>(8, 0.66f),     // 40
-    entry<Cfg<128, 64, 64, 2, 2, 6, 16, 0, 0, 0, 1, 1>>(8, 0.66f),     // 41
+    entry<Cfg<128, 64, 64, 2, 2, 6, 16, 0, 0, 0, 1, 0>>(8, 0.66f, 0.278f),     // 38
+    entry<Cfg<64, 128, 64, 2, 2, 6, 16, 0, 0, 0, 0, 1>>(8, 0.66f, 0.299f),     // 39
+    entry<Cfg<64, 128, 64, 2, 2, 6, 16, 0, 0, 0, 1, 1>>(8, 0.66f, 0.216f),     // 40
+    entry<Cfg<128, 64, 64, 2, 2, 6, 16, 0, 0, 0, 1, 1>>(8, 0.66f, 0.217f),     // 41
     // 42-44: the general kernel for NN, TT and TN (loads along the operand's
     // contiguous dimension), for arguments the direct-to-LDS kernels of those
     // layouts cannot take
@@ -1604,59 +1608,163 @@ static int64_t split_k_len(int id, int64_t K, int32_t splits)
     return cdiv(cdiv(K, splits), bk) * bk;
 }
 
-// Estimated time of configuration `id` with K split `splits` ways: rounds of
-// the persistent grid times one unit's MFMA work at the configuration's
-// relative rate (absolute scale: one CU at about 55% of its dense fp16 peak),
-// plus, when K is actually split, the fp32 partials written and read back at
-// about 4 TB/s and the reduction launch.
+// Estimated time of configuration `id` with K split `splits` ways, a model
+// fitted to measured times of every configuration and split count on 28
+// shapes per layout (under-filled grids, long and short K; one MI355X):
+//   compute  rounds of the persistent grid x (one unit's MFMA work at the
+//            configuration's split_rate of a CU's dense fp16 peak + a fixed
+//            cost per unit)
+//   operands A and B read once from HBM, at a bandwidth that falls with the
+//            fraction of CUs the units occupy
+//   time     the larger of the two plus a tenth of the smaller (they overlap
+//            almost entirely), a fixed launch cost and C written to HBM
+//   split    when K is actually split, the fp32 partials written and read
+//            back, the fp16 result written, and the reduction launch.
 static double split_cost(int id, int64_t M, int64_t N, int64_t K, int32_t splits, int32_t cus,
                          int64_t *splits_eff)
 {
-    constexpr double kCuFlops = 2.5e15 / 256 * 0.55;
-    constexpr double kBytesPerSec = 4e12;
-    constexpr double kLaunchSec = 4e-6;
+    constexpr double kCuPeak = 2.5e15 / 256;   // dense fp16 flop/s of one CU
+    constexpr double kUnitSec = 1.86e-07;      // per unit: pipeline fill and epilogue
+    constexpr double kLaunchSec = 4.4e-06;     // per launch
+    constexpr double kHbmBytesPerSec = 3.93e+12;
+    static constexpr double kActiveExp = 0.328;      // bandwidth ~ (fraction of CUs busy)^kActiveExp
+    constexpr double kOverlap = 0.1;
+    constexpr double kReduceBytesPerSec = 5.13e+12;
+    constexpr double kReduceSec = 3.21e-06;
     const KernelEntry &e = kKernels[id];
+    if (cus <= 0) cus = 1;
     const int64_t ks = split_k_len(id, K, splits);
     const int64_t eff = cdiv(K, ks);
     const int64_t units = cdiv(M, e.block_m) * cdiv(N, e.block_n) * eff;
-    const double rounds = static_cast<double>(cdiv(units, cus > 0 ? cus : 1));
-    double t = rounds * e.block_m * e.block_n * static_cast<double>(ks) * 2.0 / (e.rel_rate * kCuFlops);
-    if (eff > 1)
-        t += (2.0 * eff * static_cast<double>(M * N) * 4.0 + static_cast<double>(M * N) * 2.0) /
-                 kBytesPerSec + kLaunchSec;
+    const double rounds = static_cast<double>(cdiv(units, cus));
+    const double rate = e.split_rate > 0.0f ? e.split_rate : 0.01;
+    const double compute =
+        rounds * (e.block_m * e.block_n * static_cast<double>(eff > 1 ? ks : K) * 2.0 /
+                      (rate * kCuPeak) + kUnitSec);
+    // (fraction of CUs busy)^kActiveExp, tabulated in steps of 1/1024
+    static const std::array<float, 1025> busy_pow = [] {
+        std::array<float, 1025> t{};
+        for (int i = 0; i <= 1024; ++i)
+            t[i] = static_cast<float>(std::pow(std::max(i, 1) / 1024.0, kActiveExp));
+        return t;
+    }();
+    const double busy = units < cus ? busy_pow[units * 1024 / cus] : 1.0;
+    const double operands =
+        static_cast<double>(M + N) * static_cast<double>(K) * 2.0 / (kHbmBytesPerSec * busy);
+    const double mn = static_cast<double>(M) * static_cast<double>(N);
+    double t = std::max(compute, operands) + kOverlap * std::min(compute, operands) + kLaunchSec +
+               mn * 2.0 / kHbmBytesPerSec;
+    if (eff > 1) t += (2.0 * eff * mn * 4.0 + mn * 2.0) / kReduceBytesPerSec + kReduceSec;
     *splits_eff = eff;
     return t;
 }
 
-// Configuration and effective split count for the split-K entry points
-// (K > 0, direct-to-LDS arguments).  splits > 0 fixes the requested count,
-// config_id >= 0 the configuration; otherwise the cheapest by split_cost.
-// With one split this picks what choose_config picks.
-static void choose_split(int64_t M, int64_t N, int64_t K, int32_t cus, int32_t config_id,
-                         int32_t splits, int *id_out, int32_t *splits_out, int32_t layout = 0)
+// Whether configuration `id` takes part in the split-K planner's search: of
+// the configurations of one layout with the same tile, only the one with the
+// highest split_rate (split_cost sees nothing else of a configuration but
+// the rounding of K to its slices).  Keeps the search to a few hundred cost
+// evaluations per call.
+static bool split_candidate(int id)
 {
+    static const std::array<bool, kNumKernels> flags = [] {
+        std::array<bool, kNumKernels> f{};
+        for (int i = 0; i < kNumKernels; ++i) {
+            const KernelEntry &e = kKernels[i];
+            f[i] = e.split_rate > 0.0f && !e.general;
+            for (int j = 0; j < kNumKernels && f[i]; ++j) {
+                const KernelEntry &o = kKernels[j];
+                if (j != i && !o.general && o.layout == e.layout && o.block_m == e.block_m &&
+                    o.block_n == e.block_n &&
+                    (o.split_rate > e.split_rate || (o.split_rate == e.split_rate && j < i)))
+                    f[i] = false;
+            }
+        }
+        return f;
+    }();
+    return flags[id];
+}
+
+// Configuration and effective split count for the split-K entry points
+// (K > 0, direct-to-LDS arguments).  config_id >= 0 fixes the configuration;
+// splits > 0 fixes the requested count, and splits == 1 (or no split chosen)
+// means exactly the plain entry point's plan.  Otherwise the cheapest by
+// split_cost among the plain plan and the layout's split candidates split at
+// least two ways (K per unit at least kMinSplitK, at most 4 rounds of units).
+static void choose_split_search(int64_t M, int64_t N, int64_t K, int32_t cus, int32_t config_id,
+                                int32_t splits, int *id_out, int32_t *splits_out, int32_t layout)
+{
+    const int plain = config_id >= 0 ? config_id : choose_config(M, N, cus, layout);
     double best = 0.0;
     int best_id = -1;
     int64_t best_eff = 1;
+    auto consider = [&](int id, int32_t sp) {
+        int64_t eff = 1;
+        const double c = split_cost(id, M, N, K, sp, cus, &eff);
+        if (best_id < 0 || c < best) {
+            best = c;
+            best_id = id;
+            best_eff = eff;
+        }
+    };
+    if (splits == 1) {
+        *id_out = plain;
+        *splits_out = 1;
+        return;
+    }
+    if (splits <= 0) consider(plain, 1);
     for (int id = 0; id < kNumKernels; ++id) {
         if (config_id >= 0 ? id != config_id
-                           : (kKernels[id].rel_rate <= 0.0f || kKernels[id].layout != layout))
+                           : (!split_candidate(id) || kKernels[id].layout != layout))
             continue;
-        const int32_t s_lo = splits > 0 ? splits : 1;
+        const int32_t s_lo = splits > 0 ? splits : 2;
         const int32_t s_hi = splits > 0 ? splits : kMaxSplits;
+        const int64_t tiles = cdiv(M, kKernels[id].block_m) * cdiv(N, kKernels[id].block_n);
         for (int32_t sp = s_lo; sp <= s_hi; ++sp) {
-            if (splits <= 0 && sp > 1 && cdiv(K, sp) < kMinSplitK) break;
-            int64_t eff = 1;
-            const double c = split_cost(id, M, N, K, sp, cus, &eff);
-            if (best_id < 0 || c < best) {
-                best = c;
-                best_id = id;
-                best_eff = eff;
-            }
+            if (splits <= 0 && cdiv(K, sp) < kMinSplitK) break;
+            // beyond 4 rounds of the grid more ranges only add partials
+            if (splits <= 0 && tiles * sp > 4 * int64_t(cus > 0 ? cus : 1)) break;
+            if (splits <= 0 && cdiv(K, split_k_len(id, K, sp)) <= 1) continue;
+            consider(id, sp);
         }
     }
     *id_out = best_id;
     *splits_out = static_cast<int32_t>(best_eff);
+    if (best_eff <= 1 && splits <= 0) *id_out = plain;
+}
+
+// choose_split_search behind a per-thread cache of the last few decisions, so
+// a caller that repeats a shape does not pay for the search on every call.
+static void choose_split(int64_t M, int64_t N, int64_t K, int32_t cus, int32_t config_id,
+                         int32_t splits, int *id_out, int32_t *splits_out, int32_t layout = 0)
+{
+    struct Choice {
+        int64_t M = -1, N = -1, K = -1;
+        int32_t cus = 0, config_id = 0, splits = 0, layout = 0;
+        int id = -1;
+        int32_t eff = 1;
+    };
+    static thread_local Choice cache[4];
+    static thread_local int next = 0;
+    for (const Choice &c : cache) {
+        if (c.id >= 0 && c.M == M && c.N == N && c.K == K && c.cus == cus &&
+            c.config_id == config_id && c.splits == splits && c.layout == layout) {
+            *id_out = c.id;
+            *splits_out = c.eff;
+            return;
+        }
+    }
+    choose_split_search(M, N, K, cus, config_id, splits, id_out, splits_out, layout);
+    Choice &c = cache[next];
+    next = (next + 1) % 4;
+    c.M = M;
+    c.N = N;
+    c.K = K;
+    c.cus = cus;
+    c.config_id = config_id;
+    c.splits = splits;
+    c.layout = layout;
+    c.id = *id_out;
+    c.eff = *splits_out;
 }
 
 static int launch(const gemm_f16_nt_plan_t &plan, int64_t M, int64_t N, int64_t K,

@@ -14,11 +14,13 @@
 //     persistent kernel's workgroup `wg` handles slots wg, wg + grid, ...
 //     (page "6. Register Reallocation, Multicast, and a Persistent Kernel",
 //     Persistent Tile Loop), and the dispatcher places workgroup `wg` on
-//     XCD `wg % xcds`.  Each XCD has its own L2, so within one round of
-//     `grid` slots we hand each XCD a contiguous run of grid / xcds linear
-//     ids; the raster group then makes that run a compact block of tiles.
-//     A partial last round keeps the plain order, so the map remains a
-//     bijection on [0, tiles).
+//     XCD `wg % xcds`.  Each XCD has its own L2, so within one round we
+//     hand each XCD a contiguous run of the round's linear ids; the raster
+//     group then makes that run a compact block of tiles.  A round of n
+//     active slots (n = grid, or fewer in a partial last round; any n, not
+//     only multiples of xcds) gives XCD x the n / xcds ids after those of
+//     XCDs 0..x-1, plus one more when x < n % xcds: exactly the number of
+//     its workgroups below n, so the map is a bijection on [0, tiles).
 #ifndef GEMM_F16_TILE_SCHEDULE_H
 #define GEMM_F16_TILE_SCHEDULE_H
 
@@ -53,9 +55,12 @@ GEMM_F16_HD inline int32_t slot_to_linear(int32_t slot, int32_t grid, int32_t ti
     const int32_t round = slot / grid;
     const int32_t wg = slot - round * grid;
     const int32_t base = round * grid;
-    if (xcds <= 1 || grid % xcds != 0 || base + grid > tiles) return slot;
-    const int32_t per_xcd = grid / xcds;
-    return base + (wg % xcds) * per_xcd + wg / xcds;
+    if (xcds <= 1) return slot;
+    const int32_t n = tiles - base < grid ? tiles - base : grid;
+    const int32_t q = n / xcds;
+    const int32_t r = n - q * xcds;
+    const int32_t x = wg % xcds;
+    return base + x * q + (x < r ? x : r) + wg / xcds;
 }
 
 }  // namespace gemm_f16

@@ -195,6 +195,27 @@ def test_xcd_order_gives_each_xcd_a_compact_block(g):
             assert len(ms) * len(ns) == 32 and len(ms) + len(ns) <= 12
 
 
+@pytest.mark.parametrize("grid,tiles", [(252, 252), (250, 250), (216, 300), (256, 300), (7, 20),
+                                        (100, 100), (9, 9)])
+def test_xcd_runs_are_contiguous_for_any_grid(g, grid, tiles):
+    """Every round, full or partial, of any size (not only multiples of the 8
+    XCDs) gives each XCD's workgroups consecutive linear ids.  One tile row
+    and raster groups one column wide make the tile column the linear id."""
+    plan = g.gemm_f16_nt_plan(256, tiles * 256, 64, 256)
+    plan.tiles_m, plan.tiles_n, plan.tiles = 1, tiles, tiles
+    plan.swizzle, plan.grid, plan.xcds = 1, grid, 8
+    seen = []
+    for base in range(0, tiles, grid):
+        active = min(grid, tiles - base)
+        start = base
+        for xcd in range(8):
+            ids = [g.gemm_f16_nt_tile_of_slot(plan, base + w)[1] for w in range(xcd, active, 8)]
+            assert ids == list(range(start, start + len(ids)))
+            start += len(ids)
+            seen += ids
+    assert sorted(seen) == list(range(tiles))
+
+
 def test_wave_quantization_figure(g):
     """Page 6, Performance: 128 x 320 tiles over 8192^2 give 1664 tiles, 12.6
     rounds on 132 processors.  The same count rule (ceil per axis) applies
