@@ -1415,7 +1415,7 @@ static const KernelEntry kKernels[] = {
     entry<Cfg<64, 128, 64, 2, 2, 2, 16, 0, 6, 1, 1>>(8, 0.62f, 0.218f),     // 28: 4 waves of 32x64
     // 29: 28 with 6 stages, the refill spread over each slice: more of B in
     // flight for a small M (the streamed operand)
-    entry<Cfg<64, 128, 64, 2, 2, 6, 16, 0, 0, 0, 1>>(8, 0.66f, 0.243f),
+    entry<Cfg<64, 128, 64, 2, 2, 6, 16, 0, 0, 0, 1>>(8, 0.58f, 0.243f),
     // 30-32: A stored [K, M] and B [N, K] (gemm_f16_tt); 33-35: A [K, M] and
     // B [K, N] (gemm_f16_tn): transposing fragment reads for A as well
     entry<Cfg<256, 256, 64, 2, 2, 2, 16, 0, 16, 0, 0, 1>>(8, 1.06f, 0.728f),   // 30
@@ -1428,15 +1428,18 @@ static const KernelEntry kKernels[] = {
     // rows; A [K, M] needs 128): 4 waves of 64x32, twice the tiles of 32 for
     // a small M.  36 keeps 6 stages with the refill spread over each slice,
     // as 29 does for NN; 37 is the two-stage early-refill scheme.
-    entry<Cfg<128, 64, 64, 2, 2, 6, 16, 0, 0, 0, 0, 1>>(8, 0.66f, 0.254f),     // 36
+    entry<Cfg<128, 64, 64, 2, 2, 6, 16, 0, 0, 0, 0, 1>>(8, 0.56f, 0.254f),     // 36
     entry<Cfg<128, 64, 64, 2, 2, 2, 16, 0, 6, 1, 0, 1>>(8, 0.00f, 0.222f),     // 37
     // 38-41: 64-wide tiles on a k-outermost side (128-byte LDS rows), 6
     // stages with the refill spread over each slice, for a small M or N:
     // 38 NN 128x64 (B [K, N]), 39 TT 64x128 (A [K, M]), 40 TN 64x128, 41 TN
-    // 128x64
+    // 128x64.  Against the same-area tile of the other orientation
+    // (29, 36, 40), unsplit and timed by the autotuner over 14-16 shapes
+    // each, 38 was about 14% faster than 29, 39 18% faster than 36 and 41 2%
+    // faster than 40; the rates of 29, 36 and 40 say so.
     entry<Cfg<128, 64, 64, 2, 2, 6, 16, 0, 0, 0, 1, 0>>(8, 0.66f, 0.278f),     // 38
     entry<Cfg<64, 128, 64, 2, 2, 6, 16, 0, 0, 0, 0, 1>>(8, 0.66f, 0.299f),     // 39
-    entry<Cfg<64, 128, 64, 2, 2, 6, 16, 0, 0, 0, 1, 1>>(8, 0.66f, 0.216f),     // 40
+    entry<Cfg<64, 128, 64, 2, 2, 6, 16, 0, 0, 0, 1, 1>>(8, 0.645f, 0.216f),    // 40
     entry<Cfg<128, 64, 64, 2, 2, 6, 16, 0, 0, 0, 1, 1>>(8, 0.66f, 0.217f),     // 41
     // 42-44: the general kernel for NN, TT and TN (loads along the operand's
     // contiguous dimension), for arguments the direct-to-LDS kernels of those
