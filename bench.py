@@ -413,10 +413,9 @@ def main() -> int:
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
-        # the pages' figure is for the NT form of the headline shape only
-        "vs_baseline": (round(tflops / PAGES_H100_TFLOPS, 3)
-                        if name == workloads.HEADLINE and lay == "nt" and args.splitk is None
-                        and not args.autotune else None),
+        # no published MI355X figure exists for this metric; the pages' H100
+        # number is context only (below), never the baseline
+        "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic",
         "config": {"workload": name, "M": w.M, "N": w.N, "K": w.K, "layout": lay,
@@ -425,6 +424,12 @@ def main() -> int:
                    "autotune": tune,
                    "power": power,
                    "kernel_ms_avg": round(kernel_avg_ms, 5),
+                   # the pages' best kernel at 8192^3 ran on other hardware
+                   # (H100 SXM): the ratio is context, not a target
+                   "context_pages_h100": (
+                       {"tflops": PAGES_H100_TFLOPS, "ratio": round(tflops / PAGES_H100_TFLOPS, 3)}
+                       if name == workloads.HEADLINE and lay == "nt" and args.splitk is None
+                       and not args.autotune else None),
                    "source_digest": source_digest()},
         "roofline": roofline,
         "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_seconds),

@@ -1469,13 +1469,14 @@ static bool overlaps(const void *p, int64_t pbytes, const void *q, int64_t qbyte
 static int validate(int64_t M, int64_t N, int64_t K, const void *A, const void *B, const void *C)
 {
     if (M < 0 || N < 0 || K < 0) return GEMM_F16_INVALID_ARG;
-    if (M > INT32_MAX || N > INT32_MAX) return GEMM_F16_UNSUPPORTED;
+    // every dimension below 2^31 first: the byte counts below then stay
+    // below 2^63
+    if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return GEMM_F16_UNSUPPORTED;
     const int64_t a_bytes = M * K * 2, b_bytes = N * K * 2, c_bytes = M * N * 2;
     if ((a_bytes > 0 && !A) || (b_bytes > 0 && !B) || (c_bytes > 0 && !C))
         return GEMM_F16_INVALID_ARG;
     if (overlaps(C, c_bytes, A, a_bytes) || overlaps(C, c_bytes, B, b_bytes))
         return GEMM_F16_INVALID_ARG;
-    if (K > INT32_MAX) return GEMM_F16_UNSUPPORTED;
     // fp16 elements: every matrix at least 2-byte aligned
     if ((a_bytes > 0 && reinterpret_cast<uintptr_t>(A) % 2 != 0) ||
         (b_bytes > 0 && reinterpret_cast<uintptr_t>(B) % 2 != 0) ||
@@ -1662,21 +1663,25 @@ static double split_cost(int id, int64_t M, int64_t N, int64_t K, int32_t splits
     return t;
 }
 
-// Whether configuration `id` takes part in the split-K planner's search: of
-// the configurations of one layout with the same tile, only the one with the
-// highest split_rate (split_cost sees nothing else of a configuration but
-// the rounding of K to its slices).  Keeps the search to a few hundred cost
-// evaluations per call.
+// Whether configuration `id` takes part in the split-K planner's search:
+// only configurations the plain planner may choose (rel_rate > 0; the others
+// are compiled for sweeps and tests), and of those with one layout and tile,
+// only the one with the highest split_rate (split_cost sees nothing else of
+// a configuration but the rounding of K to its slices).  Keeps the search to
+// a few hundred cost evaluations per call.
 static bool split_candidate(int id)
 {
     static const std::array<bool, kNumKernels> flags = [] {
         std::array<bool, kNumKernels> f{};
+        auto plannable = [](const KernelEntry &e) {
+            return e.split_rate > 0.0f && e.rel_rate > 0.0f && !e.general;
+        };
         for (int i = 0; i < kNumKernels; ++i) {
             const KernelEntry &e = kKernels[i];
-            f[i] = e.split_rate > 0.0f && !e.general;
+            f[i] = plannable(e);
             for (int j = 0; j < kNumKernels && f[i]; ++j) {
                 const KernelEntry &o = kKernels[j];
-                if (j != i && !o.general && o.layout == e.layout && o.block_m == e.block_m &&
+                if (j != i && plannable(o) && o.layout == e.layout && o.block_m == e.block_m &&
                     o.block_n == e.block_n &&
                     (o.split_rate > e.split_rate || (o.split_rate == e.split_rate && j < i)))
                     f[i] = false;

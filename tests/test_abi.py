@@ -75,6 +75,11 @@ A0, B0, C0 = 0x10000, 0x20000000, 0x40000000   # fake, well-separated, aligned a
     ((8, 8, (1 << 21) + 8, A0, B0 + (1 << 40), C0 + (1 << 41)), 0),   # K past the DMA path
     ((8, 8, (1 << 31), A0, B0 + (1 << 40), C0 + (1 << 41)), 2),       # K beyond int32
     ((1 << 31, 8, 8, A0, B0 + (1 << 40), C0 + (1 << 41)), 2),         # M beyond int32
+    # K far beyond int32: rejected before any byte count (M K 2 would
+    # overflow int64) is formed
+    ((8, 8, 1 << 62, A0, B0 + (1 << 40), C0 + (1 << 41)), 2),
+    ((1 << 40, 1 << 40, 1 << 62, A0, B0, C0), 2),
+    ((8, 1 << 62, 8, A0, B0, C0), 2),
 ])
 def test_validate(g, args, status):
     assert g.gemm_f16_nt_validate(*args) == status
@@ -356,3 +361,31 @@ def test_splitk_plan_layouts(g, lay):
         plan2, eff2, ws2 = plan_fn(*shape, 256)
         if g.gemm_f16_nt_config_info(plan2.config_id).block_k == 32:
             assert eff2 == 1 and ws2 == 0 and plan2.layout == lay
+
+
+def test_splitk_plan_of_the_underfilled_workload(g):
+    # The benchmark's split-K workload (1024 x 1024 x 65536: sixteen 256 x 256
+    # tiles for 256 CUs) is planned as configuration 2 (256 x 128 tiles) over
+    # 8 K ranges of 8192: 256 units, one round.  A change to the cost model
+    # or the split candidates that moves this plan shows up here.
+    plan, splits, ws = g.gemm_f16_nt_splitk_plan(1024, 1024, 65536, 256, 0)
+    assert (plan.config_id, splits) == (2, 8)
+    assert ws == 8 * 1024 * 1024 * 4
+    assert plan.tiles * splits == 256 and plan.grid == 256
+
+
+def test_splitk_candidates_are_plannable_configurations(g):
+    # the split planner only picks configurations the plain planner may pick
+    # for some shape of the layout (the others are compiled for sweeps)
+    plannable = set()
+    for lay in ("nt", "nn", "tt", "tn"):
+        plan_fn = getattr(g, f"gemm_f16_{lay}_plan")
+        for m in (64, 128, 256, 1024, 4096, 8192, 16384):
+            for n in (64, 128, 256, 1024, 4096, 8192, 16384):
+                plannable.add(plan_fn(m, n, 4096, 256).config_id)
+    for lay in ("nt", "nn", "tt", "tn"):
+        split_fn = getattr(g, f"gemm_f16_{lay}_splitk_plan")
+        for m, n, k in [(256, 256, 65536), (1024, 1024, 65536), (512, 2048, 32768),
+                        (128, 128, 131072), (3000, 104, 50000), (2048, 512, 65536)]:
+            plan, splits, _ = split_fn(m, n, k, 256, 0)
+            assert plan.config_id in plannable, (lay, m, n, k, plan.config_id, splits)
