@@ -380,8 +380,8 @@ def test_splitk_candidates_are_plannable_configurations(g):
     plannable = set()
     for lay in ("nt", "nn", "tt", "tn"):
         plan_fn = getattr(g, f"gemm_f16_{lay}_plan")
-        for m in (64, 128, 256, 1024, 4096, 8192, 16384):
-            for n in (64, 128, 256, 1024, 4096, 8192, 16384):
+        for m in (64, 128, 256, 1024, 2048, 4096, 4992, 7000, 8192, 16384):
+            for n in (64, 128, 256, 1024, 2048, 4096, 4992, 7000, 8192, 16384):
                 plannable.add(plan_fn(m, n, 4096, 256).config_id)
     for lay in ("nt", "nn", "tt", "tn"):
         split_fn = getattr(g, f"gemm_f16_{lay}_splitk_plan")
