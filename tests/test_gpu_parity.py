@@ -5,8 +5,8 @@ compared element by element within |C - C_ref| <= 2 ulp16(C_ref) + 1e-3;
 integer inputs, identity/permutation B, all-ones, scaling and the closed-form
 probes must be bit-exact.  Shapes span several tiles with ragged tails; the
 five workload shapes run at full size in the launch configuration the
-benchmark times, checked on sampled elements (whole boundary rows/columns
-plus random positions) and through size-independent properties.
+benchmark times, checked against the whole oracle matrix and through
+size-independent properties.
 """
 import sys
 
@@ -270,32 +270,23 @@ def test_page_mae_statistic(g):
 # ---------------------------------------------------------------------------
 # full-size workloads, in the launch configuration the benchmark times
 # ---------------------------------------------------------------------------
-def _sample_positions(m, n, rng, count=4096):
-    rows = [rng.integers(0, m, count)]
-    cols = [rng.integers(0, n, count)]
-    # whole last row and column (the tails) and whole first row
-    for r in {0, m - 1}:
-        rows.append(np.full(n, r))
-        cols.append(np.arange(n))
-    rows.append(np.arange(m))
-    cols.append(np.full(m, n - 1))
-    return np.concatenate(rows), np.concatenate(cols)
-
-
 @pytest.mark.parametrize("name", list(workloads.WORKLOADS))
 def test_full_size_workload(g, oracle_mod, name):
+    """Each workload at full size, in the plan the benchmark times, against
+    the whole oracle matrix (8192^3 takes the oracle about 20 s on 16 host
+    cores)."""
     w = workloads.WORKLOADS[name]
     _say(f"  workload {name}: {w.M}x{w.N}x{w.K} {w.dist} seed={w.seed}")
     a, b = workloads.workload_inputs(name)
     got = run_gpu(g, a, b)
     assert not np.isnan(got).any(), "unwritten (NaN-poisoned) output elements"
-    rng = np.random.default_rng(w.seed)
-    r, c = _sample_positions(w.M, w.N, rng)
-    ref = oracle_mod.gemm_sampled(a, b, r, c)
+    _say(f"  oracle {name}: full {w.M}x{w.N} output")
+    ref = oracle_mod.gemm(a, b)
     if w.dist == "int2":
-        assert_bit_exact(got[r, c], ref, name)
+        assert_bit_exact(got, ref, name)
     else:
-        assert_within_tolerance(got[r, c], ref, name)
+        stats = assert_within_tolerance(got, ref, name)
+        _say(f"  {name}: {stats}")
 
 
 def test_tail_equals_padded_interior(g):
