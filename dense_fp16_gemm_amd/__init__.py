@@ -14,7 +14,7 @@ import threading
 
 from .build import LIB_PATH
 
-OK, INVALID_ARG, UNSUPPORTED, LAUNCH_FAILED = 0, 1, 2, 3
+OK, INVALID_ARG, UNSUPPORTED, LAUNCH_FAILED, SCRATCH_LIMIT = 0, 1, 2, 3, 4
 
 _lock = threading.Lock()
 _lib = None
@@ -119,6 +119,8 @@ def load():
         lib.gemm_f16_autotune.argtypes = [i32, i64, i64, i64, p, p, p, p, i64, i32, p, te, te,
                                           i32, ctypes.POINTER(i32)]
         lib.gemm_f16_autotune.restype = ctypes.c_int
+        lib.gemm_f16_nt_splitk_noalloc.argtypes = [i64, i64, i64, p, p, p, i32, p]
+        lib.gemm_f16_nt_splitk_noalloc.restype = ctypes.c_int
         lib.gemm_f16_splitk_workspace_bytes.argtypes = [i64, i64, i32, ctypes.POINTER(i64)]
         lib.gemm_f16_splitk_workspace_bytes.restype = ctypes.c_int
         lib.gemm_f16_device_cus.argtypes = [ctypes.POINTER(i32)]
@@ -215,6 +217,15 @@ gemm_f16_nt_splitk_plan, gemm_f16_nt_splitk, gemm_f16_nt_splitk_with_config = _s
 gemm_f16_nn_splitk_plan, gemm_f16_nn_splitk, gemm_f16_nn_splitk_with_config = _splitk_fns("nn")
 gemm_f16_tn_splitk_plan, gemm_f16_tn_splitk, gemm_f16_tn_splitk_with_config = _splitk_fns("tn")
 gemm_f16_tt_splitk_plan, gemm_f16_tt_splitk, gemm_f16_tt_splitk_with_config = _splitk_fns("tt")
+
+
+def gemm_f16_nt_splitk_noalloc(M: int, N: int, K: int, A: int, B: int, C: int, splits: int,
+                               stream: int = 0) -> None:
+    """gemm_f16_nt_splitk with the partials in the library's fixed scratch
+    array: no workspace argument, no allocation (calls that overlap on one
+    GPU race)."""
+    _check(load().gemm_f16_nt_splitk_noalloc(M, N, K, A, B, C, splits, stream),
+           "gemm_f16_nt_splitk_noalloc")
 
 
 def gemm_f16_device_cus() -> int:

@@ -1903,9 +1903,13 @@ static int plan_layout(int32_t layout, int64_t M, int64_t N, int64_t K, int32_t 
     return GEMM_F16_OK;
 }
 
+// fixed_scratch: the workspace is the library's own fixed-size scratch array
+// (gemm_f16_nt_splitk_noalloc), so a plan that needs more of it than it
+// holds is reported as GEMM_F16_SCRATCH_LIMIT rather than as a bad argument.
 static int run_splitk(int32_t layout, int64_t M, int64_t N, int64_t K, const void *A,
                       const void *B, void *C, int32_t splits, void *workspace,
-                      int64_t workspace_bytes, hipStream_t stream, int32_t config_id)
+                      int64_t workspace_bytes, hipStream_t stream, int32_t config_id,
+                      bool fixed_scratch = false)
 {
     const int v = validate(M, N, K, A, B, C);
     if (v != GEMM_F16_OK) return v;
@@ -1937,7 +1941,8 @@ static int run_splitk(int32_t layout, int64_t M, int64_t N, int64_t K, const voi
     if (plan.tiles * eff > INT32_MAX) return GEMM_F16_UNSUPPORTED;
     const int64_t stride = split_stride(M, N);
     const int64_t need = eff * stride * 4;
-    if (!workspace || workspace_bytes < need) return GEMM_F16_INVALID_ARG;
+    if (!workspace || workspace_bytes < need)
+        return fixed_scratch ? GEMM_F16_SCRATCH_LIMIT : GEMM_F16_INVALID_ARG;
     if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0) return GEMM_F16_UNSUPPORTED;
     if (overlaps(workspace, need, A, M * K * 2) || overlaps(workspace, need, B, N * K * 2) ||
         overlaps(workspace, need, C, M * N * 2))
@@ -1965,6 +1970,43 @@ static int run_splitk(int32_t layout, int64_t M, int64_t N, int64_t K, const voi
                                            dim3(static_cast<uint32_t>(rgrid)), dim3(256), args, 0,
                                            stream);
     return err == hipSuccess ? GEMM_F16_OK : GEMM_F16_LAUNCH_FAILED;
+}
+
+// ---------------------------------------------------------------------------
+// Split over K without allocation: the fp32 partials in a fixed array
+// ---------------------------------------------------------------------------
+// For callers that cannot allocate device memory (code under HIP graph
+// capture, tight serving loops, harnesses that forbid it), the partials of
+// gemm_f16_nt_splitk_noalloc live in this file-scope device array.  Each GPU
+// the library runs on holds its own copy, at its own address, for as long as
+// the process lives.  In host code `scratch` names a host-side stand-in, not
+// device memory: kernels get the device address that hipGetSymbolAddress
+// returns for the current device, fetched once per device.
+constexpr int64_t kScratchBytes = int64_t(64) << 20;
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+struct ScratchInfo {
+    std::once_flag once;
+    void *ptr = nullptr;
+    hipError_t err = hipSuccess;
+};
+static ScratchInfo g_scratch[kMaxDevices];
+
+// The current device's copy of `scratch` (with that device current).
+static int scratch_address(void **out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return GEMM_F16_LAUNCH_FAILED;
+    ScratchInfo &d = g_scratch[dev];
+    std::call_once(d.once, [&] {
+        void *q = nullptr;
+        d.err = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+        d.ptr = q;
+    });
+    if (d.err != hipSuccess || !d.ptr) return GEMM_F16_LAUNCH_FAILED;
+    *out = d.ptr;
+    return GEMM_F16_OK;
 }
 
 // ---------------------------------------------------------------------------
@@ -2138,6 +2180,8 @@ extern "C" const char *gemm_f16_nt_status_string(int status)
     case GEMM_F16_INVALID_ARG: return "invalid argument";
     case GEMM_F16_UNSUPPORTED: return "unsupported argument";
     case GEMM_F16_LAUNCH_FAILED: return "HIP launch failed";
+    case GEMM_F16_SCRATCH_LIMIT:
+        return "the planned split-K partials exceed the no-allocation scratch (64 MiB)";
     default: return "unknown status";
     }
 }
@@ -2292,6 +2336,20 @@ extern "C" int gemm_f16_nt_splitk_with_config(int64_t M, int64_t N, int64_t K, c
 {
     return run_splitk(0, M, N, K, A, B, C, splits, workspace, workspace_bytes, stream,
                       config_id < 0 ? -1 : config_id);
+}
+
+extern "C" int gemm_f16_nt_splitk_noalloc(int64_t M, int64_t N, int64_t K, const void *A,
+                                          const void *B, void *C, int32_t splits,
+                                          hipStream_t stream)
+{
+    // argument errors first, before the device is touched
+    const int v = validate(M, N, K, A, B, C);
+    if (v != GEMM_F16_OK) return v;
+    if (splits > kMaxSplits) return GEMM_F16_INVALID_ARG;
+    void *ws = nullptr;
+    const int s = scratch_address(&ws);
+    if (s != GEMM_F16_OK) return s;
+    return run_splitk(0, M, N, K, A, B, C, splits, ws, kScratchBytes, stream, -1, true);
 }
 
 extern "C" int gemm_f16_nn_splitk_plan(int64_t M, int64_t N, int64_t K, int32_t num_cus,

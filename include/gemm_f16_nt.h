@@ -47,7 +47,10 @@ enum {
     /* the HIP runtime reported an error for the kernel launch (the status
      * hipLaunchKernel returns; the thread's last-error state is left as it
      * was) or when querying the current device */
-    GEMM_F16_LAUNCH_FAILED = 3
+    GEMM_F16_LAUNCH_FAILED = 3,
+    /* gemm_f16_nt_splitk_noalloc only: the planned fp32 partials need more
+     * than the library's fixed 64 MiB scratch array */
+    GEMM_F16_SCRATCH_LIMIT = 4
 };
 
 /*
@@ -267,6 +270,26 @@ int gemm_f16_nt_splitk_with_config(int64_t M, int64_t N, int64_t K,
                                    int32_t splits, void *workspace,
                                    int64_t workspace_bytes, hipStream_t stream,
                                    int32_t config_id);
+
+/*
+ * gemm_f16_nt_splitk_noalloc: gemm_f16_nt_splitk for callers that cannot
+ * allocate device memory -- code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.  It takes no workspace: the fp32
+ * partials go to a fixed array inside the library (64 MiB per GPU, held by
+ * each GPU the library runs on until the process ends), and the call itself
+ * allocates nothing.  Same plan, kernels and result bits as
+ * gemm_f16_nt_splitk(M, N, K, A, B, C, splits, <workspace>, ..., stream)
+ * with a large enough workspace, and the same status codes, plus
+ * GEMM_F16_SCRATCH_LIMIT when the planned partials (the workspace bytes
+ * gemm_f16_nt_splitk_plan reports) exceed 64 MiB: pass a smaller `splits`.
+ * The array needs no clearing (every partial it holds is written before it
+ * is read), but every call on one GPU shares it: calls that may overlap on
+ * one GPU (different streams, or other host threads) race, and must be
+ * ordered by the caller, e.g. on one stream.
+ */
+int gemm_f16_nt_splitk_noalloc(int64_t M, int64_t N, int64_t K,
+                               const void *A, const void *B, void *C,
+                               int32_t splits, hipStream_t stream);
 
 /*
  * The split over K for the other layouts: the same semantics, planner,
