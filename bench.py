@@ -141,30 +141,107 @@ def power_sampler_loop() -> int:
     return 0
 
 
-def power_summary(proc, t0: float, t1: float):
-    """Stop the sampler process and summarise its samples taken in [t0, t1]."""
+def power_windows(proc, windows):
+    """Stop the sampler process and summarise its samples taken in each
+    window [t0, t1] of `windows` (None for a window without samples)."""
     proc.terminate()
     try:
         out, _ = proc.communicate(timeout=15)
     except Exception:
         proc.kill()
         out, _ = proc.communicate()
-    pw, ck = [], []
-    for line in out.splitlines():
-        parts = line.split()
-        if len(parts) == 3 and t0 <= float(parts[0]) <= t1:
-            pw.append(float(parts[1]))
-            ck.append(float(parts[2]))
-    if not pw:
-        return None
     import statistics
 
-    return {"samples": len(pw), "socket_power_w_median": statistics.median(pw),
-            "socket_power_w_avg": round(sum(pw) / len(pw), 1),
-            "socket_power_w_min": min(pw), "socket_power_w_max": max(pw),
-            "gfx_clock_mhz_median": statistics.median(ck),
-            "gfx_clock_mhz_avg": round(sum(ck) / len(ck), 1), "gfx_clock_mhz_min": min(ck),
-            "gfx_clock_mhz_max": max(ck), "source": "amd-smi metric -p -c, every 0.5 s"}
+    samples = [tuple(float(x) for x in line.split()) for line in out.splitlines()
+               if len(line.split()) == 3]
+    res = []
+    for t0, t1 in windows:
+        pw = [p for t, p, _ in samples if t0 <= t <= t1]
+        ck = [c for t, _, c in samples if t0 <= t <= t1]
+        if not pw:
+            res.append(None)
+            continue
+        res.append({"samples": len(pw), "socket_power_w_median": statistics.median(pw),
+                    "socket_power_w_avg": round(sum(pw) / len(pw), 1),
+                    "socket_power_w_min": min(pw), "socket_power_w_max": max(pw),
+                    "gfx_clock_mhz_median": statistics.median(ck),
+                    "gfx_clock_mhz_avg": round(sum(ck) / len(ck), 1), "gfx_clock_mhz_min": min(ck),
+                    "gfx_clock_mhz_max": max(ck), "source": "amd-smi metric -p -c, every 0.5 s"})
+    return res
+
+
+def power_summary(proc, t0: float, t1: float):
+    """Stop the sampler process and summarise its samples taken in [t0, t1]."""
+    return power_windows(proc, [(t0, t1)])[0]
+
+
+def mfma_ceiling(args, sampler) -> int:
+    """The GEMM's inner loop without memory traffic (libgemm_f16_calib.so):
+    16x16x32 fp16 MFMAs fed by LDS fragment reads at one wave per SIMD, 4x4
+    and 8x8 result blocks per wave, random and constant operands.  For each,
+    --warmup-ms of launches, then a window of --ceiling-ms; prints one JSON
+    line with TFLOP/s (and socket power and GFX clock with --power-sample).
+    The random-operand rate is what the board's power limit leaves for the
+    GEMM's MFMA work; the GEMM's rate over it is the share it attains."""
+    import ctypes
+
+    import torch
+
+    from dense_fp16_gemm_amd import build as libbuild
+
+    if not os.path.exists(libbuild.CALIB_PATH):
+        print(f"bench.py: {libbuild.CALIB_PATH} is missing (build first)", file=sys.stderr)
+        return 1
+    lib = ctypes.CDLL(libbuild.CALIB_PATH)
+    fn = lib.gemm_f16_calib_mfma_loop
+    i32 = ctypes.c_int32
+    fn.argtypes = [i32, i32, i32, i32, ctypes.c_void_p, ctypes.c_void_p]
+    fn.restype = ctypes.c_int
+    dev = torch.device("cuda:0")
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    out_buf = torch.empty(cus * 256, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    rows, windows = [], []
+    for fb in (8, 4):
+        for constant in (0, 1):
+            iters = max(1, int(4000 * 64 / (fb * fb)))   # about 20 ms per launch at 1.5 PF/s
+            flops = 2.0 * 16 * 16 * 32 * 8 * fb * fb * iters * 4 * cus
+
+            def launch():
+                st = fn(fb, constant, iters, cus, out_buf.data_ptr(), stream.cuda_stream)
+                if st != 0:
+                    raise RuntimeError(f"gemm_f16_calib_mfma_loop returned {st}")
+
+            e0.record(stream)
+            launch()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            one = max(e0.elapsed_time(e1), 1e-3)
+            for _ in range(max(1, int(args.warmup_ms / one))):
+                launch()
+            torch.cuda.synchronize()
+            n = max(3, int(args.ceiling_ms / one))
+            t0 = time.time()
+            e0.record(stream)
+            for _ in range(n):
+                launch()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            windows.append((t0, time.time()))
+            ms = e0.elapsed_time(e1) / n
+            rows.append({"blocks_per_wave": f"{fb}x{fb}", "mfma_per_ds_read": fb * fb // (2 * fb),
+                         "operands": "constant" if constant else "random",
+                         "launches": n, "ms_per_launch": round(ms, 4),
+                         "tflops": round(flops / (ms * 1e-3) / 1e12, 1)})
+            print(f"bench.py: ceiling {rows[-1]}", file=sys.stderr, flush=True)
+    if sampler is not None:
+        for r, pw in zip(rows, power_windows(sampler, windows)):
+            r["power"] = pw
+    print(json.dumps({"calibration": "mfma_ceiling", "unit": "TFLOP/s",
+                      "peak": PEAK_FP16_TFLOPS, "cus": cus, "rows": rows}), flush=True)
+    return 0
 
 
 def run_repeats(args) -> int:
@@ -238,6 +315,12 @@ def main() -> int:
                          "protocol; the line is the median one's (1: measure in this process)")
     ap.add_argument("--child", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--power-sampler-loop", action="store_true", help=argparse.SUPPRESS)
+    ap.add_argument("--mfma-ceiling", action="store_true",
+                    help="instead of the GEMM, time the GEMM's MFMA + LDS-read inner loop "
+                         "without memory traffic, random and constant operands (the power "
+                         "ceiling of its MFMA work)")
+    ap.add_argument("--ceiling-ms", type=float, default=2000.0,
+                    help="timed window per --mfma-ceiling case")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead of the GEMM, run a plain device copy of this many bytes "
                          "(calibrates the HBM byte counters)")
@@ -250,7 +333,7 @@ def main() -> int:
         return 2
     if args.power_sampler_loop:
         return power_sampler_loop()
-    if args.repeat > 1 and not args.child and args.copy_bytes <= 0:
+    if args.repeat > 1 and not args.child and args.copy_bytes <= 0 and not args.mfma_ceiling:
         return run_repeats(args)
     sampler = None
     if args.power_sample:
@@ -275,6 +358,8 @@ def main() -> int:
         return 1
     if args.copy_bytes > 0:
         return copy_probe(args)
+    if args.mfma_ceiling:
+        return mfma_ceiling(args, sampler)
     name = args.workload or workloads.HEADLINE
     w = workloads.ALL_WORKLOADS[name]
     dev = torch.device("cuda:0")

@@ -1093,6 +1093,172 @@ void gemm_f16_nt_kernel(Params p)
 }
 
 // ---------------------------------------------------------------------------
+// Kernel, producer and consumer waves
+// ---------------------------------------------------------------------------
+// The pages' later kernels give the loads to a producer warp and the MMAs to
+// consumer warp groups (page "3. Warp Specialization", Why a Separate
+// Producer Warp and Producer-Consumer Barriers; page "4. Pipeline Abstraction
+// and Two Consumer Warp Groups", Pipeline Abstraction).  Here WAVES consumer
+// waves compute the tile as the kernel above does, and as many producer
+// waves only issue the direct-to-LDS DMA, so a DMA instruction that waits for
+// the texture addresser never holds up an MFMA stream.  Waves w and
+// w + WAVES share a SIMD: two waves per SIMD, so every wave has at most 256
+// registers, and a consumer's wave tile is held to 128 accumulators (a
+// 256 x 128 tile over four waves).  CDNA has no per-role register split, so
+// the producers get 256 registers too.
+//
+// Ring of three stages, one s_barrier per K-slice taken by every wave as
+// both handshakes.  Before barrier g
+//   * every producer has issued slice g + 2 (into the stage that slice g - 1
+//     held, freed by barrier g - 1) and waited (vmcnt) until its part of
+//     slice g + 1 has landed: after the barrier slice g + 1 is "full";
+//   * every consumer has all fragments of slice g in registers (lgkmcnt):
+//     after the barrier its stage is "empty".
+// A consumer takes barrier g before the last K step of slice g, whose
+// fragments are already in registers, so its MFMAs cover the barrier and the
+// reads of slice g + 1.  The producers run two slices ahead through the
+// workgroup's whole tile sequence, so the next tile's first slices load
+// while this tile's epilogue stores C (straight from the MFMA layout: every
+// stage is in use by then).
+__device__ __forceinline__ void wg_barrier()
+{
+    asm volatile("s_barrier" : : : "memory");
+}
+
+template <class CF>
+__global__ __launch_bounds__(2 * CF::THREADS)
+__attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemm_f16_nt_pc_kernel(Params p)
+{
+    static_assert(CF::STAGES == 3 && CF::MI == 16 && CF::ADB && CF::KK == 2 && CF::DX == 0 &&
+                      CF::AL == 0 && CF::BL == 0,
+                  "three stages, 16x16x32 MFMAs with both fragments double-buffered, two K "
+                  "steps per slice, NT operands");
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[CF::LDS_BYTES];
+    constexpr int L = CF::LOADS;   // DMA instructions per producer wave per slice
+    const int32_t wg = blockIdx.x;
+    if (wg >= p.tiles) return;
+    const int KT = (p.K + CF::BK - 1) / CF::BK;
+    const uint32_t row_pitch = static_cast<uint32_t>(p.K) * 2u;
+    const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(smem));
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+    if (wave >= CF::WAVES) {
+        // ---- producer: slices in the workgroup's tile order, two ahead ----
+        if (KT == 0) return;   // nothing to load; the consumers store zeros
+        const int pw = wave - CF::WAVES;
+        const int lane = threadIdx.x & 63;
+        constexpr int NV = CF::A_LOADS > CF::B_LOADS ? CF::A_LOADS : CF::B_LOADS;
+        uint32_t dvoff[NV];
+#pragma unroll
+        for (int i = 0; i < NV; ++i) dvoff[i] = dma_lane_offset<CF>(i, pw, lane, row_pitch);
+        int32_t cslot = wg;   // the next slice to issue: tile cslot, slice ckt
+        int ckt = 0;
+        Tile ct = make_tile<CF, false>(p, cslot, row_pitch);
+        auto issue = [&](int stage) {
+            if ((ckt + 1) * CF::BK <= p.K) {
+                // wholly inside K: the K offset rides in the scalar offset
+                const uint32_t koff = static_cast<uint32_t>(ckt) * CF::BK * 2u;
+#pragma unroll
+                for (int i = 0; i < L; ++i)
+                    dma_full<CF>(ct, dvoff[i < CF::A_LOADS ? i : i - CF::A_LOADS], koff, stage, i,
+                                 lds0, pw);
+            } else {
+#pragma unroll
+                for (int i = 0; i < L; ++i)
+                    dma_one<CF>(p, ct, stage, ckt, i, lds0, pw, lane, row_pitch);
+            }
+            if (++ckt == KT) {
+                ckt = 0;
+                cslot += p.grid;
+                if (cslot < p.tiles) ct = make_tile<CF, false>(p, cslot, row_pitch);
+            }
+        };
+        issue(0);
+        if (cslot < p.tiles) {
+            issue(1);
+            wait_vmcnt<L>();   // slice 0 landed
+        } else {
+            wait_vmcnt<0>();
+        }
+        wg_barrier();
+        int ps = 2;   // stage of the next slice issued
+        for (int32_t slot = wg; slot < p.tiles; slot += p.grid) {
+            for (int kt = 0; kt < KT; ++kt) {
+                if (cslot < p.tiles) {
+                    issue(ps);
+                    ps = ps == 2 ? 0 : ps + 1;
+                    wait_vmcnt<L>();   // the slice after the consumers' current one landed
+                } else {
+                    wait_vmcnt<0>();
+                }
+                wg_barrier();
+            }
+        }
+        return;
+    }
+
+    // ---- consumer ----
+    const WaveCtx<CF> w(p);
+    half8_t af[2][CF::FM], bf[2][CF::FN];
+    auto read_a = [&](int buf, int stage, int kk, int i) {
+        af[buf][i] = *reinterpret_cast<const half8_t *>(smem + stage * CF::STAGE_BYTES +
+                                                        w.frag_off[i & 1][kk] + w.a_frag_base +
+                                                        i * CF::MI * CF::ROW_BYTES);
+    };
+    auto read_b = [&](int buf, int stage, int kk, int j) {
+        bf[buf][j] = *reinterpret_cast<const half8_t *>(smem + stage * CF::STAGE_BYTES +
+                                                        w.frag_off[j & 1][kk] + w.b_frag_base +
+                                                        j * CF::MI * CF::ROW_BYTES);
+    };
+    auto none = [](int) {};
+    if (KT > 0) {
+        lds_barrier();   // slice 0 is full
+#pragma unroll
+        for (int i = 0; i < CF::FM; ++i) read_a(0, 0, 0, i);
+#pragma unroll
+        for (int j = 0; j < CF::FN; ++j) read_b(0, 0, 0, j);
+    }
+    int cs = 0;   // stage of the consumers' current slice
+    for (int32_t slot = wg; slot < p.tiles; slot += p.grid) {
+        typename CF::Acc acc[CF::FM][CF::FN];
+        zero_acc<CF>(acc);
+        // the zeros are in the AGPRs before the wait states that separate
+        // their (VALU) writes from the first MFMA reading them
+#pragma unroll
+        for (int i = 0; i < CF::FM; ++i)
+#pragma unroll
+            for (int j = 0; j < CF::FN; ++j) acc_fence<CF>(acc[i][j]);
+        asm volatile("s_nop 4");
+        for (int kt = 0; kt < KT; ++kt) {
+            const int ns = cs == 2 ? 0 : cs + 1;
+            // step 0 of slice kt, reading step 1's fragments
+            auto ra1 = [&](int i) { read_a(1, cs, 1, i); };
+            auto rb1 = [&](int j) { read_b(1, cs, 1, j); };
+            Step<CF, 0>::run(acc, af[0], bf[0], ra1, rb1, none);
+            // this slice's stage is read; the next slice has landed
+            lds_barrier();
+            // step 1, reading step 0's fragments of the next slice (after the
+            // workgroup's last slice: stale data, never used)
+            auto ra0 = [&](int i) { read_a(0, ns, 0, i); };
+            auto rb0 = [&](int j) { read_b(0, ns, 0, j); };
+            Step<CF, 0>::run(acc, af[1], bf[1], ra0, rb0, none);
+            cs = ns;
+        }
+        // 24 wait states between the last MFMA and the first read of its
+        // accumulators (as in the kernel above)
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
+        int32_t tile_m, tile_n;
+        grouped_tile(slot_to_linear(slot, p.grid, p.tiles, p.xcds), p.tiles_m, p.tiles_n,
+                     p.swizzle, tile_m, tile_n);
+        Tile t;
+        t.m0 = tile_m * CF::BM;
+        t.n0 = tile_n * CF::BN;
+        store_tile<CF>(p, t, acc, w.wave_m, w.wave_n, w.lane);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Split-K reduction
 // ---------------------------------------------------------------------------
 // C = fp16_rne(W_0 + W_1 + ... + W_{splits-1}), summed in fp32 in split order,
@@ -1363,6 +1529,16 @@ KernelEntry entry(int swizzle, float rate, float split_rate)
                        swizzle, rate, split_rate, CF::STAGED_OK ? 1 : 0, 0, 1, 2 * CF::AL + CF::BL};
 }
 
+// The producer/consumer kernel: twice the waves of CF (consumers and
+// producers), no split-K instance and no staged epilogue.
+template <class CF>
+KernelEntry entry_pc(int swizzle, float rate)
+{
+    return KernelEntry{reinterpret_cast<const void *>(&gemm_f16_nt_pc_kernel<CF>), nullptr,
+                       CF::BM, CF::BN, CF::BK, 2 * CF::WAVES, CF::STAGES, CF::LDS_BYTES,
+                       2 * CF::THREADS, swizzle, rate, 0.0f, 0, 0, 1, 0};
+}
+
 template <class CF, int LA = 0, int LB = 0>
 KernelEntry entry_general(int swizzle)
 {
@@ -1441,13 +1617,20 @@ static const KernelEntry kKernels[] = {
     entry<Cfg<64, 128, 64, 2, 2, 6, 16, 0, 0, 0, 0, 1>>(8, 0.66f, 0.299f),     // 39
     entry<Cfg<64, 128, 64, 2, 2, 6, 16, 0, 0, 0, 1, 1>>(8, 0.645f, 0.216f),    // 40
     entry<Cfg<128, 64, 64, 2, 2, 6, 16, 0, 0, 0, 1, 1>>(8, 0.66f, 0.217f),     // 41
-    // 42-44: the general kernel for NN, TT and TN (loads along the operand's
+    // 42: 256x128x64, three stages, four consumer waves of 128x64 (16x16x32
+    // MFMAs, both fragments double-buffered) and four producer waves that
+    // only issue the DMA (gemm_f16_nt_pc_kernel).  Faster than 2 and 19, the
+    // same tile with every wave loading, on every shape measured (8192^3:
+    // 814 against 937 and 857 us), so it takes 2's place in the plain planner;
+    // 2 stays the split planner's 256 x 128 unit (42 has no split instance)
+    entry_pc<Cfg<256, 128, 64, 2, 2, 3, 16, 0, 0, 1>>(8, 0.87f),
+    // 43-45: the general kernel for NN, TT and TN (loads along the operand's
     // contiguous dimension), for arguments the direct-to-LDS kernels of those
     // layouts cannot take
     entry_general<Cfg<128, 128, 32, 2, 2, 2>, 0, 1>(8),
     entry_general<Cfg<128, 128, 32, 2, 2, 2>, 1, 0>(8),
     entry_general<Cfg<128, 128, 32, 2, 2, 2>, 1, 1>(8),
-    // 45: the general kernel, 4 waves of 64x64, two register-staged buffers of
+    // 46: the general kernel, 4 waves of 64x64, two register-staged buffers of
     // K 32; planned only when the direct-to-LDS path cannot run
     entry_general<Cfg<128, 128, 32, 2, 2, 2>>(8),
 };

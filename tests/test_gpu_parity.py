@@ -111,7 +111,7 @@ def test_parity_every_config(g, oracle_mod, shape):
                 assert_bit_exact(got, first, f"{shape} config {cid} epilogue {epi} vs first")
 
 
-@pytest.mark.parametrize("cid", [0, 1, 2, 3, 4, 5, 9, 11, 17, 18, 19, 20, 21, 22, 23])
+@pytest.mark.parametrize("cid", [0, 1, 2, 3, 4, 5, 9, 11, 17, 18, 19, 20, 21, 22, 23, 42])
 @pytest.mark.parametrize("k", [8, 24, 32, 40, 64, 72, 128, 136, 160, 192, 200, 256, 264, 328])
 def test_short_and_ragged_k(g, oracle_mod, cid, k):
     """K with fewer slices than stages, exactly the stages, one more, and
@@ -121,7 +121,7 @@ def test_short_and_ragged_k(g, oracle_mod, cid, k):
     assert_within_tolerance(got, oracle_mod.gemm(a, b), f"k={k} config {cid}")
 
 
-@pytest.mark.parametrize("cid", [0, 2, 4, 5, 11, 17, 18, 19, 20, 21, 22, 23])
+@pytest.mark.parametrize("cid", [0, 2, 4, 5, 11, 17, 18, 19, 20, 21, 22, 23, 42])
 def test_edge_m_n(g, oracle_mod, cid):
     info = g.gemm_f16_nt_config_info(cid)
     bm, bn = info.block_m, info.block_n
@@ -143,10 +143,11 @@ def test_unaligned_c(g, oracle_mod, c_offset, epi, cid):
     assert_within_tolerance(got, oracle_mod.gemm(a, b), f"c_offset {c_offset} epilogue {epi}")
 
 
-def test_k_zero_writes_positive_zero(g):
+@pytest.mark.parametrize("cid", [None, 11, 42])
+def test_k_zero_writes_positive_zero(g, cid):
     a = np.zeros((70, 0), np.float16)
     b = np.zeros((90, 0), np.float16)
-    got = run_gpu(g, a, b)
+    got = run_gpu(g, a, b, config=cid)
     assert np.all(got.view(np.uint16) == 0)
 
 
