@@ -1119,13 +1119,27 @@ void gemm_f16_nt_kernel(Params p)
 // reads of slice g + 1.  The producers run two slices ahead through the
 // workgroup's whole tile sequence, so the next tile's first slices load
 // while this tile's epilogue stores C (straight from the MFMA layout: every
-// stage is in use by then).
+// stage is in use by then).  SPLIT: the same over (K range, tile) work units
+// (see Params), each storing fp32 partials; units may differ in K length, and
+// both roles count every unit's slices alike.
 __device__ __forceinline__ void wg_barrier()
 {
     asm volatile("s_barrier" : : : "memory");
 }
 
-template <class CF>
+// K slices of the work unit in persistent slot `slot`
+template <class CF, bool SPLIT>
+__device__ __forceinline__ int unit_slices(const Params &p, int32_t slot)
+{
+    int32_t klen = p.K;
+    if constexpr (SPLIT) {
+        const int32_t split = slot_to_linear(slot, p.grid, p.tiles, p.xcds) / (p.tiles_m * p.tiles_n);
+        klen = min(p.k_split, p.K - split * p.k_split);
+    }
+    return (klen + CF::BK - 1) / CF::BK;
+}
+
+template <class CF, bool SPLIT>
 __global__ __launch_bounds__(2 * CF::THREADS)
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_f16_nt_pc_kernel(Params p)
@@ -1138,7 +1152,7 @@ void gemm_f16_nt_pc_kernel(Params p)
     constexpr int L = CF::LOADS;   // DMA instructions per producer wave per slice
     const int32_t wg = blockIdx.x;
     if (wg >= p.tiles) return;
-    const int KT = (p.K + CF::BK - 1) / CF::BK;
+    const int KT = (p.K + CF::BK - 1) / CF::BK;   // 0 only for K = 0 (never split)
     const uint32_t row_pitch = static_cast<uint32_t>(p.K) * 2u;
     const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(smem));
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1152,11 +1166,12 @@ void gemm_f16_nt_pc_kernel(Params p)
         uint32_t dvoff[NV];
 #pragma unroll
         for (int i = 0; i < NV; ++i) dvoff[i] = dma_lane_offset<CF>(i, pw, lane, row_pitch);
-        int32_t cslot = wg;   // the next slice to issue: tile cslot, slice ckt
+        int32_t cslot = wg;   // the next slice to issue: unit cslot, slice ckt
         int ckt = 0;
-        Tile ct = make_tile<CF, false>(p, cslot, row_pitch);
+        Tile ct = make_tile<CF, SPLIT>(p, cslot, row_pitch);
+        int ckts = (ct.klen + CF::BK - 1) / CF::BK;
         auto issue = [&](int stage) {
-            if ((ckt + 1) * CF::BK <= p.K) {
+            if ((ckt + 1) * CF::BK <= ct.klen) {
                 // wholly inside K: the K offset rides in the scalar offset
                 const uint32_t koff = static_cast<uint32_t>(ckt) * CF::BK * 2u;
 #pragma unroll
@@ -1168,10 +1183,13 @@ void gemm_f16_nt_pc_kernel(Params p)
                 for (int i = 0; i < L; ++i)
                     dma_one<CF>(p, ct, stage, ckt, i, lds0, pw, lane, row_pitch);
             }
-            if (++ckt == KT) {
+            if (++ckt == ckts) {
                 ckt = 0;
                 cslot += p.grid;
-                if (cslot < p.tiles) ct = make_tile<CF, false>(p, cslot, row_pitch);
+                if (cslot < p.tiles) {
+                    ct = make_tile<CF, SPLIT>(p, cslot, row_pitch);
+                    ckts = (ct.klen + CF::BK - 1) / CF::BK;
+                }
             }
         };
         issue(0);
@@ -1184,7 +1202,8 @@ void gemm_f16_nt_pc_kernel(Params p)
         wg_barrier();
         int ps = 2;   // stage of the next slice issued
         for (int32_t slot = wg; slot < p.tiles; slot += p.grid) {
-            for (int kt = 0; kt < KT; ++kt) {
+            const int kts = unit_slices<CF, SPLIT>(p, slot);
+            for (int kt = 0; kt < kts; ++kt) {
                 if (cslot < p.tiles) {
                     issue(ps);
                     ps = ps == 2 ? 0 : ps + 1;
@@ -1230,7 +1249,8 @@ void gemm_f16_nt_pc_kernel(Params p)
 #pragma unroll
             for (int j = 0; j < CF::FN; ++j) acc_fence<CF>(acc[i][j]);
         asm volatile("s_nop 4");
-        for (int kt = 0; kt < KT; ++kt) {
+        const int kts = KT > 0 ? unit_slices<CF, SPLIT>(p, slot) : 0;
+        for (int kt = 0; kt < kts; ++kt) {
             const int ns = cs == 2 ? 0 : cs + 1;
             // step 0 of slice kt, reading step 1's fragments
             auto ra1 = [&](int i) { read_a(1, cs, 1, i); };
@@ -1248,13 +1268,11 @@ void gemm_f16_nt_pc_kernel(Params p)
         // 24 wait states between the last MFMA and the first read of its
         // accumulators (as in the kernel above)
         asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
-        int32_t tile_m, tile_n;
-        grouped_tile(slot_to_linear(slot, p.grid, p.tiles, p.xcds), p.tiles_m, p.tiles_n,
-                     p.swizzle, tile_m, tile_n);
-        Tile t;
-        t.m0 = tile_m * CF::BM;
-        t.n0 = tile_n * CF::BN;
-        store_tile<CF>(p, t, acc, w.wave_m, w.wave_n, w.lane);
+        const Tile t = make_tile<CF, SPLIT>(p, slot, w.row_pitch);
+        if constexpr (SPLIT)
+            store_tile_f32<CF>(p, t, acc, w.wave_m, w.wave_n, w.lane);
+        else
+            store_tile<CF>(p, t, acc, w.wave_m, w.wave_n, w.lane);
     }
 }
 
@@ -1530,13 +1548,14 @@ KernelEntry entry(int swizzle, float rate, float split_rate)
 }
 
 // The producer/consumer kernel: twice the waves of CF (consumers and
-// producers), no split-K instance and no staged epilogue.
+// producers), no staged epilogue.
 template <class CF>
-KernelEntry entry_pc(int swizzle, float rate)
+KernelEntry entry_pc(int swizzle, float rate, float split_rate)
 {
-    return KernelEntry{reinterpret_cast<const void *>(&gemm_f16_nt_pc_kernel<CF>), nullptr,
+    return KernelEntry{reinterpret_cast<const void *>(&gemm_f16_nt_pc_kernel<CF, false>),
+                       reinterpret_cast<const void *>(&gemm_f16_nt_pc_kernel<CF, true>),
                        CF::BM, CF::BN, CF::BK, 2 * CF::WAVES, CF::STAGES, CF::LDS_BYTES,
-                       2 * CF::THREADS, swizzle, rate, 0.0f, 0, 0, 1, 0};
+                       2 * CF::THREADS, swizzle, rate, split_rate, 0, 0, 1, 0};
 }
 
 template <class CF, int LA = 0, int LB = 0>
@@ -1621,9 +1640,9 @@ static const KernelEntry kKernels[] = {
     // MFMAs, both fragments double-buffered) and four producer waves that
     // only issue the DMA (gemm_f16_nt_pc_kernel).  Faster than 2 and 19, the
     // same tile with every wave loading, on every shape measured (8192^3:
-    // 814 against 937 and 857 us), so it takes 2's place in the plain planner;
-    // 2 stays the split planner's 256 x 128 unit (42 has no split instance)
-    entry_pc<Cfg<256, 128, 64, 2, 2, 3, 16, 0, 0, 1>>(8, 0.87f),
+    // 814 against 937 and 857 us), so it takes 2's place in both planners
+    // (split_rate: 2's scaled by the unsplit gain at 2048 x 4096 x 8192, 1.11)
+    entry_pc<Cfg<256, 128, 64, 2, 2, 3, 16, 0, 0, 1>>(8, 0.87f, 0.79f),
     // 43-45: the general kernel for NN, TT and TN (loads along the operand's
     // contiguous dimension), for arguments the direct-to-LDS kernels of those
     // layouts cannot take

@@ -365,11 +365,12 @@ def test_splitk_plan_layouts(g, lay):
 
 def test_splitk_plan_of_the_underfilled_workload(g):
     # The benchmark's split-K workload (1024 x 1024 x 65536: sixteen 256 x 256
-    # tiles for 256 CUs) is planned as configuration 2 (256 x 128 tiles) over
-    # 8 K ranges of 8192: 256 units, one round.  A change to the cost model
-    # or the split candidates that moves this plan shows up here.
+    # tiles for 256 CUs) is planned as configuration 42 (256 x 128 tiles,
+    # producer and consumer waves) over 8 K ranges of 8192: 256 units, one
+    # round.  A change to the cost model or the split candidates that moves
+    # this plan shows up here.
     plan, splits, ws = g.gemm_f16_nt_splitk_plan(1024, 1024, 65536, 256, 0)
-    assert (plan.config_id, splits) == (2, 8)
+    assert (plan.config_id, splits) == (42, 8)
     assert ws == 8 * 1024 * 1024 * 4
     assert plan.tiles * splits == 256 and plan.grid == 256
 

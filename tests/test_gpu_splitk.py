@@ -76,7 +76,7 @@ def test_splitk_parity(g, oracle_mod, shape, splits, dist, seed):
     assert_within_tolerance(got, oracle_mod.gemm(a, b), f"splitk {shape} splits {splits}")
 
 
-@pytest.mark.parametrize("config", [None, 2, 4, 9, 11, 18, 21, 22, 23])
+@pytest.mark.parametrize("config", [None, 2, 4, 9, 11, 18, 21, 22, 23, 42])
 def test_splitk_integer_bit_exact(g, oracle_mod, config):
     a, b = workloads.make_inputs(200, 300, 6152, "int2", 1.0, seed=311)
     got, eff = run_splitk(g, a, b, 6, config=config)
