@@ -456,6 +456,27 @@ __device__ __forceinline__ void dma_full(const Tile &t, uint32_t voff, uint32_t 
                  : "v"(voff), "s"(is_a ? t.rsrc_a : t.rsrc_b), "s"(koff), "{m0}"(lds));
 }
 
+// The operands of one fast-form DMA instruction, for issue fused with an
+// MFMA (Step with FUSED): lane offset, buffer resource, scalar offset and the
+// LDS address that goes in M0.
+struct DmaOp {
+    uint32_t voff;
+    i32x4_t rsrc;
+    uint32_t soff;
+    uint32_t m0;
+};
+
+template <class CF>
+__device__ __forceinline__ DmaOp dma_full_op(const Tile &t, uint32_t voff, uint32_t koff, int stage,
+                                             int i, uint32_t lds0, int wave)
+{
+    const bool is_a = i < CF::A_LOADS;
+    const int rblk = (is_a ? i : i - CF::A_LOADS) * CF::WAVES + wave;
+    return DmaOp{voff, is_a ? t.rsrc_a : t.rsrc_b, koff,
+                 lds0 + stage * CF::STAGE_BYTES + (is_a ? 0 : CF::A_BYTES) +
+                     rblk * CF::DMA_ROWS * CF::ROW_BYTES};
+}
+
 // All DMA instructions of one slice, back to back (prefill only).
 template <class CF>
 __device__ __forceinline__ void dma_slice(const Params &p, const Tile &t, int stage, int kt,
@@ -477,7 +498,10 @@ __device__ __forceinline__ void dma_slice(const Params &p, const Tile &t, int st
 //     earliest point its register is free (single-buffered), or, when A is
 //     double-buffered, over the first half of the step like B;
 //   * NLD global DMA instructions over the whole step, so the vector-memory
-//     queue drains between them instead of stalling the wave.
+//     queue drains between them instead of stalling the wave.  FUSED (16x16
+//     MFMAs, ld(w) returning a DmaOp): the M0 write, the MFMA and the DMA go
+//     out as one statement, so the MFMA is the wait state the M0 write needs
+//     before an LDS DMA and no s_nop takes an issue slot of the wave.
 // sched_barrier(0) after each MFMA group keeps the compiler from regrouping.
 //
 // The 16x16x32 MFMA goes through inline assembly with its accumulator bound
@@ -487,7 +511,7 @@ __device__ __forceinline__ void dma_slice(const Params &p, const Tile &t, int st
 // kernel supplies the wait states the ISA requires around them itself: after
 // the accumulators are zeroed (VALU write, then MFMA reads them) and before
 // they are read back (MFMA write, then VALU read); see the kernel body.
-template <class CF, int NLD>
+template <class CF, int NLD, bool FUSED = false>
 struct Step {
     template <class RdA, class RdB, class Ld>
     __device__ __forceinline__ static void run(typename CF::Acc (&acc)[CF::FM][CF::FN],
@@ -506,11 +530,32 @@ struct Step {
                                   : t / CF::FN;
             const int j = CF::ADB ? t / CF::FM
                                   : ((i & 1) ? CF::FN - 1 - t % CF::FN : t % CF::FN);
-            if constexpr (CF::MI == 32)
+            // the DMA instruction of this slot, if any (one at most: NLD <= NM)
+            int dw = -1;
+#pragma unroll
+            for (int w = 0; w < NLD; ++w)
+                if ((w * NM) / NLD == t) dw = w;
+            if constexpr (FUSED) {
+                static_assert(CF::MI == 16 && NLD <= NM, "fused DMA: hand-issued MFMAs, one DMA per slot");
+                if (dw >= 0) {
+                    const DmaOp op = ld(dw);
+                    asm volatile("s_mov_b32 m0, %5\n\t"
+                                 "v_mfma_f32_16x16x32_f16 %0, %1, %2, %0\n\t"
+                                 "buffer_load_dwordx4 %3, %4, %6 offen lds"
+                                 : "+a"(acc[i][j])
+                                 : "v"(bf[j]), "v"(af[i]), "v"(op.voff), "s"(op.rsrc), "s"(op.m0),
+                                   "s"(op.soff)
+                                 : "m0");
+                } else {
+                    asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0"
+                                 : "+a"(acc[i][j]) : "v"(bf[j]), "v"(af[i]));
+                }
+            } else if constexpr (CF::MI == 32) {
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[j], af[i], acc[i][j], 0, 0, 0);
-            else
+            } else {
                 asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0"
                              : "+a"(acc[i][j]) : "v"(bf[j]), "v"(af[i]));
+            }
 #pragma unroll
             for (int w = 0; w < CF::FN; ++w)
                 if ((w * RSPAN) / CF::FN == t) rdb(w);
@@ -521,10 +566,8 @@ struct Step {
             } else {
                 if (t % CF::FN == CF::FN - 1) rda(i);
             }
-            if constexpr (NLD > 0) {
-#pragma unroll
-                for (int w = 0; w < NLD; ++w)
-                    if ((w * NM) / NLD == t) ld(w);
+            if constexpr (NLD > 0 && !FUSED) {
+                if (dw >= 0) ld(dw);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -1009,6 +1052,28 @@ void gemm_f16_nt_kernel(Params p)
                     } else
                         dma_one<CF>(p, cur, rd, kt + 2, d, lds0, w.wave, w.lane, w.row_pitch);
                 };
+                // the same DMA as operands, for issue fused with an MFMA
+                auto dma_early_op = [&](int d) -> DmaOp {
+                    const uint32_t kslice = static_cast<uint32_t>(kt + 2) * CF::BK;
+                    if (d < CF::A_LOADS) {
+                        if constexpr (CF::AL == 1)
+                            return dma_full_op<CF>(cur, dvoffa[d % CF::A_NB],
+                                                   (kslice + static_cast<uint32_t>(d / CF::A_NB) *
+                                                                 CF::A_NB * CF::A_RB) * lda,
+                                                   rd, d, lds0, w.wave);
+                        else
+                            return dma_full_op<CF>(cur, dvoff[d], kslice * 2, rd, d, lds0, w.wave);
+                    } else {
+                        const int db = d - CF::A_LOADS;
+                        if constexpr (CF::BL == 1)
+                            return dma_full_op<CF>(cur, dvoffb[db % CF::B_NB],
+                                                   (kslice + static_cast<uint32_t>(db / CF::B_NB) *
+                                                                 CF::B_NB * CF::B_RB) * ldb,
+                                                   rd, d, lds0, w.wave);
+                        else
+                            return dma_full_op<CF>(cur, dvoff[db], kslice * 2, rd, d, lds0, w.wave);
+                    }
+                };
                 if (kk + 1 < KK) {
                     auto ra = [&](int i) { read_a(CF::ADB ? (kk + 1) & 1 : 0, rd, kk + 1, i); };
                     auto rb = [&](int j) { read_b((kk + 1) & 1, rd, kk + 1, j); };
@@ -1029,7 +1094,10 @@ void gemm_f16_nt_kernel(Params p)
                     lds_barrier();
                     auto ra = [&](int i) { read_a(0, rd_next, 0, i); };
                     auto rb = [&](int j) { read_b(0, rd_next, 0, j); };
-                    if constexpr (DX > 0)
+                    if constexpr (DX > 0 && FAST && CF::MI == 16)
+                        Step<CF, DX, true>::run(acc, af[CF::ADB ? kk & 1 : 0], bf[kk & 1], ra, rb,
+                                                dma_early_op);
+                    else if constexpr (DX > 0)
                         Step<CF, DX>::run(acc, af[CF::ADB ? kk & 1 : 0], bf[kk & 1], ra, rb, dma_early);
                     else if (kk < DSTEPS)
                         Step<CF, DPS>::run(acc, af[CF::ADB ? kk & 1 : 0], bf[kk & 1], ra, rb, dma);
