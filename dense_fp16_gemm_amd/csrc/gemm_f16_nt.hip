@@ -816,6 +816,11 @@ struct WaveCtx {
         // the fragment XOR 32 j (j < TN / 16) touches chunk bits below
         // log2(TN / 8); the wave's offset, a multiple of TN / 8 chunks, lies
         // above them when TN is a power of two
+        // the fragment XOR (bits 5..8) and the offsets added to the bases
+        // before it (multiples of 512) never share a bit
+        static_assert(CF::STAGE_BYTES % 512 == 0 && CF::A_BYTES % 512 == 0 &&
+                          32 * CF::FN <= 512 && 32 * CF::FM <= 512,
+                      "stage and tile offsets clear of the fragment XOR");
         if constexpr (CF::BL == 1) {
             static_assert(CF::TN >= 32 && (CF::TN & (CF::TN - 1)) == 0,
                           "wave column offset clear of the XOR bits");
@@ -914,9 +919,12 @@ void gemm_f16_nt_kernel(Params p)
                                                         w.frag_off[i & 1][kk] + w.a_frag_base +
                                                         i * CF::MI * CF::ROW_BYTES);
         } else {
+            // the stage's offset joins the base before the XOR (see read_b)
             uint32_t off;
-            asm volatile("v_xor_b32 %0, %2, %1" : "=v"(off) : "v"(w.atr0), "n"(32 * i));
-            const uint8_t *q = smem + stage * CF::STAGE_BYTES + off + kk * 32 * CF::A_ROW_BYTES;
+            asm volatile("v_xor_b32 %0, %2, %1"
+                         : "=v"(off)
+                         : "v"(w.atr0 + static_cast<uint32_t>(stage) * CF::STAGE_BYTES), "n"(32 * i));
+            const uint8_t *q = smem + off + kk * 32 * CF::A_ROW_BYTES;
             const half4_t lo = lds_read_tr16(q);
             const half4_t hi = lds_read_tr16(q + 4 * CF::A_ROW_BYTES);
             af[buf][i] = half8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -930,11 +938,19 @@ void gemm_f16_nt_kernel(Params p)
         } else {
             // the XOR is issued at the read (an asm the compiler cannot hoist):
             // hoisted, the FN offsets would each hold a register for the
-            // whole loop
+            // whole loop.  The stage's and the A tile's offsets (multiples of
+            // 1 KB) join the base before the XOR, which touches bits 5..8
+            // only: (x + c) ^ 32 j = (x ^ 32 j) + c.  The XOR result then
+            // addresses the reads directly (the K step's offset fits their
+            // immediate), with no vector add after the asm -- which the
+            // compiler would separate from it by a wait state, not knowing
+            // what the asm computes.
             uint32_t off;
-            asm volatile("v_xor_b32 %0, %2, %1" : "=v"(off) : "v"(w.btr0), "n"(32 * j));
-            const uint8_t *q = smem + stage * CF::STAGE_BYTES + CF::A_BYTES + off +
-                               kk * 32 * CF::B_ROW_BYTES;
+            asm volatile("v_xor_b32 %0, %2, %1"
+                         : "=v"(off)
+                         : "v"(w.btr0 + CF::A_BYTES + static_cast<uint32_t>(stage) * CF::STAGE_BYTES),
+                           "n"(32 * j));
+            const uint8_t *q = smem + off + kk * 32 * CF::B_ROW_BYTES;
             const half4_t lo = lds_read_tr16(q);
             const half4_t hi = lds_read_tr16(q + 4 * CF::B_ROW_BYTES);
             bf[buf][j] = half8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
