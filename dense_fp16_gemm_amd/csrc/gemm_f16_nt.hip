@@ -1900,7 +1900,8 @@ static int64_t split_k_len(int id, int64_t K, int32_t splits)
 
 // Estimated time of configuration `id` with K split `splits` ways, a model
 // fitted to measured times of every configuration and split count on 28
-// shapes per layout (under-filled grids, long and short K; one MI355X):
+// shapes per layout (under-filled grids, long and short K; one MI355X; the
+// tables and the fit are in planner_fit/, beside this directory):
 //   compute  rounds of the persistent grid x (one unit's MFMA work at the
 //            configuration's split_rate of a CU's dense fp16 peak + a fixed
 //            cost per unit)
