@@ -227,6 +227,18 @@ struct Cfg {
     static constexpr int B_NB = (16 / (B_RB < 16 ? B_RB : 16)) < B_LOADS
                                     ? (16 / (B_RB < 16 ? B_RB : 16)) : B_LOADS;
     static constexpr int LOADS = A_LOADS + B_LOADS;
+    // K-contiguous parts in the fused early refill (Step with FUSED): a
+    // wave's DMA instructions fill consecutive 1 KB LDS blocks in groups of
+    // DMA_G (dma_block), so a group shares one M0 value and the instruction's
+    // immediate offset, which moves the LDS and the global address alike,
+    // steps through it; DMA_G divides the instruction count of every
+    // K-contiguous part (1, the plain interleaving, elsewhere)
+    static constexpr int A_KL = AL ? 4 : A_LOADS;
+    static constexpr int B_KL = BL ? 4 : B_LOADS;
+    static constexpr bool FUSED_REFILL = STAGES_ == 2 && DX_ == A_LOADS + B_LOADS && MI_ == 16;
+    static constexpr int DMA_G = !FUSED_REFILL ? 1
+                                 : (A_KL % 4 == 0 && B_KL % 4 == 0) ? 4
+                                 : (A_KL % 2 == 0 && B_KL % 2 == 0) ? 2 : 1;
     // the LDS-staged epilogue writes one block row of every wave (WM * MI tile
     // rows of BN halves, rows padded by 16 bytes) into one ring stage
     static constexpr bool STAGED_OK = WM * MI * (BN * 2 + 16) <= STAGE_BYTES;
@@ -374,6 +386,17 @@ __device__ __forceinline__ int kn_swizzle_of(int r)
         return 0;
 }
 
+// The LDS block (DMA_ROWS rows, 1 KB) that DMA instruction ip of a
+// K-contiguous part fills for wave `wave`: groups of DMA_G consecutive
+// blocks per wave, the groups of the waves interleaved (with DMA_G = 1,
+// instruction ip of every wave in turn).  Parts stored k-outermost keep
+// ip * WAVES + wave.
+template <class CF>
+__host__ __device__ constexpr int dma_block(int ip, int wave)
+{
+    return (ip / CF::DMA_G) * (CF::DMA_G * CF::WAVES) + wave * CF::DMA_G + ip % CF::DMA_G;
+}
+
 // One of this wave's DMA instructions for K-slice `kt` of tile `t`, into ring
 // stage `stage`.  Instruction i fills rows R = (i' * WAVES + wave) * DMA_ROWS
 // .. R + DMA_ROWS - 1 of the A tile (i < A_LOADS, i' = i) or of the B tile
@@ -403,13 +426,14 @@ __device__ __forceinline__ void dma_one(const Params &p, const Tile &t, int stag
               lds0 + stage * CF::STAGE_BYTES + (is_a ? 0 : CF::A_BYTES) + rblk * DMA_BYTES);
         return;
     }
-    const int row = rblk * CF::DMA_ROWS + lane / CF::CHUNKS;
+    const int kb = dma_block<CF>(is_a ? i : i - CF::A_LOADS, wave);
+    const int row = kb * CF::DMA_ROWS + lane / CF::CHUNKS;
     const int chunk = (lane % CF::CHUNKS) ^ chunk_swizzle<CF::CHUNKS, CF::MI>(row);
     uint32_t v = static_cast<uint32_t>(row) * row_pitch + chunk * 16 + k0 * 2;
     if (k0 + chunk * 8 >= static_cast<uint32_t>(t.klen)) v = OOB_OFFSET;
     dma16(is_a ? t.rsrc_a : t.rsrc_b, v,
           lds0 + stage * CF::STAGE_BYTES + (is_a ? 0 : CF::A_BYTES) +
-              rblk * CF::DMA_ROWS * CF::ROW_BYTES);
+              kb * CF::DMA_ROWS * CF::ROW_BYTES);
 }
 
 // Fast form of dma_one for a slice that lies wholly inside K: the lane's
@@ -422,8 +446,7 @@ __device__ __forceinline__ void dma_one(const Params &p, const Tile &t, int stag
 template <class CF>
 __device__ __forceinline__ uint32_t dma_lane_offset(int ip, int wave, int lane, uint32_t row_pitch)
 {
-    const int rblk = ip * CF::WAVES + wave;
-    const int row = rblk * CF::DMA_ROWS + lane / CF::CHUNKS;
+    const int row = dma_block<CF>(ip, wave) * CF::DMA_ROWS + lane / CF::CHUNKS;
     const int chunk = (lane % CF::CHUNKS) ^ chunk_swizzle<CF::CHUNKS, CF::MI>(row);
     return static_cast<uint32_t>(row) * row_pitch + chunk * 16;
 }
@@ -448,7 +471,9 @@ __device__ __forceinline__ void dma_full(const Tile &t, uint32_t voff, uint32_t 
                                          int i, uint32_t lds0, int wave)
 {
     const bool is_a = i < CF::A_LOADS;
-    const int rblk = (is_a ? i : i - CF::A_LOADS) * CF::WAVES + wave;
+    const int ip = is_a ? i : i - CF::A_LOADS;
+    const bool kn = is_a ? CF::AL == 1 : CF::BL == 1;
+    const int rblk = kn ? ip * CF::WAVES + wave : dma_block<CF>(ip, wave);
     const uint32_t lds = lds0 + stage * CF::STAGE_BYTES + (is_a ? 0 : CF::A_BYTES) +
                          rblk * CF::DMA_ROWS * CF::ROW_BYTES;
     asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
@@ -464,17 +489,27 @@ struct DmaOp {
     i32x4_t rsrc;
     uint32_t soff;
     uint32_t m0;
+    int imm;   // the instruction's immediate offset: 0, 1024, 2048 or 3072
 };
 
 template <class CF>
 __device__ __forceinline__ DmaOp dma_full_op(const Tile &t, uint32_t voff, uint32_t koff, int stage,
                                              int i, uint32_t lds0, int wave)
 {
+    // For a K-contiguous part, `voff` is the lane's offset already lowered
+    // by the group position's immediate offset (see the kernel), so the
+    // global address and the bounds check (lane offset + immediate) are
+    // those of the plain form, while the LDS address steps through the
+    // group from one M0 value.
     const bool is_a = i < CF::A_LOADS;
-    const int rblk = (is_a ? i : i - CF::A_LOADS) * CF::WAVES + wave;
+    const int ip = is_a ? i : i - CF::A_LOADS;
+    const bool kn = is_a ? CF::AL == 1 : CF::BL == 1;
+    const int rblk = kn ? ip * CF::WAVES + wave : dma_block<CF>(ip, wave);
+    const int j = kn ? 0 : ip % CF::DMA_G;
     return DmaOp{voff, is_a ? t.rsrc_a : t.rsrc_b, koff,
                  lds0 + stage * CF::STAGE_BYTES + (is_a ? 0 : CF::A_BYTES) +
-                     rblk * CF::DMA_ROWS * CF::ROW_BYTES};
+                     (rblk - j) * CF::DMA_ROWS * CF::ROW_BYTES,
+                 j * CF::DMA_ROWS * CF::ROW_BYTES};
 }
 
 // All DMA instructions of one slice, back to back (prefill only).
@@ -539,13 +574,22 @@ struct Step {
                 static_assert(CF::MI == 16 && NLD <= NM, "fused DMA: hand-issued MFMAs, one DMA per slot");
                 if (dw >= 0) {
                     const DmaOp op = ld(dw);
-                    asm volatile("s_mov_b32 m0, %5\n\t"
-                                 "v_mfma_f32_16x16x32_f16 %0, %1, %2, %0\n\t"
-                                 "buffer_load_dwordx4 %3, %4, %6 offen lds"
-                                 : "+a"(acc[i][j])
-                                 : "v"(bf[j]), "v"(af[i]), "v"(op.voff), "s"(op.rsrc), "s"(op.m0),
-                                   "s"(op.soff)
-                                 : "m0");
+                    // M0 is an operand, so a group's later DMAs reuse the
+                    // value already there; the immediate offset is a literal
+                    // of the instruction, one statement per value
+#define GEMM_F16_FUSED_DMA(IMM)                                                          \
+    asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0\n\t"                           \
+                 "buffer_load_dwordx4 %3, %4, %6 offen offset:" #IMM " lds"              \
+                 : "+a"(acc[i][j])                                                       \
+                 : "v"(bf[j]), "v"(af[i]), "v"(op.voff), "s"(op.rsrc), "{m0}"(op.m0),      \
+                   "s"(op.soff))
+                    switch (op.imm) {
+                    case 1024: GEMM_F16_FUSED_DMA(1024); break;
+                    case 2048: GEMM_F16_FUSED_DMA(2048); break;
+                    case 3072: GEMM_F16_FUSED_DMA(3072); break;
+                    default: GEMM_F16_FUSED_DMA(0); break;
+                    }
+#undef GEMM_F16_FUSED_DMA
                 } else {
                     asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0"
                                  : "+a"(acc[i][j]) : "v"(bf[j]), "v"(af[i]));
@@ -903,8 +947,15 @@ void gemm_f16_nt_kernel(Params p)
     constexpr int NA_K = CF::AL ? 0 : CF::A_LOADS, NB_K = CF::BL ? 0 : CF::B_LOADS;
     constexpr int NVOFF = !FAST_DMA ? 1 : (NA_K > NB_K ? NA_K : (NB_K > 0 ? NB_K : 1));
     uint32_t dvoff[NVOFF];
+    // In the fused early refill (16x16 MFMAs) a K-contiguous part's DMA at
+    // group position j carries the immediate offset 1024 j: its lane offset is
+    // lowered by as much (never below zero: the row of position j lies at
+    // least 8 j rows in, 8 j x 2K >= 1024 j bytes, and the fused refill runs
+    // only for K >= 192).
 #pragma unroll
-    for (int i = 0; i < NVOFF; ++i) dvoff[i] = dma_lane_offset<CF>(i, w.wave, w.lane, w.row_pitch);
+    for (int i = 0; i < NVOFF; ++i)
+        dvoff[i] = dma_lane_offset<CF>(i, w.wave, w.lane, w.row_pitch) -
+                   (FAST_DMA && CF::MI == 16 ? static_cast<uint32_t>(i % CF::DMA_G) * DMA_BYTES : 0u);
     uint32_t dvoffa[FAST_DMA && CF::AL ? CF::A_NB : 1];
     uint32_t dvoffb[FAST_DMA && CF::BL ? CF::B_NB : 1];
     const uint32_t lda = static_cast<uint32_t>(p.M) * 2u;   // [K, M] A row pitch
