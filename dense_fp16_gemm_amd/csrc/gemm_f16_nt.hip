@@ -337,14 +337,19 @@ __device__ __forceinline__ Tile make_tile(const Params &p, int32_t slot, uint32_
     int32_t k0 = 0;
     if constexpr (SPLIT) {
         const int32_t tiles_mn = p.tiles_m * p.tiles_n;
-        t.split = unit / tiles_mn;
+        t.split = static_cast<int32_t>(static_cast<uint32_t>(unit) / static_cast<uint32_t>(tiles_mn));
         grouped_tile(unit - t.split * tiles_mn, p.tiles_m, p.tiles_n, p.swizzle, tile_m, tile_n);
         k0 = t.split * p.k_split;
         t.klen = min(p.k_split, p.K - k0);
     } else {
         t.split = 0;
         grouped_tile(unit, p.tiles_m, p.tiles_n, p.swizzle, tile_m, tile_n);
+        // opaque, as the unit's K length is in the split instance: the lane
+        // masks of the K-tail checks (dma_one) are then computed per tile,
+        // not hoisted out of the tile loop to hold scalar registers
+        // throughout the kernel
         t.klen = p.K;
+        asm volatile("" : "+s"(t.klen));
     }
     t.m0 = tile_m * CF::BM;
     t.n0 = tile_n * CF::BN;
@@ -397,6 +402,29 @@ __host__ __device__ constexpr int dma_block(int ip, int wave)
     return (ip / CF::DMA_G) * (CF::DMA_G * CF::WAVES) + wave * CF::DMA_G + ip % CF::DMA_G;
 }
 
+// This wave's base LDS addresses for its DMA blocks: `kc` for the parts
+// stored K-contiguous (block dma_block(ip, wave) = wave * DMA_G + a constant),
+// `kn` for the parts stored k-outermost (block ip * WAVES + wave).  Every M0
+// value is one of these plus a constant.  The empty asm makes both opaque to
+// the optimiser, so each M0 value is computed from them where it is used: the
+// compiler cannot fold the wave's offset into a per-instruction constant and
+// hoist one scalar register per DMA instruction out of the tile loop, which
+// would hold them across the whole kernel.  Made once per tile (and again
+// for the next tile's prefill), it costs one scalar add per distinct M0.
+struct DmaLds {
+    uint32_t kc, kn;
+};
+
+template <class CF>
+__device__ __forceinline__ DmaLds dma_lds(uint32_t lds0, int wave)
+{
+    // the inputs are made opaque, so the wave's offsets are recomputed here
+    // too rather than held from the kernel's start
+    asm volatile("" : "+s"(lds0), "+s"(wave));
+    return DmaLds{lds0 + static_cast<uint32_t>(wave * CF::DMA_G) * DMA_BYTES,
+                  lds0 + static_cast<uint32_t>(wave) * DMA_BYTES};
+}
+
 // One of this wave's DMA instructions for K-slice `kt` of tile `t`, into ring
 // stage `stage`.  Instruction i fills rows R = (i' * WAVES + wave) * DMA_ROWS
 // .. R + DMA_ROWS - 1 of the A tile (i < A_LOADS, i' = i) or of the B tile
@@ -405,7 +433,7 @@ __host__ __device__ constexpr int dma_block(int ip, int wave)
 // chunk at or past K gets an offset beyond the resource and lands as zeros.
 template <class CF>
 __device__ __forceinline__ void dma_one(const Params &p, const Tile &t, int stage, int kt, int i,
-                                        uint32_t lds0, int wave, int lane, uint32_t row_pitch)
+                                        const DmaLds &lb, int wave, int lane, uint32_t row_pitch)
 {
     const uint32_t k0 = static_cast<uint32_t>(kt) * CF::BK;
     const bool is_a = i < CF::A_LOADS;
@@ -423,7 +451,8 @@ __device__ __forceinline__ void dma_one(const Params &p, const Tile &t, int stag
         uint32_t v = (k0 + r) * ld + chunk * 16;
         if (k0 + r >= static_cast<uint32_t>(t.klen) || x0 + chunk * 8 >= xn) v = OOB_OFFSET;
         dma16(is_a ? t.rsrc_a : t.rsrc_b, v,
-              lds0 + stage * CF::STAGE_BYTES + (is_a ? 0 : CF::A_BYTES) + rblk * DMA_BYTES);
+              lb.kn + stage * CF::STAGE_BYTES + (is_a ? 0 : CF::A_BYTES) +
+                  (rblk - wave) * DMA_BYTES);
         return;
     }
     const int kb = dma_block<CF>(is_a ? i : i - CF::A_LOADS, wave);
@@ -432,8 +461,8 @@ __device__ __forceinline__ void dma_one(const Params &p, const Tile &t, int stag
     uint32_t v = static_cast<uint32_t>(row) * row_pitch + chunk * 16 + k0 * 2;
     if (k0 + chunk * 8 >= static_cast<uint32_t>(t.klen)) v = OOB_OFFSET;
     dma16(is_a ? t.rsrc_a : t.rsrc_b, v,
-          lds0 + stage * CF::STAGE_BYTES + (is_a ? 0 : CF::A_BYTES) +
-              kb * CF::DMA_ROWS * CF::ROW_BYTES);
+          lb.kc + stage * CF::STAGE_BYTES + (is_a ? 0 : CF::A_BYTES) +
+              (kb - wave * CF::DMA_G) * DMA_BYTES);
 }
 
 // Fast form of dma_one for a slice that lies wholly inside K: the lane's
@@ -468,14 +497,15 @@ __device__ __forceinline__ uint32_t dma_lane_offset_kn(int ip, int wave, int lan
 
 template <class CF>
 __device__ __forceinline__ void dma_full(const Tile &t, uint32_t voff, uint32_t koff, int stage,
-                                         int i, uint32_t lds0, int wave)
+                                         int i, const DmaLds &lb)
 {
     const bool is_a = i < CF::A_LOADS;
     const int ip = is_a ? i : i - CF::A_LOADS;
     const bool kn = is_a ? CF::AL == 1 : CF::BL == 1;
-    const int rblk = kn ? ip * CF::WAVES + wave : dma_block<CF>(ip, wave);
-    const uint32_t lds = lds0 + stage * CF::STAGE_BYTES + (is_a ? 0 : CF::A_BYTES) +
-                         rblk * CF::DMA_ROWS * CF::ROW_BYTES;
+    // the block less the wave's own part, which the base carries
+    const int rblk = kn ? ip * CF::WAVES : dma_block<CF>(ip, 0);
+    const uint32_t lds = (kn ? lb.kn : lb.kc) + stage * CF::STAGE_BYTES + (is_a ? 0 : CF::A_BYTES) +
+                         rblk * DMA_BYTES;
     asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
                  :
                  : "v"(voff), "s"(is_a ? t.rsrc_a : t.rsrc_b), "s"(koff), "{m0}"(lds));
@@ -494,7 +524,7 @@ struct DmaOp {
 
 template <class CF>
 __device__ __forceinline__ DmaOp dma_full_op(const Tile &t, uint32_t voff, uint32_t koff, int stage,
-                                             int i, uint32_t lds0, int wave)
+                                             int i, const DmaLds &lb)
 {
     // For a K-contiguous part, `voff` is the lane's offset already lowered
     // by the group position's immediate offset (see the kernel), so the
@@ -504,21 +534,21 @@ __device__ __forceinline__ DmaOp dma_full_op(const Tile &t, uint32_t voff, uint3
     const bool is_a = i < CF::A_LOADS;
     const int ip = is_a ? i : i - CF::A_LOADS;
     const bool kn = is_a ? CF::AL == 1 : CF::BL == 1;
-    const int rblk = kn ? ip * CF::WAVES + wave : dma_block<CF>(ip, wave);
+    const int rblk = kn ? ip * CF::WAVES : dma_block<CF>(ip, 0);
     const int j = kn ? 0 : ip % CF::DMA_G;
     return DmaOp{voff, is_a ? t.rsrc_a : t.rsrc_b, koff,
-                 lds0 + stage * CF::STAGE_BYTES + (is_a ? 0 : CF::A_BYTES) +
-                     (rblk - j) * CF::DMA_ROWS * CF::ROW_BYTES,
-                 j * CF::DMA_ROWS * CF::ROW_BYTES};
+                 (kn ? lb.kn : lb.kc) + stage * CF::STAGE_BYTES + (is_a ? 0 : CF::A_BYTES) +
+                     (rblk - j) * DMA_BYTES,
+                 j * DMA_BYTES};
 }
 
 // All DMA instructions of one slice, back to back (prefill only).
 template <class CF>
 __device__ __forceinline__ void dma_slice(const Params &p, const Tile &t, int stage, int kt,
-                                          uint32_t lds0, int wave, int lane, uint32_t row_pitch)
+                                          const DmaLds &lb, int wave, int lane, uint32_t row_pitch)
 {
 #pragma unroll
-    for (int i = 0; i < CF::LOADS; ++i) dma_one<CF>(p, t, stage, kt, i, lds0, wave, lane, row_pitch);
+    for (int i = 0; i < CF::LOADS; ++i) dma_one<CF>(p, t, stage, kt, i, lb, wave, lane, row_pitch);
 }
 
 // Work of one MFMA K step, in a fixed issue order.  The wave owns one SIMD's
@@ -907,6 +937,18 @@ __device__ __forceinline__ void zero_acc(typename CF::Acc (&acc)[CF::FM][CF::FN]
 // ---------------------------------------------------------------------------
 // Kernel, direct-to-LDS fill
 // ---------------------------------------------------------------------------
+// The kernel's arguments, read afresh from the kernarg segment (Params is the
+// kernel's only argument and sits at its start).  The empty asm makes every
+// call a new pointer value, so the scalar loads of the fields used after it
+// are issued there: no field is held in a scalar register from the kernel's
+// start to its last use across every tile.
+__device__ __forceinline__ const Params &kernel_args()
+{
+    auto q = __builtin_amdgcn_kernarg_segment_ptr();
+    asm volatile("" : "+s"(q));
+    return *(const Params *)q;
+}
+
 template <class CF, bool SPLIT>
 __global__ __launch_bounds__(CF::THREADS)
 __attribute__((amdgpu_waves_per_eu(CF::WAVES_PER_SIMD, CF::WAVES_PER_SIMD)))
@@ -958,8 +1000,6 @@ void gemm_f16_nt_kernel(Params p)
                    (FAST_DMA && CF::MI == 16 ? static_cast<uint32_t>(i % CF::DMA_G) * DMA_BYTES : 0u);
     uint32_t dvoffa[FAST_DMA && CF::AL ? CF::A_NB : 1];
     uint32_t dvoffb[FAST_DMA && CF::BL ? CF::B_NB : 1];
-    const uint32_t lda = static_cast<uint32_t>(p.M) * 2u;   // [K, M] A row pitch
-    const uint32_t ldb = static_cast<uint32_t>(p.N) * 2u;   // [K, N] B row pitch
     const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(smem));
 
     half8_t af[CF::ADB ? 2 : 1][CF::FM], bf[2][CF::FN];
@@ -1019,19 +1059,26 @@ void gemm_f16_nt_kernel(Params p)
     // while slice 0 is computed.  Issued even when K has fewer slices (those
     // move no data), so every wait below counts the same instructions.
 #pragma unroll
-    for (int s = 0; s < S - 1; ++s) dma_slice<CF>(p, cur, s, s, lds0, w.wave, w.lane, w.row_pitch);
+    for (int s = 0; s < S - 1; ++s)
+        dma_slice<CF>(p, cur, s, s, dma_lds<CF>(lds0, w.wave), w.wave, w.lane, w.row_pitch);
 
     while (true) {
+        const Params pt = kernel_args();
+        const uint32_t lda = static_cast<uint32_t>(pt.M) * 2u;   // [K, M] A row pitch
+        const uint32_t ldb = static_cast<uint32_t>(pt.N) * 2u;   // [K, N] B row pitch
         const int KT = (cur.klen + CF::BK - 1) / CF::BK;   // slices of this unit
+        // this tile's DMA base addresses (see DmaLds), made opaque again at
+        // every slice below
+        DmaLds lt = dma_lds<CF>(lds0, w.wave);
         if constexpr (FAST_DMA && CF::AL == 1) {
 #pragma unroll
             for (int i = 0; i < CF::A_NB; ++i)
-                dvoffa[i] = dma_lane_offset_kn<CF, true>(i, w.wave, w.lane, cur.m0, p.M);
+                dvoffa[i] = dma_lane_offset_kn<CF, true>(i, w.wave, w.lane, cur.m0, pt.M);
         }
         if constexpr (FAST_DMA && CF::BL == 1) {
 #pragma unroll
             for (int i = 0; i < CF::B_NB; ++i)
-                dvoffb[i] = dma_lane_offset_kn<CF, false>(i, w.wave, w.lane, cur.n0, p.N);
+                dvoffb[i] = dma_lane_offset_kn<CF, false>(i, w.wave, w.lane, cur.n0, pt.N);
         }
         typename CF::Acc acc[CF::FM][CF::FN];
         zero_acc<CF>(acc);
@@ -1052,7 +1099,7 @@ void gemm_f16_nt_kernel(Params p)
             if constexpr (DX > 0) {
 #pragma unroll
                 for (int d = 0; d < DX; ++d)
-                    dma_one<CF>(p, cur, 1, 1, d, lds0, w.wave, w.lane, w.row_pitch);
+                    dma_one<CF>(pt, cur, 1, 1, d, lt, w.wave, w.lane, w.row_pitch);
             }
             // slice 0 landed (slices 1 .. S-2, and slice 1's early part, may
             // still be in flight).  After the staged epilogue of an interior
@@ -1084,13 +1131,17 @@ void gemm_f16_nt_kernel(Params p)
         int pst = S - 1;   // stage receiving slice kt + S - 1, freed before slice kt
         auto slice = [&](int kt, auto fast) {
             constexpr bool FAST = decltype(fast)::value;
+            // M0 values are computed from the bases where they are written
+            // (one scalar add into M0 each), not held in a scalar register
+            // per value across the loop
+            asm volatile("" : "+s"(lt.kc), "+s"(lt.kn));
             const int rd_next = rd + 1 == S ? 0 : rd + 1;
             const int pkt = kt + S - 1;
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) {
                 auto dma = [&](int d) {
                     if (kk * DPS + d < LY)
-                        dma_one<CF>(p, cur, pst, pkt, DX + kk * DPS + d, lds0, w.wave, w.lane,
+                        dma_one<CF>(pt, cur, pst, pkt, DX + kk * DPS + d, lt, w.wave, w.lane,
                                     w.row_pitch);
                 };
                 // early part of slice kt + 2, into stage rd, which the barrier
@@ -1103,21 +1154,21 @@ void gemm_f16_nt_kernel(Params p)
                                 dma_full<CF>(cur, dvoffa[d % CF::A_NB],
                                              (kslice + static_cast<uint32_t>(d / CF::A_NB) *
                                                            CF::A_NB * CF::A_RB) * lda,
-                                             rd, d, lds0, w.wave);
+                                             rd, d, lt);
                             else
-                                dma_full<CF>(cur, dvoff[d], kslice * 2, rd, d, lds0, w.wave);
+                                dma_full<CF>(cur, dvoff[d], kslice * 2, rd, d, lt);
                         } else {
                             const int db = d - CF::A_LOADS;
                             if constexpr (CF::BL == 1)
                                 dma_full<CF>(cur, dvoffb[db % CF::B_NB],
                                              (kslice + static_cast<uint32_t>(db / CF::B_NB) *
                                                            CF::B_NB * CF::B_RB) * ldb,
-                                             rd, d, lds0, w.wave);
+                                             rd, d, lt);
                             else
-                                dma_full<CF>(cur, dvoff[db], kslice * 2, rd, d, lds0, w.wave);
+                                dma_full<CF>(cur, dvoff[db], kslice * 2, rd, d, lt);
                         }
                     } else
-                        dma_one<CF>(p, cur, rd, kt + 2, d, lds0, w.wave, w.lane, w.row_pitch);
+                        dma_one<CF>(pt, cur, rd, kt + 2, d, lt, w.wave, w.lane, w.row_pitch);
                 };
                 // the same DMA as operands, for issue fused with an MFMA
                 auto dma_early_op = [&](int d) -> DmaOp {
@@ -1127,18 +1178,18 @@ void gemm_f16_nt_kernel(Params p)
                             return dma_full_op<CF>(cur, dvoffa[d % CF::A_NB],
                                                    (kslice + static_cast<uint32_t>(d / CF::A_NB) *
                                                                  CF::A_NB * CF::A_RB) * lda,
-                                                   rd, d, lds0, w.wave);
+                                                   rd, d, lt);
                         else
-                            return dma_full_op<CF>(cur, dvoff[d], kslice * 2, rd, d, lds0, w.wave);
+                            return dma_full_op<CF>(cur, dvoff[d], kslice * 2, rd, d, lt);
                     } else {
                         const int db = d - CF::A_LOADS;
                         if constexpr (CF::BL == 1)
                             return dma_full_op<CF>(cur, dvoffb[db % CF::B_NB],
                                                    (kslice + static_cast<uint32_t>(db / CF::B_NB) *
                                                                  CF::B_NB * CF::B_RB) * ldb,
-                                                   rd, d, lds0, w.wave);
+                                                   rd, d, lt);
                         else
-                            return dma_full_op<CF>(cur, dvoff[db], kslice * 2, rd, d, lds0, w.wave);
+                            return dma_full_op<CF>(cur, dvoff[db], kslice * 2, rd, d, lt);
                     }
                 };
                 if (kk + 1 < KK) {
@@ -1202,26 +1253,28 @@ void gemm_f16_nt_kernel(Params p)
         // tile's prefill may start, and it flies while this tile is stored.
         wait_vmcnt<0>();
         lds_barrier();
-        const int32_t next = slot + p.grid;
+        const Params pe = kernel_args();
+        const int32_t next = slot + pe.grid;
         Tile nxt;
-        if (next < p.tiles) {
-            nxt = make_tile<CF, SPLIT>(p, next, w.row_pitch);
+        if (next < pe.tiles) {
+            nxt = make_tile<CF, SPLIT>(pe, next, w.row_pitch);
 #pragma unroll
             for (int s = 0; s < S - 1; ++s)
-                dma_slice<CF>(p, nxt, s, s, lds0, w.wave, w.lane, w.row_pitch);
+                dma_slice<CF>(pe, nxt, s, s, dma_lds<CF>(lds0, w.wave), w.wave, w.lane, w.row_pitch);
         }
+        const Params pc = kernel_args();
         if constexpr (SPLIT) {
-            store_tile_f32<CF>(p, cur, acc, w.wave_m, w.wave_n, w.lane);
+            store_tile_f32<CF>(pc, cur, acc, w.wave_m, w.wave_n, w.lane);
         } else if constexpr (CF::STAGED_OK) {
-            if (p.staged)
-                store_tile_staged<CF>(p, cur, acc, w.wave_m, w.wave_n, w.lane, smem);
+            if (pc.staged)
+                store_tile_staged<CF>(pc, cur, acc, w.wave_m, w.wave_n, w.lane, smem);
             else
-                store_tile<CF>(p, cur, acc, w.wave_m, w.wave_n, w.lane);
-            prev_interior = p.staged && cur.m0 + CF::BM <= p.M && cur.n0 + CF::BN <= p.N;
+                store_tile<CF>(pc, cur, acc, w.wave_m, w.wave_n, w.lane);
+            prev_interior = pc.staged && cur.m0 + CF::BM <= pc.M && cur.n0 + CF::BN <= pc.N;
         } else {
-            store_tile<CF>(p, cur, acc, w.wave_m, w.wave_n, w.lane);
+            store_tile<CF>(pc, cur, acc, w.wave_m, w.wave_n, w.lane);
         }
-        if (next >= p.tiles) break;
+        if (next >= pc.tiles) break;
         slot = next;
         cur = nxt;
     }
@@ -1268,7 +1321,9 @@ __device__ __forceinline__ int unit_slices(const Params &p, int32_t slot)
 {
     int32_t klen = p.K;
     if constexpr (SPLIT) {
-        const int32_t split = slot_to_linear(slot, p.grid, p.tiles, p.xcds) / (p.tiles_m * p.tiles_n);
+        const int32_t split = static_cast<int32_t>(
+            static_cast<uint32_t>(slot_to_linear(slot, p.grid, p.tiles, p.xcds)) /
+            static_cast<uint32_t>(p.tiles_m * p.tiles_n));
         klen = min(p.k_split, p.K - split * p.k_split);
     }
     return (klen + CF::BK - 1) / CF::BK;
@@ -1301,6 +1356,7 @@ void gemm_f16_nt_pc_kernel(Params p)
         uint32_t dvoff[NV];
 #pragma unroll
         for (int i = 0; i < NV; ++i) dvoff[i] = dma_lane_offset<CF>(i, pw, lane, row_pitch);
+        const DmaLds plb = dma_lds<CF>(lds0, pw);
         int32_t cslot = wg;   // the next slice to issue: unit cslot, slice ckt
         int ckt = 0;
         Tile ct = make_tile<CF, SPLIT>(p, cslot, row_pitch);
@@ -1312,11 +1368,11 @@ void gemm_f16_nt_pc_kernel(Params p)
 #pragma unroll
                 for (int i = 0; i < L; ++i)
                     dma_full<CF>(ct, dvoff[i < CF::A_LOADS ? i : i - CF::A_LOADS], koff, stage, i,
-                                 lds0, pw);
+                                 plb);
             } else {
 #pragma unroll
                 for (int i = 0; i < L; ++i)
-                    dma_one<CF>(p, ct, stage, ckt, i, lds0, pw, lane, row_pitch);
+                    dma_one<CF>(p, ct, stage, ckt, i, plb, pw, lane, row_pitch);
             }
             if (++ckt == ckts) {
                 ckt = 0;

@@ -35,32 +35,40 @@
 namespace gemm_f16 {
 
 // Linear tile id -> (tile_m, tile_n) with raster groups `swizzle` columns wide.
+// Every argument is non-negative; the arithmetic is unsigned, which spares
+// the device code the sign handling of signed division.
 GEMM_F16_HD inline void grouped_tile(int32_t linear, int32_t tiles_m, int32_t tiles_n,
                                      int32_t swizzle, int32_t &tile_m, int32_t &tile_n)
 {
-    const int32_t per_group = tiles_m * swizzle;
-    const int32_t group = linear / per_group;
-    const int32_t in_group = linear - group * per_group;
-    const int32_t first_n = group * swizzle;
-    const int32_t rest = tiles_n - first_n;
-    const int32_t width = rest < swizzle ? rest : swizzle;
-    tile_m = in_group / width;
-    tile_n = first_n + (in_group - tile_m * width);
+    const uint32_t sw = static_cast<uint32_t>(swizzle);
+    const uint32_t per_group = static_cast<uint32_t>(tiles_m) * sw;
+    const uint32_t lin = static_cast<uint32_t>(linear);
+    const uint32_t group = lin / per_group;
+    const uint32_t in_group = lin - group * per_group;
+    const uint32_t first_n = group * sw;
+    const uint32_t rest = static_cast<uint32_t>(tiles_n) - first_n;
+    const uint32_t width = rest < sw ? rest : sw;
+    const uint32_t tm = in_group / width;
+    tile_m = static_cast<int32_t>(tm);
+    tile_n = static_cast<int32_t>(first_n + (in_group - tm * width));
 }
 
 // Persistent slot (round * grid + wg) -> linear tile id, XCD-contiguous.
 GEMM_F16_HD inline int32_t slot_to_linear(int32_t slot, int32_t grid, int32_t tiles,
                                           int32_t xcds)
 {
-    const int32_t round = slot / grid;
-    const int32_t wg = slot - round * grid;
-    const int32_t base = round * grid;
     if (xcds <= 1) return slot;
-    const int32_t n = tiles - base < grid ? tiles - base : grid;
-    const int32_t q = n / xcds;
-    const int32_t r = n - q * xcds;
-    const int32_t x = wg % xcds;
-    return base + x * q + (x < r ? x : r) + wg / xcds;
+    const uint32_t g = static_cast<uint32_t>(grid), xc = static_cast<uint32_t>(xcds);
+    const uint32_t sl = static_cast<uint32_t>(slot);
+    const uint32_t round = sl / g;
+    const uint32_t wg = sl - round * g;
+    const uint32_t base = round * g;
+    const uint32_t left = static_cast<uint32_t>(tiles) - base;
+    const uint32_t n = left < g ? left : g;
+    const uint32_t q = n / xc;
+    const uint32_t r = n - q * xc;
+    const uint32_t x = wg % xc;
+    return static_cast<int32_t>(base + x * q + (x < r ? x : r) + wg / xc);
 }
 
 }  // namespace gemm_f16
