@@ -763,8 +763,11 @@ constexpr int staged_stores()
 // LDS as fp16, as many as the stage holds per round, rows padded by 16 bytes
 // so that the 32 rows one write instruction touches fall in distinct banks;
 // after a barrier every thread stores 16-byte row segments, a wave covering
-// 512 consecutive columns.  Masked at M and N.  A barrier ends each round
-// before the buffer is reused.
+// 512 consecutive columns.  A barrier ends each round before the buffer is
+// reused.  A tile wholly inside M x N (the common case, known for the whole
+// workgroup) takes a path with no per-item checks: a block row's LDS reads go
+// out back to back and its stores follow, so the reads' latencies overlap.
+// Other tiles check every item against M and N.
 template <class CF>
 __device__ __forceinline__ void store_tile_staged(const Params &p, const Tile &t,
                                                   typename CF::Acc (&acc)[CF::FM][CF::FN],
@@ -778,10 +781,17 @@ __device__ __forceinline__ void store_tile_staged(const Params &p, const Tile &t
     constexpr int R = CF::STAGE_BYTES / BROW < CF::FM ? CF::STAGE_BYTES / BROW : CF::FM;
     static_assert(R >= 1, "one block row per round at least");
     uint8_t *buf = smem + (CF::STAGES - 1) * CF::STAGE_BYTES;
+    // the thread's indices, opaque to the optimiser: the per-thread offsets
+    // derived from them are computed here for each tile, not hoisted to the
+    // kernel's start where they would hold registers through the K loop
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid), "+v"(lane));
     const int lrow = lane % CF::MI;
     const int lq = lane / CF::MI;
-    const int tid = threadIdx.x;
     constexpr int SEGS = CF::BN / 8;           // 8-column segments per row
+    constexpr int ITEMS_R = CROWS * SEGS;      // items (16-byte segments) per block row
+    constexpr int NI = (ITEMS_R + CF::THREADS - 1) / CF::THREADS;   // per thread
+    const bool interior = t.m0 + CF::BM <= p.M && t.n0 + CF::BN <= p.N;
 #pragma unroll
     for (int i0 = 0; i0 < CF::FM; i0 += R) {
         const int nr = CF::FM - i0 < R ? CF::FM - i0 : R;   // block rows this round
@@ -790,18 +800,29 @@ __device__ __forceinline__ void store_tile_staged(const Params &p, const Tile &t
             if (r < nr) {
                 const int i = i0 + r;
                 const int srow = wave_m * CF::MI + lrow;   // staged row of this lane
+                // one block row at a time: its accumulators are read out
+                // after the previous row's writes
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int j = 0; j < CF::FN; ++j) {
-                    acc_fence<CF>(acc[i][j]);
+                    // the block, copied into VGPRs by an empty volatile
+                    // statement: the copy comes after the wait states that
+                    // follow the last hand-issued MFMA (see the kernel), and
+                    // the compiler keeps the AGPRs where the MFMAs left them
+                    typename CF::Acc av;
+                    if constexpr (CF::MI == 16)
+                        asm volatile("" : "=v"(av) : "0"(acc[i][j]));
+                    else
+                        av = acc[i][j];
 #pragma unroll
                     for (int g = 0; g < CF::ACC_N / 4; ++g) {
                         const int ncol = wave_n * CF::TN + j * CF::MI +
                                          (CF::MI == 32 ? g * 8 + lq * 4 : lq * 4);
                         f32x4_t v;
-                        v.x = acc[i][j][4 * g + 0];
-                        v.y = acc[i][j][4 * g + 1];
-                        v.z = acc[i][j][4 * g + 2];
-                        v.w = acc[i][j][4 * g + 3];
+                        v.x = av[4 * g + 0];
+                        v.y = av[4 * g + 1];
+                        v.z = av[4 * g + 2];
+                        v.w = av[4 * g + 3];
                         *reinterpret_cast<half4_t *>(buf + r * BROW + srow * PITCH + ncol * 2) =
                             __builtin_convertvector(v, half4_t);
                     }
@@ -809,37 +830,66 @@ __device__ __forceinline__ void store_tile_staged(const Params &p, const Tile &t
             }
         }
         lds_barrier();
-        // 16 bytes per lane at any 2-byte alignment: memcpy lets the compiler
-        // emit one 16-byte store, which the target's unaligned-access mode
-        // allows; only the segment crossing N is stored element by element.
-        // one block row's items at a time (a scheduling barrier between
-        // them keeps only those in registers)
-        constexpr int ITEMS_R = CROWS * SEGS;   // items per block row
+        // item cr of block row r: staged row sr = cr / SEGS, segment sc
+        auto row_of = [&](int r, int sr) {
+            return t.m0 + (sr / CF::MI) * CF::TM + (i0 + r) * CF::MI + sr % CF::MI;
+        };
+        if (interior) {
+            // per block row: its NI reads back to back, then its NI stores
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            if (r >= nr) break;
+            for (int r = 0; r < R; ++r) {
+                if (r >= nr) break;
+                half8_t h[NI];
 #pragma unroll
-            for (int it = 0; it < (ITEMS_R + CF::THREADS - 1) / CF::THREADS; ++it) {
-                const int cr = it * CF::THREADS + tid;
-                if (cr >= ITEMS_R) continue;
-                const int sr = cr / SEGS, sc = cr % SEGS;
-                const int32_t m = t.m0 + (sr / CF::MI) * CF::TM + (i0 + r) * CF::MI + sr % CF::MI;
-                const int32_t n = t.n0 + sc * 8;
-                if (m >= p.M || n >= p.N) continue;
-                const half8_t h =
-                    *reinterpret_cast<const half8_t *>(buf + r * BROW + sr * PITCH + sc * 16);
-                _Float16 *dst = reinterpret_cast<_Float16 *>(p.C) + static_cast<int64_t>(m) * p.N + n;
-                if (n + 8 <= p.N) {
+                for (int it = 0; it < NI; ++it) {
+                    const int cr = it * CF::THREADS + tid;
+                    if (ITEMS_R % CF::THREADS != 0 && cr >= ITEMS_R) continue;
+                    h[it] = *reinterpret_cast<const half8_t *>(buf + r * BROW + (cr / SEGS) * PITCH +
+                                                               (cr % SEGS) * 16);
+                }
+#pragma unroll
+                for (int it = 0; it < NI; ++it) {
+                    const int cr = it * CF::THREADS + tid;
+                    if (ITEMS_R % CF::THREADS != 0 && cr >= ITEMS_R) continue;
+                    const int32_t m = row_of(r, cr / SEGS);
+                    const int32_t n = t.n0 + (cr % SEGS) * 8;
+                    _Float16 *dst = reinterpret_cast<_Float16 *>(p.C) + static_cast<int64_t>(m) * p.N + n;
                     // non-temporal: C is written once, and left out of L2 it
                     // does not evict the A and B strips the XCD's tiles share
-                    __builtin_nontemporal_store(h, reinterpret_cast<half8_u_t *>(dst));
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        if (n + e < p.N) dst[e] = h[e];
+                    __builtin_nontemporal_store(h[it], reinterpret_cast<half8_u_t *>(dst));
                 }
+                __builtin_amdgcn_sched_barrier(0);
             }
-            __builtin_amdgcn_sched_barrier(0);
+        } else {
+            // 16 bytes per lane at any 2-byte alignment: memcpy lets the
+            // compiler emit one 16-byte store, which the target's
+            // unaligned-access mode allows; only the segment crossing N is
+            // stored element by element.  One block row's items at a time (a
+            // scheduling barrier between them keeps only those in registers)
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                if (r >= nr) break;
+#pragma unroll
+                for (int it = 0; it < NI; ++it) {
+                    const int cr = it * CF::THREADS + tid;
+                    if (cr >= ITEMS_R) continue;
+                    const int sr = cr / SEGS, sc = cr % SEGS;
+                    const int32_t m = row_of(r, sr);
+                    const int32_t n = t.n0 + sc * 8;
+                    if (m >= p.M || n >= p.N) continue;
+                    const half8_t h =
+                        *reinterpret_cast<const half8_t *>(buf + r * BROW + sr * PITCH + sc * 16);
+                    _Float16 *dst = reinterpret_cast<_Float16 *>(p.C) + static_cast<int64_t>(m) * p.N + n;
+                    if (n + 8 <= p.N) {
+                        __builtin_nontemporal_store(h, reinterpret_cast<half8_u_t *>(dst));
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            if (n + e < p.N) dst[e] = h[e];
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
         lds_barrier();
     }
@@ -1003,12 +1053,22 @@ void gemm_f16_nt_kernel(Params p)
     const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(smem));
 
     half8_t af[CF::ADB ? 2 : 1][CF::FM], bf[2][CF::FN];
+    // the lane's fragment read offsets in the A and B tiles of a stage, one
+    // register each, so every read of the loop is that register plus an
+    // immediate offset
+    uint32_t fra[2][KK], frb[2][KK];
+#pragma unroll
+    for (int par = 0; par < 2; ++par)
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            fra[par][kk] = w.frag_off[par][kk] + w.a_frag_base;
+            frb[par][kk] = w.frag_off[par][kk] + w.b_frag_base;
+        }
     // A fragment i / B fragment j of step kk of `stage`, into buffer `buf`
     auto read_a = [&](int buf, int stage, int kk, int i) {
         if constexpr (CF::AL == 0) {
             af[buf][i] = *reinterpret_cast<const half8_t *>(smem + stage * CF::STAGE_BYTES +
-                                                        w.frag_off[i & 1][kk] + w.a_frag_base +
-                                                        i * CF::MI * CF::ROW_BYTES);
+                                                        fra[i & 1][kk] + i * CF::MI * CF::ROW_BYTES);
         } else {
             // the stage's offset joins the base before the XOR (see read_b)
             uint32_t off;
@@ -1024,8 +1084,7 @@ void gemm_f16_nt_kernel(Params p)
     auto read_b = [&](int buf, int stage, int kk, int j) {
         if constexpr (CF::BL == 0) {
             bf[buf][j] = *reinterpret_cast<const half8_t *>(smem + stage * CF::STAGE_BYTES +
-                                                             w.frag_off[j & 1][kk] + w.b_frag_base +
-                                                             j * CF::MI * CF::ROW_BYTES);
+                                                             frb[j & 1][kk] + j * CF::MI * CF::ROW_BYTES);
         } else {
             // the XOR is issued at the read (an asm the compiler cannot hoist):
             // hoisted, the FN offsets would each hold a register for the
@@ -1249,6 +1308,8 @@ void gemm_f16_nt_kernel(Params p)
         // and the first VALU read of it: 24, more than the ISA asks for after
         // any MFMA, whatever its pass count.
         if constexpr (CF::MI == 16) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
+        // no accumulator read is scheduled ahead of those wait states
+        __builtin_amdgcn_sched_barrier(0);
         // Every wave is done with the ring (and every DMA has landed): the next
         // tile's prefill may start, and it flies while this tile is stored.
         wait_vmcnt<0>();
