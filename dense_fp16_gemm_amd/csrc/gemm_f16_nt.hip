@@ -242,6 +242,16 @@ struct Cfg {
     // the LDS-staged epilogue writes one block row of every wave (WM * MI tile
     // rows of BN halves, rows padded by 16 bytes) into one ring stage
     static constexpr bool STAGED_OK = WM * MI * (BN * 2 + 16) <= STAGE_BYTES;
+    // Double-buffered staging for tiles wholly inside M x N: two buffers of
+    // EPI_RB block rows each, in the free stage and, where the ring already
+    // takes more than half of the LDS (one workgroup per CU), the LDS past
+    // the ring (EPI_EXTRA more bytes); 0 where two buffers of one block row
+    // do not fit.
+    static constexpr int EPI_BROW = WM * MI * (BN * 2 + 16);
+    static constexpr int EPI_AVAIL = STAGE_BYTES + (2 * LDS_BYTES > LDS_LIMIT ? LDS_LIMIT - LDS_BYTES : 0);
+    static constexpr int EPI_RB = EPI_AVAIL / (2 * EPI_BROW) < FM ? EPI_AVAIL / (2 * EPI_BROW) : FM;
+    static constexpr int EPI_EXTRA = EPI_RB > 0 && 2 * EPI_RB * EPI_BROW > STAGE_BYTES
+                                         ? 2 * EPI_RB * EPI_BROW - STAGE_BYTES : 0;
     static_assert(BK == 32 || BK == 64 || BK == 128, "BK is 32, 64 or 128");
     static_assert(KK % 2 == 0, "fragment double buffer alternates within a slice");
     static_assert(MI == 32 || MI == 16, "MFMA is 32x32x16 or 16x16x32");
@@ -765,9 +775,10 @@ constexpr int staged_stores()
 // after a barrier every thread stores 16-byte row segments, a wave covering
 // 512 consecutive columns.  A barrier ends each round before the buffer is
 // reused.  A tile wholly inside M x N (the common case, known for the whole
-// workgroup) takes a path with no per-item checks: a block row's LDS reads go
-// out back to back and its stores follow, so the reads' latencies overlap.
-// Other tiles check every item against M and N.
+// workgroup) takes a path with no per-item checks, and where two buffers fit
+// (Cfg::EPI_RB) its rounds alternate between them, so that one round's
+// read-back and stores overlap the next round's conversions.  Other tiles
+// check every item against M and N.
 template <class CF>
 __device__ __forceinline__ void store_tile_staged(const Params &p, const Tile &t,
                                                   typename CF::Acc (&acc)[CF::FM][CF::FN],
@@ -777,6 +788,7 @@ __device__ __forceinline__ void store_tile_staged(const Params &p, const Tile &t
     constexpr int CROWS = CF::WM * CF::MI;     // tile rows per block row
     constexpr int BROW = CROWS * PITCH;        // bytes per staged block row
     static_assert(CF::STAGED_OK, "staged block row fits one stage");
+    static_assert(CF::EPI_BROW == BROW, "staged block row size");
     // block rows per round: as many as one stage holds
     constexpr int R = CF::STAGE_BYTES / BROW < CF::FM ? CF::STAGE_BYTES / BROW : CF::FM;
     static_assert(R >= 1, "one block row per round at least");
@@ -792,43 +804,99 @@ __device__ __forceinline__ void store_tile_staged(const Params &p, const Tile &t
     constexpr int ITEMS_R = CROWS * SEGS;      // items (16-byte segments) per block row
     constexpr int NI = (ITEMS_R + CF::THREADS - 1) / CF::THREADS;   // per thread
     const bool interior = t.m0 + CF::BM <= p.M && t.n0 + CF::BN <= p.N;
+    // block row i of the wave's accumulators, converted to fp16, into staged
+    // block row r of buffer b
+    auto write_row = [&](uint8_t *b, int r, int i) {
+        const int srow = wave_m * CF::MI + lrow;   // staged row of this lane
+        // one block row at a time: its accumulators are read out after the
+        // previous row's writes
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < CF::FN; ++j) {
+            // the block, copied into VGPRs by an empty volatile statement: the
+            // copy comes after the wait states that follow the last
+            // hand-issued MFMA (see the kernel), and the compiler keeps the
+            // AGPRs where the MFMAs left them
+            typename CF::Acc av;
+            if constexpr (CF::MI == 16)
+                asm volatile("" : "=v"(av) : "0"(acc[i][j]));
+            else
+                av = acc[i][j];
+#pragma unroll
+            for (int g = 0; g < CF::ACC_N / 4; ++g) {
+                const int ncol = wave_n * CF::TN + j * CF::MI + (CF::MI == 32 ? g * 8 + lq * 4 : lq * 4);
+                f32x4_t v;
+                v.x = av[4 * g + 0];
+                v.y = av[4 * g + 1];
+                v.z = av[4 * g + 2];
+                v.w = av[4 * g + 3];
+                *reinterpret_cast<half4_t *>(b + r * BROW + srow * PITCH + ncol * 2) =
+                    __builtin_convertvector(v, half4_t);
+            }
+        }
+    };
+    if constexpr (CF::EPI_RB > 0) {
+        if (interior) {
+            // Rounds of RB block rows alternate between two buffers, so the
+            // read-back of round q (its LDS reads first, their latency under
+            // the conversions) and its stores share one barrier interval
+            // with the conversion of round q + 1.  Buffer q % 2 is written
+            // again only after the barrier that follows its reads.
+            constexpr int RB = CF::EPI_RB;
+            constexpr int NR = (CF::FM + RB - 1) / RB;
+            half8_t h[RB][NI];
+#pragma unroll
+            for (int r = 0; r < RB; ++r) write_row(buf, r, r);
+            lds_barrier();
+#pragma unroll
+            for (int q = 0; q < NR; ++q) {
+                uint8_t *bq = buf + (q & 1) * RB * BROW;
+#pragma unroll
+                for (int r = 0; r < RB; ++r) {
+                    if (q * RB + r >= CF::FM) break;
+#pragma unroll
+                    for (int it = 0; it < NI; ++it) {
+                        const int cr = it * CF::THREADS + tid;
+                        if (ITEMS_R % CF::THREADS != 0 && cr >= ITEMS_R) continue;
+                        h[r][it] = *reinterpret_cast<const half8_t *>(bq + r * BROW + (cr / SEGS) * PITCH +
+                                                                      (cr % SEGS) * 16);
+                    }
+                }
+                if (q + 1 < NR) {
+                    uint8_t *bn = buf + ((q + 1) & 1) * RB * BROW;
+#pragma unroll
+                    for (int r = 0; r < RB; ++r)
+                        if ((q + 1) * RB + r < CF::FM) write_row(bn, r, (q + 1) * RB + r);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int r = 0; r < RB; ++r) {
+                    if (q * RB + r >= CF::FM) break;
+#pragma unroll
+                    for (int it = 0; it < NI; ++it) {
+                        const int cr = it * CF::THREADS + tid;
+                        if (ITEMS_R % CF::THREADS != 0 && cr >= ITEMS_R) continue;
+                        const int sr = cr / SEGS;
+                        const int32_t m = t.m0 + (sr / CF::MI) * CF::TM + (q * RB + r) * CF::MI + sr % CF::MI;
+                        const int32_t n = t.n0 + (cr % SEGS) * 8;
+                        _Float16 *dst = reinterpret_cast<_Float16 *>(p.C) + static_cast<int64_t>(m) * p.N + n;
+                        // non-temporal: C is written once, and left out of
+                        // L2 it does not evict the A and B strips the XCD's
+                        // tiles share
+                        __builtin_nontemporal_store(h[r][it], reinterpret_cast<half8_u_t *>(dst));
+                    }
+                }
+                lds_barrier();
+            }
+            return;
+        }
+    }
 #pragma unroll
     for (int i0 = 0; i0 < CF::FM; i0 += R) {
         const int nr = CF::FM - i0 < R ? CF::FM - i0 : R;   // block rows this round
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            if (r < nr) {
-                const int i = i0 + r;
-                const int srow = wave_m * CF::MI + lrow;   // staged row of this lane
-                // one block row at a time: its accumulators are read out
-                // after the previous row's writes
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int j = 0; j < CF::FN; ++j) {
-                    // the block, copied into VGPRs by an empty volatile
-                    // statement: the copy comes after the wait states that
-                    // follow the last hand-issued MFMA (see the kernel), and
-                    // the compiler keeps the AGPRs where the MFMAs left them
-                    typename CF::Acc av;
-                    if constexpr (CF::MI == 16)
-                        asm volatile("" : "=v"(av) : "0"(acc[i][j]));
-                    else
-                        av = acc[i][j];
-#pragma unroll
-                    for (int g = 0; g < CF::ACC_N / 4; ++g) {
-                        const int ncol = wave_n * CF::TN + j * CF::MI +
-                                         (CF::MI == 32 ? g * 8 + lq * 4 : lq * 4);
-                        f32x4_t v;
-                        v.x = av[4 * g + 0];
-                        v.y = av[4 * g + 1];
-                        v.z = av[4 * g + 2];
-                        v.w = av[4 * g + 3];
-                        *reinterpret_cast<half4_t *>(buf + r * BROW + srow * PITCH + ncol * 2) =
-                            __builtin_convertvector(v, half4_t);
-                    }
-                }
-            }
-        }
+        for (int r = 0; r < R; ++r)
+            if (r < nr) write_row(buf, r, i0 + r);
         lds_barrier();
         // item cr of block row r: staged row sr = cr / SEGS, segment sc
         auto row_of = [&](int r, int sr) {
@@ -1004,7 +1072,8 @@ __global__ __launch_bounds__(CF::THREADS)
 __attribute__((amdgpu_waves_per_eu(CF::WAVES_PER_SIMD, CF::WAVES_PER_SIMD)))
 void gemm_f16_nt_kernel(Params p)
 {
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[CF::LDS_BYTES];
+    // the ring, then the staged epilogue's second buffer where it needs more
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[CF::LDS_BYTES + (SPLIT ? 0 : CF::EPI_EXTRA)];
     constexpr int S = CF::STAGES;
     constexpr int KK = CF::KK;
     constexpr int L = CF::LOADS;
