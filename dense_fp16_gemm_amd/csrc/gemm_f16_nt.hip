@@ -586,7 +586,7 @@ __device__ __forceinline__ void dma_slice(const Params &p, const Tile &t, int st
 // kernel supplies the wait states the ISA requires around them itself: after
 // the accumulators are zeroed (VALU write, then MFMA reads them) and before
 // they are read back (MFMA write, then VALU read); see the kernel body.
-template <class CF, int NLD, bool FUSED = false>
+template <class CF, int NLD, bool FUSED = false, bool ZERO = false>
 struct Step {
     template <class RdA, class RdB, class Ld>
     __device__ __forceinline__ static void run(typename CF::Acc (&acc)[CF::FM][CF::FN],
@@ -610,6 +610,7 @@ struct Step {
 #pragma unroll
             for (int w = 0; w < NLD; ++w)
                 if ((w * NM) / NLD == t) dw = w;
+            static_assert(!ZERO || (!FUSED && CF::MI == 16), "zero start: hand-issued MFMAs, no fused DMA");
             if constexpr (FUSED) {
                 static_assert(CF::MI == 16 && NLD <= NM, "fused DMA: hand-issued MFMAs, one DMA per slot");
                 if (dw >= 0) {
@@ -636,6 +637,10 @@ struct Step {
                 }
             } else if constexpr (CF::MI == 32) {
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[j], af[i], acc[i][j], 0, 0, 0);
+            } else if constexpr (ZERO) {
+                // a tile's first step: the accumulator input is the constant 0
+                asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, 0"
+                             : "=a"(acc[i][j]) : "v"(bf[j]), "v"(af[i]));
             } else {
                 asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0"
                              : "+a"(acc[i][j]) : "v"(bf[j]), "v"(af[i]));
@@ -1208,9 +1213,15 @@ void gemm_f16_nt_kernel(Params p)
             for (int i = 0; i < CF::B_NB; ++i)
                 dvoffb[i] = dma_lane_offset_kn<CF, false>(i, w.wave, w.lane, cur.n0, pt.N);
         }
+        // slices whose early refill (slice kt + 2) lies wholly inside K
+        const int kt_fast = FAST_DMA ? min(max(cur.klen / CF::BK - 2, 0), KT) : 0;
+        // With hand-issued MFMAs and two such slices, the tile's first K
+        // step takes 0 as its accumulator input, so nothing is zeroed here.
+        constexpr bool CAN_ZERO_START = FAST_DMA && CF::MI == 16;
+        const bool zero_start = CAN_ZERO_START && kt_fast >= 2;
         typename CF::Acc acc[CF::FM][CF::FN];
-        zero_acc<CF>(acc);
-        if constexpr (CF::MI == 16) {
+        if (!zero_start) zero_acc<CF>(acc);
+        if (CF::MI == 16 && !zero_start) {
             // the zeros are in the AGPRs before the wait states that separate
             // their (VALU) writes from the first MFMA reading them
 #pragma unroll
@@ -1257,8 +1268,9 @@ void gemm_f16_nt_kernel(Params p)
         // Their accounting is therefore identical to the real ones.
         int rd = 0;        // stage holding slice kt
         int pst = S - 1;   // stage receiving slice kt + S - 1, freed before slice kt
-        auto slice = [&](int kt, auto fast) {
+        auto slice = [&](int kt, auto fast, auto zero) {
             constexpr bool FAST = decltype(fast)::value;
+            constexpr bool ZERO = decltype(zero)::value;
             // M0 values are computed from the bases where they are written
             // (one scalar add into M0 each), not held in a scalar register
             // per value across the loop
@@ -1323,7 +1335,9 @@ void gemm_f16_nt_kernel(Params p)
                 if (kk + 1 < KK) {
                     auto ra = [&](int i) { read_a(CF::ADB ? (kk + 1) & 1 : 0, rd, kk + 1, i); };
                     auto rb = [&](int j) { read_b((kk + 1) & 1, rd, kk + 1, j); };
-                    if (kk < DSTEPS)
+                    if (ZERO && kk == 0)
+                        Step<CF, 0, false, ZERO>::run(acc, af[CF::ADB ? kk & 1 : 0], bf[kk & 1], ra, rb, none);
+                    else if (kk < DSTEPS)
                         Step<CF, DPS>::run(acc, af[CF::ADB ? kk & 1 : 0], bf[kk & 1], ra, rb, dma);
                     else
                         Step<CF, 0>::run(acc, af[CF::ADB ? kk & 1 : 0], bf[kk & 1], ra, rb, none);
@@ -1354,24 +1368,35 @@ void gemm_f16_nt_kernel(Params p)
             pst = rd;
             rd = rd_next;
         };
-        // slices whose early refill (slice kt + 2) lies wholly inside K, then the rest
-        const int kt_fast = FAST_DMA ? min(max(cur.klen / CF::BK - 2, 0), KT) : 0;
+        // slices whose early refill lies wholly inside K, then the rest
         int kt = 0;
         if constexpr (FAST_DMA) {
             // two slices per trip (FAST_DMA implies two stages), so the ring
             // stage of each is a compile-time constant: LDS addresses and M0
-            // values become loop-invariant registers
+            // values become loop-invariant registers.  The first trip is
+            // separate where the tile starts with the zero-input step.
+            if constexpr (CAN_ZERO_START) {
+                if (zero_start) {
+                    rd = 0;
+                    pst = 1;
+                    slice(0, std::true_type{}, std::true_type{});
+                    rd = 1;
+                    pst = 0;
+                    slice(1, std::true_type{}, std::false_type{});
+                    kt = 2;
+                }
+            }
             for (; kt + 1 < kt_fast; kt += 2) {
                 rd = 0;
                 pst = 1;
-                slice(kt, std::true_type{});
+                slice(kt, std::true_type{}, std::false_type{});
                 rd = 1;
                 pst = 0;
-                slice(kt + 1, std::true_type{});
+                slice(kt + 1, std::true_type{}, std::false_type{});
             }
         }
-        for (; kt < kt_fast; ++kt) slice(kt, std::true_type{});
-        for (; kt < KT; ++kt) slice(kt, std::false_type{});
+        for (; kt < kt_fast; ++kt) slice(kt, std::true_type{}, std::false_type{});
+        for (; kt < KT; ++kt) slice(kt, std::false_type{}, std::false_type{});
 
         // Wait states between the last hand-issued MFMA writing an accumulator
         // and the first VALU read of it: 24, more than the ISA asks for after
