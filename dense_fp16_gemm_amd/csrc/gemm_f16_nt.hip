@@ -1914,63 +1914,63 @@ KernelEntry entry_general(int swizzle)
 }
 
 static const KernelEntry kKernels[] = {
-    entry<Cfg<256, 256, 32, 2, 2, 4>>(8, 0.00f, 0.751f),   // 0: 4 waves of 128x128, 4 stages of K 32
-    entry<Cfg<256, 256, 32, 2, 2, 5>>(8, 0.00f, 0.746f),   // 1: the same, 5 stages
-    entry<Cfg<256, 128, 64, 2, 2, 3>>(8, 0.85f, 0.711f),   // 2: 4 waves of 128x64, 3 stages of K 64
-    entry<Cfg<256, 128, 32, 2, 2, 6>>(8, 0.00f, 0.555f),   // 3: the same tile, 6 stages of K 32
-    entry<Cfg<128, 128, 64, 2, 2, 4>>(8, 0.75f, 0.558f),   // 4: 4 waves of 64x64, 4 stages
-    entry<Cfg<128, 64, 64, 2, 1, 6>>(8, 0.60f, 0.287f),    // 5: 2 waves of 64x64, 6 stages
-    entry<Cfg<256, 256, 32, 2, 4, 4>>(8, 0.00f, 0.748f),   // 6: 8 waves of 128x64, 4 stages of K 32
-    entry<Cfg<256, 256, 32, 4, 2, 4>>(8, 0.00f, 0.750f),   // 7: 8 waves of 64x128, 4 stages of K 32
-    entry<Cfg<256, 256, 32, 2, 4, 5>>(8, 0.00f, 0.745f),   // 8: 8 waves of 128x64, 5 stages of K 32
-    entry<Cfg<256, 256, 64, 2, 2, 2>>(8, 1.00f, 0.723f),   // 9: 4 waves of 128x128, 2 stages of K 64
-    entry<Cfg<256, 256, 64, 2, 4, 2>>(8, 0.00f, 0.718f),   // 10: 8 waves of 128x64, 2 stages of K 64
+    entry<Cfg<256, 256, 32, 2, 2, 4>>(8, 0.00f, 0.749f),   // 0: 4 waves of 128x128, 4 stages of K 32
+    entry<Cfg<256, 256, 32, 2, 2, 5>>(8, 0.00f, 0.742f),   // 1: the same, 5 stages
+    entry<Cfg<256, 128, 64, 2, 2, 3>>(8, 0.85f, 0.700f),   // 2: 4 waves of 128x64, 3 stages of K 64
+    entry<Cfg<256, 128, 32, 2, 2, 6>>(8, 0.00f, 0.551f),   // 3: the same tile, 6 stages of K 32
+    entry<Cfg<128, 128, 64, 2, 2, 4>>(8, 0.75f, 0.547f),   // 4: 4 waves of 64x64, 4 stages
+    entry<Cfg<128, 64, 64, 2, 1, 6>>(8, 0.60f, 0.286f),    // 5: 2 waves of 64x64, 6 stages
+    entry<Cfg<256, 256, 32, 2, 4, 4>>(8, 0.00f, 0.747f),   // 6: 8 waves of 128x64, 4 stages of K 32
+    entry<Cfg<256, 256, 32, 4, 2, 4>>(8, 0.00f, 0.747f),   // 7: 8 waves of 64x128, 4 stages of K 32
+    entry<Cfg<256, 256, 32, 2, 4, 5>>(8, 0.00f, 0.742f),   // 8: 8 waves of 128x64, 5 stages of K 32
+    entry<Cfg<256, 256, 64, 2, 2, 2>>(8, 1.00f, 0.721f),   // 9: 4 waves of 128x128, 2 stages of K 64
+    entry<Cfg<256, 256, 64, 2, 4, 2>>(8, 0.00f, 0.713f),   // 10: 8 waves of 128x64, 2 stages of K 64
     // 11: as 9 with 16x16x32 MFMAs, the whole refill issued early, A double-buffered
-    entry<Cfg<256, 256, 64, 2, 2, 2, 16, 0, 16, 1>>(8, 1.06f, 0.792f),
-    entry<Cfg<256, 128, 64, 2, 2, 3, 16>>(8, 0.00f, 0.652f),   // 12: as 2 with 16x16x32 MFMAs
-    entry<Cfg<192, 256, 64, 2, 2, 2>>(8, 0.80f, 0.635f),   // 13: 4 waves of 96x128, 2 stages of K 64
-    entry<Cfg<256, 192, 64, 2, 2, 2>>(8, 0.82f, 0.636f),   // 14: 4 waves of 128x96, 2 stages of K 64
-    entry<Cfg<192, 256, 32, 2, 2, 5>>(8, 0.00f, 0.684f),   // 15: 4 waves of 96x128, 5 stages of K 32
-    entry<Cfg<256, 192, 32, 2, 2, 5>>(8, 0.00f, 0.702f),   // 16: 4 waves of 128x96, 5 stages of K 32
+    entry<Cfg<256, 256, 64, 2, 2, 2, 16, 0, 16, 1>>(8, 1.06f, 0.828f),
+    entry<Cfg<256, 128, 64, 2, 2, 3, 16>>(8, 0.00f, 0.675f),   // 12: as 2 with 16x16x32 MFMAs
+    entry<Cfg<192, 256, 64, 2, 2, 2>>(8, 0.80f, 0.628f),   // 13: 4 waves of 96x128, 2 stages of K 64
+    entry<Cfg<256, 192, 64, 2, 2, 2>>(8, 0.82f, 0.628f),   // 14: 4 waves of 128x96, 2 stages of K 64
+    entry<Cfg<192, 256, 32, 2, 2, 5>>(8, 0.00f, 0.672f),   // 15: 4 waves of 96x128, 5 stages of K 32
+    entry<Cfg<256, 192, 32, 2, 2, 5>>(8, 0.00f, 0.697f),   // 16: 4 waves of 128x96, 5 stages of K 32
     // 17-20: the scheme of 11 on smaller tiles
-    entry<Cfg<256, 192, 64, 2, 2, 2, 16, 0, 14, 1>>(8, 0.94f, 0.760f),   // 17: 4 waves of 128x96
-    entry<Cfg<192, 256, 64, 2, 2, 2, 16, 0, 14, 1>>(8, 0.97f, 0.752f),   // 18: 4 waves of 96x128
-    entry<Cfg<256, 128, 64, 2, 2, 2, 16, 0, 12, 1>>(8, 0.00f, 0.570f),   // 19: 4 waves of 128x64
-    entry<Cfg<128, 128, 64, 2, 2, 2, 16, 0, 8, 1>>(8, 0.00f, 0.384f),    // 20: 4 waves of 64x64
+    entry<Cfg<256, 192, 64, 2, 2, 2, 16, 0, 14, 1>>(8, 0.94f, 0.769f),   // 17: 4 waves of 128x96
+    entry<Cfg<192, 256, 64, 2, 2, 2, 16, 0, 14, 1>>(8, 0.97f, 0.759f),   // 18: 4 waves of 96x128
+    entry<Cfg<256, 128, 64, 2, 2, 2, 16, 0, 12, 1>>(8, 0.00f, 0.575f),   // 19: 4 waves of 128x64
+    entry<Cfg<128, 128, 64, 2, 2, 2, 16, 0, 8, 1>>(8, 0.00f, 0.389f),    // 20: 4 waves of 64x64
     // 21: 4 waves of 32x64.  For a small M the two tile rows that share a B
     // strip run together on one XCD, and B, the operand streamed from HBM,
     // holds two thirds of every stage (a 128x64 tile gives it one third).
-    entry<Cfg<64, 128, 64, 2, 2, 6>>(8, 0.65f, 0.357f),
+    entry<Cfg<64, 128, 64, 2, 2, 6>>(8, 0.65f, 0.349f),
     // 22: 21 with K 128 per stage (256-byte rows): twice the contiguous bytes
     // per row and DMA instruction, which the HBM stream of B prefers
-    entry<Cfg<64, 128, 128, 2, 2, 3>>(8, 0.66f, 0.366f),
+    entry<Cfg<64, 128, 128, 2, 2, 3>>(8, 0.66f, 0.369f),
     // 23: 4 waves of 32x32, five stages of K 128: more tiles for a small M
     // whose 64x128 tiles would leave CUs idle (M <= 256, N of a few thousand)
     entry<Cfg<64, 64, 128, 2, 2, 5>>(8, 0.62f, 0.259f),
     // 24-29: B stored [K, N] (gemm_f16_nn), the schemes of 11 and 18-21 with
     // transposing fragment reads of B
-    entry<Cfg<256, 256, 64, 2, 2, 2, 16, 0, 16, 0, 1>>(8, 1.06f, 0.736f),   // 24: as 11, A single-buffered
-    entry<Cfg<192, 256, 64, 2, 2, 2, 16, 0, 14, 1, 1>>(8, 0.97f, 0.706f),   // 25: as 18
-    entry<Cfg<256, 128, 64, 2, 2, 2, 16, 0, 12, 1, 1>>(8, 0.85f, 0.568f),   // 26: as 19
-    entry<Cfg<128, 128, 64, 2, 2, 2, 16, 0, 8, 1, 1>>(8, 0.75f, 0.377f),    // 27: as 20
-    entry<Cfg<64, 128, 64, 2, 2, 2, 16, 0, 6, 1, 1>>(8, 0.62f, 0.218f),     // 28: 4 waves of 32x64
+    entry<Cfg<256, 256, 64, 2, 2, 2, 16, 0, 16, 0, 1>>(8, 1.06f, 0.781f),   // 24: as 11, A single-buffered
+    entry<Cfg<192, 256, 64, 2, 2, 2, 16, 0, 14, 1, 1>>(8, 0.97f, 0.740f),   // 25: as 18
+    entry<Cfg<256, 128, 64, 2, 2, 2, 16, 0, 12, 1, 1>>(8, 0.85f, 0.584f),   // 26: as 19
+    entry<Cfg<128, 128, 64, 2, 2, 2, 16, 0, 8, 1, 1>>(8, 0.75f, 0.391f),    // 27: as 20
+    entry<Cfg<64, 128, 64, 2, 2, 2, 16, 0, 6, 1, 1>>(8, 0.62f, 0.225f),     // 28: 4 waves of 32x64
     // 29: 28 with 6 stages, the refill spread over each slice: more of B in
     // flight for a small M (the streamed operand)
-    entry<Cfg<64, 128, 64, 2, 2, 6, 16, 0, 0, 0, 1>>(8, 0.58f, 0.243f),
+    entry<Cfg<64, 128, 64, 2, 2, 6, 16, 0, 0, 0, 1>>(8, 0.58f, 0.261f),
     // 30-32: A stored [K, M] and B [N, K] (gemm_f16_tt); 33-35: A [K, M] and
     // B [K, N] (gemm_f16_tn): transposing fragment reads for A as well
-    entry<Cfg<256, 256, 64, 2, 2, 2, 16, 0, 16, 0, 0, 1>>(8, 1.06f, 0.728f),   // 30
-    entry<Cfg<256, 128, 64, 2, 2, 2, 16, 0, 12, 1, 0, 1>>(8, 0.85f, 0.558f),   // 31
-    entry<Cfg<128, 128, 64, 2, 2, 2, 16, 0, 8, 1, 0, 1>>(8, 0.75f, 0.375f),    // 32
-    entry<Cfg<256, 256, 64, 2, 2, 2, 16, 0, 16, 0, 1, 1>>(8, 1.06f, 0.676f),   // 33
-    entry<Cfg<256, 128, 64, 2, 2, 2, 16, 0, 12, 1, 1, 1>>(8, 0.85f, 0.558f),   // 34
-    entry<Cfg<128, 128, 64, 2, 2, 2, 16, 0, 8, 1, 1, 1>>(8, 0.75f, 0.374f),    // 35
+    entry<Cfg<256, 256, 64, 2, 2, 2, 16, 0, 16, 0, 0, 1>>(8, 1.06f, 0.778f),   // 30
+    entry<Cfg<256, 128, 64, 2, 2, 2, 16, 0, 12, 1, 0, 1>>(8, 0.85f, 0.573f),   // 31
+    entry<Cfg<128, 128, 64, 2, 2, 2, 16, 0, 8, 1, 0, 1>>(8, 0.75f, 0.395f),    // 32
+    entry<Cfg<256, 256, 64, 2, 2, 2, 16, 0, 16, 0, 1, 1>>(8, 1.06f, 0.735f),   // 33
+    entry<Cfg<256, 128, 64, 2, 2, 2, 16, 0, 12, 1, 1, 1>>(8, 0.85f, 0.579f),   // 34
+    entry<Cfg<128, 128, 64, 2, 2, 2, 16, 0, 8, 1, 1, 1>>(8, 0.75f, 0.396f),    // 35
     // 36-37: TT with a 64-wide B side (B [N, K] takes any multiple of 32
     // rows; A [K, M] needs 128): 4 waves of 64x32, twice the tiles of 32 for
     // a small M.  36 keeps 6 stages with the refill spread over each slice,
     // as 29 does for NN; 37 is the two-stage early-refill scheme.
-    entry<Cfg<128, 64, 64, 2, 2, 6, 16, 0, 0, 0, 0, 1>>(8, 0.56f, 0.254f),     // 36
-    entry<Cfg<128, 64, 64, 2, 2, 2, 16, 0, 6, 1, 0, 1>>(8, 0.00f, 0.222f),     // 37
+    entry<Cfg<128, 64, 64, 2, 2, 6, 16, 0, 0, 0, 0, 1>>(8, 0.56f, 0.266f),     // 36
+    entry<Cfg<128, 64, 64, 2, 2, 2, 16, 0, 6, 1, 0, 1>>(8, 0.00f, 0.228f),     // 37
     // 38-41: 64-wide tiles on a k-outermost side (128-byte LDS rows), 6
     // stages with the refill spread over each slice, for a small M or N:
     // 38 NN 128x64 (B [K, N]), 39 TT 64x128 (A [K, M]), 40 TN 64x128, 41 TN
@@ -1978,17 +1978,17 @@ static const KernelEntry kKernels[] = {
     // (29, 36, 40), unsplit and timed by the autotuner over 14-16 shapes
     // each, 38 was about 14% faster than 29, 39 18% faster than 36 and 41 2%
     // faster than 40; the rates of 29, 36 and 40 say so.
-    entry<Cfg<128, 64, 64, 2, 2, 6, 16, 0, 0, 0, 1, 0>>(8, 0.66f, 0.278f),     // 38
-    entry<Cfg<64, 128, 64, 2, 2, 6, 16, 0, 0, 0, 0, 1>>(8, 0.66f, 0.299f),     // 39
-    entry<Cfg<64, 128, 64, 2, 2, 6, 16, 0, 0, 0, 1, 1>>(8, 0.645f, 0.216f),    // 40
-    entry<Cfg<128, 64, 64, 2, 2, 6, 16, 0, 0, 0, 1, 1>>(8, 0.66f, 0.217f),     // 41
+    entry<Cfg<128, 64, 64, 2, 2, 6, 16, 0, 0, 0, 1, 0>>(8, 0.66f, 0.294f),     // 38
+    entry<Cfg<64, 128, 64, 2, 2, 6, 16, 0, 0, 0, 0, 1>>(8, 0.66f, 0.317f),     // 39
+    entry<Cfg<64, 128, 64, 2, 2, 6, 16, 0, 0, 0, 1, 1>>(8, 0.645f, 0.229f),    // 40
+    entry<Cfg<128, 64, 64, 2, 2, 6, 16, 0, 0, 0, 1, 1>>(8, 0.66f, 0.228f),     // 41
     // 42: 256x128x64, three stages, four consumer waves of 128x64 (16x16x32
     // MFMAs, both fragments double-buffered) and four producer waves that
     // only issue the DMA (gemm_f16_nt_pc_kernel).  Faster than 2 and 19, the
     // same tile with every wave loading, on every shape measured (8192^3:
     // 814 against 937 and 857 us), so it takes 2's place in both planners
     // (split_rate: 2's scaled by the unsplit gain at 2048 x 4096 x 8192, 1.11)
-    entry_pc<Cfg<256, 128, 64, 2, 2, 3, 16, 0, 0, 1>>(8, 0.87f, 0.79f),
+    entry_pc<Cfg<256, 128, 64, 2, 2, 3, 16, 0, 0, 1>>(8, 0.87f, 0.754f),
     // 43-45: the general kernel for NN, TT and TN (loads along the operand's
     // contiguous dimension), for arguments the direct-to-LDS kernels of those
     // layouts cannot take
@@ -2177,13 +2177,13 @@ static double split_cost(int id, int64_t M, int64_t N, int64_t K, int32_t splits
                          int64_t *splits_eff)
 {
     constexpr double kCuPeak = 2.5e15 / 256;   // dense fp16 flop/s of one CU
-    constexpr double kUnitSec = 1.86e-07;      // per unit: pipeline fill and epilogue
-    constexpr double kLaunchSec = 4.4e-06;     // per launch
-    constexpr double kHbmBytesPerSec = 3.93e+12;
-    static constexpr double kActiveExp = 0.328;      // bandwidth ~ (fraction of CUs busy)^kActiveExp
+    constexpr double kUnitSec = 2.3e-07;      // per unit: pipeline fill and epilogue
+    constexpr double kLaunchSec = 3.59e-06;     // per launch
+    constexpr double kHbmBytesPerSec = 4.08e+12;
+    static constexpr double kActiveExp = 0.351;      // bandwidth ~ (fraction of CUs busy)^kActiveExp
     constexpr double kOverlap = 0.1;
-    constexpr double kReduceBytesPerSec = 5.13e+12;
-    constexpr double kReduceSec = 3.21e-06;
+    constexpr double kReduceBytesPerSec = 4.95e+12;
+    constexpr double kReduceSec = 3.34e-06;
     const KernelEntry &e = kKernels[id];
     if (cus <= 0) cus = 1;
     const int64_t ks = split_k_len(id, K, splits);

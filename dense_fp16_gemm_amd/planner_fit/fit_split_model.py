@@ -5,10 +5,9 @@ the measurements in autotune_tables.jsonl, runs no GPU code.
 autotune_tables.jsonl: one MI355X (256 CUs), every configuration x split
 count that gemm_f16_autotune tried on 28 shapes per operand layout (under-
 filled grids, long and short K): one record per shape, entries
-[config_id, splits, status, ms].  The tables predate configuration 42 (the
-producer/consumer kernel), which was added with a split_rate scaled from
-configuration 2's by their measured unsplit ratio; configurations 0..41 are
-fitted here.
+[config_id, splits, status, ms].  Configurations 0..42 (every direct-to-LDS
+configuration, the producer/consumer one included) are fitted here; the
+general kernels are never split.
 
 The model (times in seconds, per launch):
   compute  = rounds x (unit flops / (rate_c x CU peak) + f1)
@@ -60,7 +59,7 @@ def split_len(bk, k, s):
     return cdiv(cdiv(k, s), bk) * bk
 
 
-def load_rows(cfgs, max_id=42):
+def load_rows(cfgs, max_id=43):
     recs = [json.loads(line) for line in open(TABLES)]
     rows = []
     for ri, r in enumerate(recs):

@@ -378,12 +378,14 @@ def test_splitk_plan_of_the_underfilled_workload(g):
 def test_splitk_candidates_are_plannable_configurations(g):
     # the split planner only picks configurations the plain planner may pick
     # for some shape of the layout (the others are compiled for sweeps)
+    sizes = (8, 32, 64, 96, 128, 192, 256, 512, 1024, 2048, 4096, 4992, 7000, 8192, 16384, 32768)
     plannable = set()
     for lay in ("nt", "nn", "tt", "tn"):
         plan_fn = getattr(g, f"gemm_f16_{lay}_plan")
-        for m in (64, 128, 256, 1024, 2048, 4096, 4992, 7000, 8192, 16384):
-            for n in (64, 128, 256, 1024, 2048, 4096, 4992, 7000, 8192, 16384):
-                plannable.add(plan_fn(m, n, 4096, 256).config_id)
+        for m in sizes:
+            for n in sizes:
+                for k in (1024, 4096, 65536):
+                    plannable.add(plan_fn(m, n, k, 256).config_id)
     for lay in ("nt", "nn", "tt", "tn"):
         split_fn = getattr(g, f"gemm_f16_{lay}_splitk_plan")
         for m, n, k in [(256, 256, 65536), (1024, 1024, 65536), (512, 2048, 32768),
