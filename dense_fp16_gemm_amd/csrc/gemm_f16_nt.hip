@@ -1888,8 +1888,11 @@ const void *split_instance()
 template <class CF>
 KernelEntry entry(int swizzle, float rate, float split_rate)
 {
+    // LDS of the unsplit instance: the ring and the staged epilogue's second
+    // buffer (the split instance has the ring only)
     return KernelEntry{reinterpret_cast<const void *>(&gemm_f16_nt_kernel<CF, false>),
-                       split_instance<CF>(), CF::BM, CF::BN, CF::BK, CF::WAVES, CF::STAGES, CF::LDS_BYTES, CF::THREADS,
+                       split_instance<CF>(), CF::BM, CF::BN, CF::BK, CF::WAVES, CF::STAGES,
+                       CF::LDS_BYTES + CF::EPI_EXTRA, CF::THREADS,
                        swizzle, rate, split_rate, CF::STAGED_OK ? 1 : 0, 0, 1, 2 * CF::AL + CF::BL};
 }
 

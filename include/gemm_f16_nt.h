@@ -111,7 +111,8 @@ typedef struct {
     int32_t tiles_n;     /* ceil(N / block_n)                              */
     int32_t grid;        /* persistent workgroups launched                 */
     int64_t tiles;       /* tiles_m * tiles_n                              */
-    int32_t lds_bytes;   /* LDS used by one workgroup                      */
+    int32_t lds_bytes;   /* LDS used by one workgroup: the ring, plus the
+                            staged epilogue's second buffer where it has one */
     int32_t xcds;        /* XCD count the tile order is arranged for       */
     int32_t epilogue;    /* 0: stores straight from the MFMA registers;
                             1: C staged through LDS for row-contiguous stores */

@@ -94,10 +94,18 @@ def test_config_table(g):
         assert info.block_k in (32, 64, 128)
         # (the last entry, the general kernel, stages through registers into
         # two LDS buffers with the same layout)
-        # the LDS ring: stages * (BM + BN) * BK * 2 bytes within 160 KB
-        assert info.lds_bytes == info.stages * (info.block_m + info.block_n) * info.block_k * 2
-        assert info.lds_bytes <= 160 * 1024
+        # the LDS ring, stages * (BM + BN) * BK * 2 bytes, and where the
+        # staged epilogue double-buffers past the ring its second buffer: all
+        # within 160 KB
+        ring = info.stages * (info.block_m + info.block_n) * info.block_k * 2
+        assert ring <= info.lds_bytes <= 160 * 1024
+        if info.lds_bytes > ring:
+            assert 2 * ring > 160 * 1024   # only where one workgroup fills a CU anyway
         assert info.block_m % 32 == 0 and info.block_n % 32 == 0
+    # configuration 11 (256 x 256 x 64, two stages): a 128 KB ring and two
+    # staging buffers of 2 padded block rows (16896 bytes each) that share
+    # the ring's last 64 KB stage
+    assert g.gemm_f16_nt_config_info(11).lds_bytes == 131072 + 2 * 2 * 16896 - 65536
     with pytest.raises(g.GemmError):
         g.gemm_f16_nt_config_info(n)
 
