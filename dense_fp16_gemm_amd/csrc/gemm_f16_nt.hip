@@ -934,8 +934,8 @@ __device__ __forceinline__ void store_tile_staged(const Params &p, const Tile &t
                 __builtin_amdgcn_sched_barrier(0);
             }
         } else {
-            // 16 bytes per lane at any 2-byte alignment: memcpy lets the
-            // compiler emit one 16-byte store, which the target's
+            // 16 bytes per lane at any 2-byte alignment: the 2-byte-aligned
+            // vector type still gives one 16-byte store, which the target's
             // unaligned-access mode allows; only the segment crossing N is
             // stored element by element.  One block row's items at a time (a
             // scheduling barrier between them keeps only those in registers)
