@@ -2084,14 +2084,34 @@ static void make_plan(int id, int64_t M, int64_t N, int32_t num_cus, int32_t swi
     out->grid = static_cast<int32_t>(out->tiles < cap ? out->tiles : cap);
 }
 
+static double split_cost(int id, int64_t M, int64_t N, int64_t K, int32_t splits, int32_t cus,
+                         int64_t *splits_eff);
+
 // Cost model: rounds of the persistent grid times the time one tile takes,
 // which scales with its area over the configuration's relative MFMA rate.
 // Entries with rel_rate 0 are compiled for sweeps but never planned.  Between
 // tiles of equal cost, one whose long side lies along the longer of M and N
 // is preferred (1%): its strip of the larger operand, the one streamed from
 // HBM, then fills most of each LDS stage.
-static int choose_config(int64_t M, int64_t N, int32_t num_cus, int32_t layout = 0)
+//
+// This rule sees no K.  When K is long and the tiles are small, their
+// operand traffic (which grows as the tile shrinks) decides instead: at
+// 1536 x 1536 x 16384 the rule's 64 x 64 tiles took 1.78 times as long as
+// 128 x 128 ones, at 2048 x 3072 x 4096 its 64 x 128 tiles 1.54 times as long
+// as the 256 x 128 producer/consumer tile.  So the plan is then checked
+// against the fitted time model of the split planner (split_cost, one range),
+// which counts K and the operand bytes, and the model's unsplit pick replaces
+// the rule's when it predicts a gain above kModelMargin.  Below that the rule
+// stands: against measured times the model errs by up to about 11% on fully
+// occupied shapes (8192 x 5120 x 8192: it prefers the 256 x 128 tile by 8%,
+// the 256 x 256 one measures 2.5% faster).  Timed on one MI355X over square
+// and oblong shapes from 256 to 8192 in all four layouts, the plans this
+// check changes ran at 0.64 of the rule's time (geometric mean, none
+// slower), while the model's picks below the margin were no better than the
+// rule's.
+static int choose_config_search(int64_t M, int64_t N, int64_t K, int32_t num_cus, int32_t layout)
 {
+    constexpr double kModelMargin = 1.15;
     int best = -1;
     double best_cost = 0.0;
     for (int id = 0; id < kNumKernels; ++id) {
@@ -2107,7 +2127,42 @@ static int choose_config(int64_t M, int64_t N, int32_t num_cus, int32_t layout =
             best_cost = cost;
         }
     }
-    return best;
+    if (best < 0 || K <= 0) return best;
+    int64_t eff = 1;
+    const double rule_time = split_cost(best, M, N, K, 1, num_cus, &eff);
+    int alt = best;
+    double alt_time = rule_time;
+    for (int id = 0; id < kNumKernels; ++id) {
+        const KernelEntry &e = kKernels[id];
+        if (e.rel_rate <= 0.0f || e.layout != layout || e.general) continue;
+        const double t = split_cost(id, M, N, K, 1, num_cus, &eff);
+        if (t < alt_time) {
+            alt = id;
+            alt_time = t;
+        }
+    }
+    return rule_time > kModelMargin * alt_time ? alt : best;
+}
+
+// choose_config_search behind a per-thread cache of the last few decisions
+// (the search prices every configuration of the layout), so a caller that
+// repeats a shape pays for it once.
+static int choose_config(int64_t M, int64_t N, int64_t K, int32_t num_cus, int32_t layout = 0)
+{
+    struct Choice {
+        int64_t M = -1, N = -1, K = -1;
+        int32_t cus = 0, layout = 0;
+        int id = -1;
+    };
+    static thread_local Choice cache[4];
+    static thread_local int next = 0;
+    for (const Choice &c : cache)
+        if (c.id >= 0 && c.M == M && c.N == N && c.K == K && c.cus == num_cus && c.layout == layout)
+            return c.id;
+    const int id = choose_config_search(M, N, K, num_cus, layout);
+    cache[next] = Choice{M, N, K, num_cus, layout, id};
+    next = (next + 1) % 4;
+    return id;
 }
 
 struct DeviceInfo {
@@ -2253,7 +2308,7 @@ static bool split_candidate(int id)
 static void choose_split_search(int64_t M, int64_t N, int64_t K, int32_t cus, int32_t config_id,
                                 int32_t splits, int *id_out, int32_t *splits_out, int32_t layout)
 {
-    const int plain = config_id >= 0 ? config_id : choose_config(M, N, cus, layout);
+    const int plain = config_id >= 0 ? config_id : choose_config(M, N, K, cus, layout);
     double best = 0.0;
     int best_id = -1;
     int64_t best_eff = 1;
@@ -2376,7 +2431,7 @@ static int run(int64_t M, int64_t N, int64_t K, const void *A, const void *B, vo
     const int s = current_cus(&cus);
     if (s != GEMM_F16_OK) return s;
     const int id = config_id >= 0 ? config_id
-                                  : (general ? kGeneralConfig : choose_config(M, N, cus));
+                                  : (general ? kGeneralConfig : choose_config(M, N, K, cus));
     gemm_f16_nt_plan_t plan;
     make_plan(id, M, N, cus, swizzle, grid, &plan);
     if (epilogue < 0) {
@@ -2430,7 +2485,7 @@ static int run_layout(int32_t layout, int64_t M, int64_t N, int64_t K, const voi
     const int s = current_cus(&cus);
     if (s != GEMM_F16_OK) return s;
     const int id = config_id >= 0 ? config_id
-                                  : (fast ? choose_config(M, N, cus, layout) : general_config(layout));
+                                  : (fast ? choose_config(M, N, K, cus, layout) : general_config(layout));
     gemm_f16_nt_plan_t plan;
     make_plan(id, M, N, cus, swizzle, grid, &plan);
     if (epilogue < 0) {
@@ -2450,7 +2505,7 @@ static int plan_layout(int32_t layout, int64_t M, int64_t N, int64_t K, int32_t 
         return GEMM_F16_UNSUPPORTED;
     if (K == 0) return gemm_f16_nt_plan(M, N, K, num_cus, plan);
     const int id = layout_supported(layout, M, N, K, nullptr, nullptr, false)
-                       ? choose_config(M, N, num_cus, layout) : general_config(layout);
+                       ? choose_config(M, N, K, num_cus, layout) : general_config(layout);
     make_plan(id, M, N, num_cus, 0, 0, plan);
     return GEMM_F16_OK;
 }
@@ -2751,7 +2806,7 @@ extern "C" int gemm_f16_nt_plan(int64_t M, int64_t N, int64_t K, int32_t num_cus
     if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX || cdiv(M, 64) * cdiv(N, 64) > INT32_MAX)
         return GEMM_F16_UNSUPPORTED;
     const int id = needs_general(K, nullptr, nullptr, false) ? kGeneralConfig
-                                                              : choose_config(M, N, num_cus);
+                                                              : choose_config(M, N, K, num_cus);
     make_plan(id, M, N, num_cus, 0, 0, plan);
     return GEMM_F16_OK;
 }

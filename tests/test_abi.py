@@ -137,6 +137,34 @@ def test_plan_headline_and_skinny(g):
     assert s.block_m <= 128 and s.tiles >= 256 and s.grid == 256   # M = 128 must still fill the chip
 
 
+@pytest.mark.parametrize("lay, shape, tile", [
+    # 64 x 64 tiles in three rounds (the area rule's pick) measured 1.6-1.8
+    # times the time of 128 x 128 tiles in one
+    ("nt", (1536, 1536, 16384), (128, 128)),
+    ("nt", (1536, 1536, 1024), (128, 128)),
+    # 64 x 128 tiles against the 256 x 128 producer/consumer tile: 1.5 times
+    ("nt", (2048, 3072, 4096), (256, 128)),
+    ("nn", (2048, 3072, 4096), (256, 128)),
+    ("tt", (2048, 3072, 4096), (256, 128)),
+    ("tn", (2048, 3072, 4096), (256, 128)),
+])
+def test_plain_plan_weighs_k(g, lay, shape, tile):
+    # the fitted time model, which counts K and the operand bytes, overrides
+    # the area rule where it predicts a clear gain
+    p = getattr(g, f"gemm_f16_{lay}_plan")(*shape, 256)
+    assert (p.block_m, p.block_n) == tile
+
+
+@pytest.mark.parametrize("shape, cid", [((8192, 8192, 8192), 11), ((4096, 4096, 4096), 11),
+                                        ((4999, 7001, 4160), 18), ((128, 16384, 16384), 22),
+                                        ((256, 256, 256), 23), ((8192, 5120, 8192), 11)])
+def test_plain_plan_keeps_the_rule_within_the_model_margin(g, shape, cid):
+    # the benchmark workloads, and 8192 x 5120 x 8192, where the model's
+    # preference for the 256 x 128 tile (8%) lies within its error and the
+    # 256 x 256 tile measures faster
+    assert g.gemm_f16_nt_plan(*shape, 256).config_id == cid
+
+
 def _order(g, plan):
     return [g.gemm_f16_nt_tile_of_slot(plan, s) for s in range(plan.tiles)]
 

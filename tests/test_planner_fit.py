@@ -18,7 +18,8 @@ SOURCE = os.path.join(ROOT, "dense_fp16_gemm_amd", "csrc", "gemm_f16_nt.hip")
 
 def _source_constants():
     src = open(SOURCE).read()
-    body = src[src.index("static double split_cost("):]
+    # the definition: the last occurrence (a declaration may precede it)
+    body = src[src.rindex("static double split_cost("):]
     consts = {k: float(v) for k, v in re.findall(r"(k[A-Za-z]+) = ([0-9.e+-]+);", body[:2000])}
     tab = src[src.index("static const KernelEntry kKernels[] = {"):]
     tab = tab[:tab.index("};")]
