@@ -289,6 +289,42 @@ def gemm_f16_autotune(layout: int, M: int, N: int, K: int, A: int, B: int, C: in
 
 
 # ---- torch convenience -------------------------------------------------------
+class _NoDeviceSwitch:
+    def __enter__(self):
+        return None
+
+    def __exit__(self, *exc):
+        return False
+
+
+_NO_SWITCH = _NoDeviceSwitch()
+
+
+def _on_device(t):
+    """Make t's device current for the call (the library launches on the
+    current device); a no-op context when it already is, since switching
+    costs more than a small GEMM's launch."""
+    import torch
+
+    idx = t.get_device()
+    return _NO_SWITCH if idx == torch.cuda.current_device() else torch.cuda.device(idx)
+
+
+def _stream_handle(t, stream) -> int:
+    """The raw HIP stream of `stream`, or of t's device's current stream.
+    torch's raw-stream query skips building a Stream object (the public
+    torch.cuda.current_stream takes about 2 us); the public call is the
+    fallback where the query is absent."""
+    import torch
+
+    if stream is not None:
+        return stream.cuda_stream
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is not None:
+        return raw(t.get_device())
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
 def _operands(a, b, layout: str, out):
     """Check fp16 operands stored as `layout` says; return (M, N, K, out)."""
     import torch
@@ -340,13 +376,13 @@ def gemm_nt(a, b, out=None, config: int | None = None, swizzle: int = 0, grid: i
     elif (out.dtype != torch.float16 or tuple(out.shape) != (m, n) or not out.is_contiguous()
           or out.device != a.device):
         raise ValueError("out must be a contiguous float16 [M, N] tensor on a's device")
-    s = stream if stream is not None else torch.cuda.current_stream(a.device)
-    with torch.cuda.device(a.device):
+    with _on_device(a):
+        s = _stream_handle(a, stream)
         if config is None and epilogue < 0:
-            gemm_f16_nt(m, n, k, a.data_ptr(), b.data_ptr(), out.data_ptr(), s.cuda_stream)
+            gemm_f16_nt(m, n, k, a.data_ptr(), b.data_ptr(), out.data_ptr(), s)
         else:
             gemm_f16_nt_with_config(m, n, k, a.data_ptr(), b.data_ptr(), out.data_ptr(),
-                                    s.cuda_stream, -1 if config is None else config, swizzle,
+                                    s, -1 if config is None else config, swizzle,
                                     grid, epilogue)
     return out
 
@@ -360,7 +396,7 @@ def gemm_splitk(a, b, layout: str = "nt", splits: int = 0, out=None, workspace=N
     import torch
 
     m, n, k, out = _operands(a, b, layout, out)
-    with torch.cuda.device(a.device):
+    with _on_device(a):
         cus = gemm_f16_device_cus()
     _, _, need = globals()[f"gemm_f16_{layout}_splitk_plan"](m, n, k, cus, splits)
     if config is not None and splits > 1:
@@ -371,11 +407,10 @@ def gemm_splitk(a, b, layout: str = "nt", splits: int = 0, out=None, workspace=N
     elif not workspace.is_cuda or workspace.device != a.device:
         raise ValueError("workspace must be a tensor on a's device")
     ws_bytes = workspace.numel() * workspace.element_size()
-    s = stream if stream is not None else torch.cuda.current_stream(a.device)
-    with torch.cuda.device(a.device):
+    with _on_device(a):
         globals()[f"gemm_f16_{layout}_splitk_with_config"](
             m, n, k, a.data_ptr(), b.data_ptr(), out.data_ptr(), splits, workspace.data_ptr(),
-            ws_bytes, s.cuda_stream, -1 if config is None else config)
+            ws_bytes, _stream_handle(a, stream), -1 if config is None else config)
     return out
 
 
@@ -392,16 +427,13 @@ def gemm(a, b, layout: str = "nt", out=None, config: int | None = None, swizzle:
     'nt': a [M,K], b [N,K] (C = a @ b.T);   'nn': a [M,K], b [K,N] (C = a @ b);
     'tn': a [K,M], b [K,N] (C = a.T @ b);   'tt': a [K,M], b [N,K] (C = a.T @ b.T).
     Same checks as gemm_nt."""
-    import torch
-
     if layout == "nt":
         return gemm_nt(a, b, out=out, config=config, swizzle=swizzle, grid=grid, stream=stream,
                        epilogue=epilogue)
     m, n, k, out = _operands(a, b, layout, out)
-    s = stream if stream is not None else torch.cuda.current_stream(a.device)
     fn = globals()[f"gemm_f16_{layout}_with_config"]
-    with torch.cuda.device(a.device):
-        fn(m, n, k, a.data_ptr(), b.data_ptr(), out.data_ptr(), s.cuda_stream,
+    with _on_device(a):
+        fn(m, n, k, a.data_ptr(), b.data_ptr(), out.data_ptr(), _stream_handle(a, stream),
            -1 if config is None else config, swizzle, grid, epilogue)
     return out
 
@@ -443,7 +475,7 @@ def autotune(a, b, layout: str = "nt", iters: int = 10, out=None, workspace=None
 
     m, n, k, out = _operands(a, b, layout, out)
     code = LAYOUT_CODES[layout]
-    with torch.cuda.device(a.device):
+    with _on_device(a):
         cus = gemm_f16_device_cus()
     aligned = a.data_ptr() % 16 == 0 and b.data_ptr() % 16 == 0
     _, need = gemm_f16_autotune_candidates(code, m, n, k, cus, aligned, 0)
@@ -452,11 +484,10 @@ def autotune(a, b, layout: str = "nt", iters: int = 10, out=None, workspace=None
     elif not workspace.is_cuda or workspace.device != a.device:
         raise ValueError("workspace must be a tensor on a's device")
     ws_bytes = workspace.numel() * workspace.element_size()
-    s = stream if stream is not None else torch.cuda.current_stream(a.device)
-    with torch.cuda.device(a.device):
+    with _on_device(a):
         best, entries = gemm_f16_autotune(code, m, n, k, a.data_ptr(), b.data_ptr(),
                                           out.data_ptr(), workspace.data_ptr(), ws_bytes, iters,
-                                          s.cuda_stream)
+                                          _stream_handle(a, stream))
     return Tuned(layout, best, entries, out)
 
 
