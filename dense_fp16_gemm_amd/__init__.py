@@ -378,7 +378,7 @@ def gemm_nt(a, b, out=None, config: int | None = None, swizzle: int = 0, grid: i
         raise ValueError("out must be a contiguous float16 [M, N] tensor on a's device")
     with _on_device(a):
         s = _stream_handle(a, stream)
-        if config is None and epilogue < 0:
+        if config is None and swizzle <= 0 and grid <= 0 and epilogue < 0:
             gemm_f16_nt(m, n, k, a.data_ptr(), b.data_ptr(), out.data_ptr(), s)
         else:
             gemm_f16_nt_with_config(m, n, k, a.data_ptr(), b.data_ptr(), out.data_ptr(),

@@ -246,6 +246,24 @@ def test_determinism_and_launch_shape_independence(g):
         assert_bit_exact(run_gpu(g, a, b, config=0, grid=grid), first, f"grid {grid}")
 
 
+def test_gemm_nt_passes_swizzle_and_grid_without_a_config(g, monkeypatch):
+    # a raster width or grid given alone must reach the library (the plain
+    # entry point takes neither); results stay bit-identical
+    a, b = workloads.make_inputs(700, 600, 512, "int2", 1.0, seed=53)
+    first = run_gpu(g, a, b)
+    seen = []
+    real = g.gemm_f16_nt_with_config
+
+    def spy(*args):
+        seen.append(args[-4:])   # config, swizzle, grid, epilogue
+        return real(*args)
+
+    monkeypatch.setattr(g, "gemm_f16_nt_with_config", spy)
+    assert_bit_exact(run_gpu(g, a, b, swizzle=3), first, "swizzle 3, planned config")
+    assert_bit_exact(run_gpu(g, a, b, grid=5), first, "grid 5, planned config")
+    assert seen == [(-1, 3, 0, -1), (-1, 0, 5, -1)]
+
+
 def test_page_mae_statistic(g):
     """K = 8192 with unit-variance outputs: the mean |error| against the exact
     sum must sit at the pages' fp32-accumulation figure, 0.00014 (page 6,
