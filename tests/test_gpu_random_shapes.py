@@ -60,3 +60,29 @@ def test_random_shapes_bit_exact(g, oracle_mod, lay, split):
         torch.cuda.synchronize()
         assert_bit_exact(out.cpu().numpy(), oracle_mod.gemm(a_mk, b_nk),
                          f"{lay} split={split} {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("lay, shape, tile", [
+    ("nt", (2000, 3000, 776), (256, 128)),
+    ("nn", (2000, 3000, 776), (256, 128)),
+    ("tn", (2000, 3000, 776), (256, 128)),
+    ("tt", (2000, 3000, 776), (256, 128)),
+    ("nt", (1000, 3000, 1000), (128, 128)),
+])
+def test_plans_the_time_model_overrides(g, oracle_mod, lay, shape, tile):
+    # shapes where the planner's time model replaces the area rule's tile:
+    # the plain entry point runs the model's configuration, bit-exact
+    import torch
+
+    m, n, k = shape
+    plan = getattr(g, f"gemm_f16_{lay}_plan")(m, n, k, g.gemm_f16_device_cus())
+    assert (plan.block_m, plan.block_n) == tile
+    a_mk, b_nk = workloads.make_inputs(m, n, k, "int2", 1.0, seed=433)
+    a = np.ascontiguousarray(a_mk.T) if lay[0] == "t" else a_mk
+    b = np.ascontiguousarray(b_nk.T) if lay[1] == "n" else b_nk
+    print(f"  gpu planned {lay} {m}x{n}x{k} config {plan.config_id}", file=sys.stderr, flush=True)
+    ta, tb = torch.from_numpy(a).cuda(), torch.from_numpy(b).cuda()
+    out = torch.full((m, n), float("nan"), dtype=torch.float16, device="cuda")
+    g.gemm(ta, tb, lay, out=out)
+    torch.cuda.synchronize()
+    assert_bit_exact(out.cpu().numpy(), oracle_mod.gemm(a_mk, b_nk), f"{lay} {m}x{n}x{k}")
