@@ -402,7 +402,8 @@ def gemm_splitk(a, b, layout: str = "nt", splits: int = 0, out=None, workspace=N
     if config is not None and splits > 1:
         # a forced configuration may split into more ranges than the planner's
         need = max(need, gemm_f16_splitk_workspace_bytes(m, n, splits))
-    if workspace is None:
+    own = workspace is None
+    if own:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=a.device)
     elif not workspace.is_cuda or workspace.device != a.device:
         raise ValueError("workspace must be a tensor on a's device")
@@ -411,6 +412,10 @@ def gemm_splitk(a, b, layout: str = "nt", splits: int = 0, out=None, workspace=N
         globals()[f"gemm_f16_{layout}_splitk_with_config"](
             m, n, k, a.data_ptr(), b.data_ptr(), out.data_ptr(), splits, workspace.data_ptr(),
             ws_bytes, _stream_handle(a, stream), -1 if config is None else config)
+    if own and stream is not None:
+        # the allocator gave the workspace to the current stream; it is used
+        # on `stream`, so it must not be reused before that work is done
+        workspace.record_stream(stream)
     return out
 
 
@@ -515,11 +520,40 @@ def matmul_layout(a, b):
     return la + lb, xa, xb
 
 
+# split counts the split planner chose, per (layout, M, N, K, device)
+_split_choice: dict = {}
+
+
+def matmul_splits(lay: str, m: int, n: int, k: int, a) -> int:
+    """The split count matmul() runs (layout, M, N, K) with on a's device:
+    the split planner's choice for 16-byte aligned operands (1: no split).
+    Cached per shape, so a repeated call costs a dictionary lookup."""
+    key = (lay, m, n, k, a.get_device())
+    got = _split_choice.get(key)
+    if got is None:
+        with _on_device(a):
+            cus = gemm_f16_device_cus()
+        _, got, _ = globals()[f"gemm_f16_{lay}_splitk_plan"](m, n, k, cus, 0)
+        if len(_split_choice) >= 1024:
+            _split_choice.clear()
+        _split_choice[key] = got
+    return got
+
+
 def matmul(a, b, out=None, stream=None):
     """C = a @ b for fp16 GPU matrices a [M,K] and b [K,N], each row-major or
     a transposed view of a row-major matrix (see matmul_layout): the storage
-    picks gemm_f16_nn, gemm_f16_nt, gemm_f16_tn or gemm_f16_tt, with no copy."""
+    picks gemm_f16_nn, gemm_f16_nt, gemm_f16_tn or gemm_f16_tt, with no copy.
+
+    Where the split planner splits K (few output tiles, a long K), the call
+    runs gemm_f16_<layout>_splitk with its fp32 workspace taken from torch's
+    allocator: much faster there, and the result differs from the unsplit
+    one only in the fp32 rounding of each sum (none for integer sums that
+    fp32 holds exactly).  Use gemm() for the unsplit path."""
     lay, xa, xb = matmul_layout(a, b)
     if a.shape[1] != b.shape[0]:
         raise ValueError(f"shape mismatch: a{tuple(a.shape)} b{tuple(b.shape)}")
+    m, k, n = a.shape[0], a.shape[1], b.shape[1]
+    if m > 0 and n > 0 and k > 0 and a.is_cuda and matmul_splits(lay, m, n, k, a) > 1:
+        return gemm_splitk(xa, xb, lay, out=out, stream=stream)
     return gemm(xa, xb, lay, out=out, stream=stream)

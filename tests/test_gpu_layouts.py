@@ -208,3 +208,29 @@ def test_matmul_picks_the_layout_from_strides(g, oracle_mod, ta, tb):
     c = g.matmul(ga, gb)
     torch.cuda.synchronize()
     assert_bit_exact(c.cpu().numpy(), oracle_mod.gemm(a_mk, b_nk), f"matmul ta={ta} tb={tb}")
+
+
+@pytest.mark.parametrize("ta,tb", [(False, False), (False, True), (True, False), (True, True)])
+@pytest.mark.parametrize("side_stream", [False, True])
+def test_matmul_splits_an_underfilled_long_k(g, oracle_mod, ta, tb, side_stream):
+    """Few output tiles and a long K: matmul runs the split over K (workspace
+    from torch's allocator), bit-exact on integer inputs, on the current
+    stream or on a stream passed in."""
+    import torch
+
+    m, n, k = 256, 256, 16384
+    a_mk, b_nk = workloads.make_inputs(m, n, k, "int2", 1.0, seed=367)
+    ga = torch.from_numpy(a_mk.T.copy()).cuda().t() if ta else torch.from_numpy(a_mk).cuda()
+    gb = torch.from_numpy(b_nk.copy()).cuda().t() if tb else torch.from_numpy(b_nk.T.copy()).cuda()
+    lay = g.matmul_layout(ga, gb)[0]
+    assert g.matmul_splits(lay, m, n, k, ga) > 1
+    _say(f"  gpu matmul split {lay} side_stream={side_stream}")
+    if side_stream:
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        c = g.matmul(ga, gb, stream=s)
+        s.synchronize()
+    else:
+        c = g.matmul(ga, gb)
+    torch.cuda.synchronize()
+    assert_bit_exact(c.cpu().numpy(), oracle_mod.gemm(a_mk, b_nk), f"matmul split {lay}")
