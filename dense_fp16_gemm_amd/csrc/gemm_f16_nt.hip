@@ -257,6 +257,11 @@ struct Cfg {
     static_assert(MI == 32 || MI == 16, "MFMA is 32x32x16 or 16x16x32");
     static_assert(MI == 32 || CHUNKS == 8, "16x16x32 fragments need 128-byte rows");
     static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be whole 32-row blocks");
+    // No configuration has a single wave row.  Trial instances with WM = 1
+    // and 32 x 32 x 16 MFMAs (32 x 64 and 32 x 128 tiles, K 128 per stage)
+    // returned wrong results, for a cause not found (one with 16 x 16 x 32
+    // MFMAs was correct), so the template accepts none.
+    static_assert(WM >= 2, "at least two wave rows");
     static_assert((AL ? BK % (A_DMA_ROWS * WAVES) : BM % (DMA_ROWS * WAVES)) == 0 &&
                       (BL ? BK % (B_DMA_ROWS * WAVES) : BN % (DMA_ROWS * WAVES)) == 0,
                   "every wave issues the same number of DMA instructions");
