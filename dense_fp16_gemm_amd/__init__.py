@@ -65,6 +65,9 @@ def library_path() -> str:
 def load():
     """Load libgemm_f16.so (built in-tree); raise if it is not there."""
     global _lib
+    lib = _lib
+    if lib is not None:   # loaded: no lock on the per-call path
+        return lib
     with _lock:
         if _lib is not None:
             return _lib
