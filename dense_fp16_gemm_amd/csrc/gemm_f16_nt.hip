@@ -1628,6 +1628,109 @@ void gemm_f16_nt_pc_kernel(Params p)
 }
 
 // ---------------------------------------------------------------------------
+// Kernel, B streamed through registers (few rows of A)
+// ---------------------------------------------------------------------------
+// With a handful of A rows each B element is used a handful of times, and the
+// GEMM is a stream of B from HBM.  The LDS ring then limits it: what a CU
+// keeps in flight is what its stages hold, and for M = 1 most of each stage
+// is zero rows of the A tile.  Here one wave owns a 16 x 16 output tile (16
+// rows of A, zero past M, and 16 rows of B) and loads both fragments of every
+// K step straight from global memory in the MFMA's operand layout: lane l
+// reads 16 bytes of row l % 16 at k = 32 s + 8 (l / 16), so one load covers
+// 64 bytes of each of 16 rows.  Blocks of D steps are double-buffered: the
+// next block's loads fly while this block's MFMAs run.
+//
+// The MFMA is the 16 x 16 x 32 one of the other configurations, stepping K
+// in the same ascending 32-wide steps into one fp32 accumulator per element
+// from +0, so every result bit equals theirs.  Chunks past K load as zeros
+// (K is a multiple of 8, so a chunk never straddles K); lanes past M or N
+// read row 0, whose products land only in outputs that are not stored.  A
+// persistent loop walks the tiles row-major (t = blockIdx.x + i gridDim.x)
+// for any grid; any M is computed, though only a few rows of A use it well.
+template <int D>
+__global__ __launch_bounds__(64) void gemm_f16_nt_stream_kernel(Params p)
+{
+    const int lane = threadIdx.x;
+    const int r = lane & 15;    // operand row: B row n0 + r, A row m0 + r
+    const int kq = lane >> 4;   // which 8-element chunk of the 32-wide K step
+    const int32_t M = p.M, N = p.N, K = p.K;
+    const int steps = (K + 31) / 32;
+    const int blocks = (K / 32) / D;   // blocks of D steps whose chunks all lie inside K
+    const half8_t zero = {};
+    for (int32_t t = blockIdx.x; t < p.tiles; t += gridDim.x) {
+        const int32_t tm = t / p.tiles_n;
+        const int32_t tn = t - tm * p.tiles_n;
+        const int32_t m = tm * 16 + r, n = tn * 16 + r;
+        const bool a_ok = m < M, b_ok = n < N;
+        const uint16_t *arow = p.A + static_cast<int64_t>(a_ok ? m : 0) * K + kq * 8;
+        const uint16_t *brow = p.B + static_cast<int64_t>(b_ok ? n : 0) * K + kq * 8;
+        f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        // whole blocks, double-buffered: block j + 1's loads are in flight
+        // while block j's MFMAs (one accumulator, so a dependent chain) run
+        half8_t af[2][D], bf[2][D];
+        // Unconditional loads (a lane past M or N reads row 0 instead): a
+        // load under a branch would make the compiler's vmcnt bookkeeping
+        // wait for the other buffer's loads as well.  Row m of A only feeds
+        // output column m and row n of B output row n, so those lanes only
+        // produce outputs that are never stored.
+        auto load = [&](int buf, int j) {
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                bf[buf][d] = *reinterpret_cast<const half8_t *>(brow + (j * D + d) * 32);
+                af[buf][d] = *reinterpret_cast<const half8_t *>(arow + (j * D + d) * 32);
+            }
+        };
+        auto mma = [&](int buf) {
+#pragma unroll
+            for (int d = 0; d < D; ++d)
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(bf[buf][d], af[buf][d], acc, 0, 0, 0);
+        };
+        // Every load inside is unconditional, so the compiler's waits on a
+        // buffer's loads leave the other buffer's in flight (a load that
+        // might be skipped would make them wait for everything).  The last
+        // trip's prefetch repeats the last block where there is no next one.
+        if (blocks > 0) {
+            load(0, 0);
+            int j = 0;
+            for (; j + 2 <= blocks; j += 2) {
+                load(1, j + 1);
+                mma(0);
+                load(0, j + 2 < blocks ? j + 2 : blocks - 1);
+                mma(1);
+            }
+            if (j < blocks) mma(0);
+        }
+        // the remaining steps, up to and past K: chunks at or past K are zeros
+        for (int s0 = blocks * D; s0 < steps; s0 += D) {
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                const int s = s0 + d;
+                const bool in = s < steps && s * 32 + kq * 8 < K;
+                bf[0][d] = in ? *reinterpret_cast<const half8_t *>(brow + s * 32) : zero;
+                af[0][d] = in ? *reinterpret_cast<const half8_t *>(arow + s * 32) : zero;
+            }
+#pragma unroll
+            for (int d = 0; d < D; ++d)
+                if (s0 + d < steps)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(bf[0][d], af[0][d], acc, 0, 0, 0);
+        }
+        // lane l holds C[m0 + l % 16][n0 + 4 (l / 16) + 0..3]
+        if (a_ok) {
+            const int32_t c0 = tn * 16 + kq * 4;
+            uint16_t *crow = p.C + static_cast<int64_t>(m) * N;
+            const half4_t h = __builtin_convertvector(acc, half4_t);
+            if (c0 + 3 < N) {
+                __builtin_memcpy(crow + c0, &h, 8);   // any 2-byte alignment
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (c0 + e < N) reinterpret_cast<_Float16 *>(crow)[c0 + e] = h[e];
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Split-K reduction
 // ---------------------------------------------------------------------------
 // C = fp16_rne(W_0 + W_1 + ... + W_{splits-1}), summed in fp32 in split order,
@@ -1912,6 +2015,15 @@ KernelEntry entry_pc(int swizzle, float rate, float split_rate)
                        2 * CF::THREADS, swizzle, rate, split_rate, 0, 0, 1, 0};
 }
 
+// The register-streaming kernel: 16 x 16 tiles, K 32 per MFMA step, no LDS
+// ring (stages and LDS 0), one wave per workgroup, never split.
+template <int D>
+KernelEntry entry_stream(float rate)
+{
+    return KernelEntry{reinterpret_cast<const void *>(&gemm_f16_nt_stream_kernel<D>), nullptr,
+                       16, 16, 32, 1, 0, 0, 64, 1, rate, 0.0f, 0, 0, 8, 0};
+}
+
 template <class CF, int LA = 0, int LB = 0>
 KernelEntry entry_general(int swizzle)
 {
@@ -1997,13 +2109,16 @@ static const KernelEntry kKernels[] = {
     // 814 against 937 and 857 us), so it takes 2's place in both planners
     // (split_rate: 2's scaled by the unsplit gain at 2048 x 4096 x 8192, 1.11)
     entry_pc<Cfg<256, 128, 64, 2, 2, 3, 16, 0, 0, 1>>(8, 0.87f, 0.754f),
-    // 43-45: the general kernel for NN, TT and TN (loads along the operand's
+    // 43: B streamed through registers for a few rows of A (planned for M <=
+    // 16: see choose_config)
+    entry_stream<12>(0.0f),
+    // 44-46: the general kernel for NN, TT and TN (loads along the operand's
     // contiguous dimension), for arguments the direct-to-LDS kernels of those
     // layouts cannot take
     entry_general<Cfg<128, 128, 32, 2, 2, 2>, 0, 1>(8),
     entry_general<Cfg<128, 128, 32, 2, 2, 2>, 1, 0>(8),
     entry_general<Cfg<128, 128, 32, 2, 2, 2>, 1, 1>(8),
-    // 46: the general kernel, 4 waves of 64x64, two register-staged buffers of
+    // 47: the general kernel, 4 waves of 64x64, two register-staged buffers of
     // K 32; planned only when the direct-to-LDS path cannot run
     entry_general<Cfg<128, 128, 32, 2, 2, 2>>(8),
 };
@@ -2149,7 +2264,37 @@ static int choose_config_search(int64_t M, int64_t N, int64_t K, int32_t num_cus
     return rule_time > kModelMargin * alt_time ? alt : best;
 }
 
-// choose_config_search behind a per-thread cache of the last few decisions
+// The register-streaming configuration (no LDS ring) and when the plain plan
+// takes it: NT, at most kStreamMaxM rows of A, and a plan whose tiles would
+// fill at most a quarter of the CUs.  Timed on one MI355X in captured graphs
+// against the plan it replaces (M = 1 / 4 / 8 / 16): 4096 x 4096 8.4 / 9.5 /
+// 10.1 / 11.5 us against 15.6-15.7; N = 4096, K = 14336 24.1 / 25.6 / 28.0 /
+// 32.4 us against 45.4-45.7.  With more tiles the tile kernels keep up (N =
+// 8192 at K = 8192: within -7..+1%; N = 14336 at K = 4096 they are faster),
+// and from M = 32 on streaming loses (B is read again for every 16 rows of A).
+constexpr int64_t kStreamMaxM = 16;
+
+static int stream_config()
+{
+    static const int id = [] {
+        for (int i = 0; i < kNumKernels; ++i)
+            if (kKernels[i].stages == 0) return i;
+        return -1;
+    }();
+    return id;
+}
+
+static int choose_config_planned(int64_t M, int64_t N, int64_t K, int32_t num_cus, int32_t layout)
+{
+    const int id = choose_config_search(M, N, K, num_cus, layout);
+    const int st = stream_config();
+    if (layout == 0 && st >= 0 && id >= 0 && M <= kStreamMaxM && K > 0 &&
+        cdiv(M, kKernels[id].block_m) * cdiv(N, kKernels[id].block_n) * 4 <= num_cus)
+        return st;
+    return id;
+}
+
+// choose_config_planned behind a per-thread cache of the last few decisions
 // (the search prices every configuration of the layout), so a caller that
 // repeats a shape pays for it once.
 static int choose_config(int64_t M, int64_t N, int64_t K, int32_t num_cus, int32_t layout = 0)
@@ -2164,7 +2309,7 @@ static int choose_config(int64_t M, int64_t N, int64_t K, int32_t num_cus, int32
     for (const Choice &c : cache)
         if (c.id >= 0 && c.M == M && c.N == N && c.K == K && c.cus == num_cus && c.layout == layout)
             return c.id;
-    const int id = choose_config_search(M, N, K, num_cus, layout);
+    const int id = choose_config_planned(M, N, K, num_cus, layout);
     cache[next] = Choice{M, N, K, num_cus, layout, id};
     next = (next + 1) % 4;
     return id;
@@ -2628,6 +2773,7 @@ static int scratch_address(void **out)
 // count (ranges of whole K slices) and repeated effective counts are dropped.
 constexpr int32_t kTuneSplits[] = {2, 3, 4, 6, 8, 12, 16, 24, 32, 48, 64};
 constexpr int64_t kTuneMinSplitK = 256;   // K per range the tuner goes down to
+constexpr int64_t kStreamTuneMaxM = 64;   // M up to which the streaming kernel is tried
 
 // The (configuration, split) pairs the tuner times for these arguments, in
 // configuration order, each configuration's unsplit run first.  Splits are
@@ -2646,6 +2792,8 @@ static void tune_candidates(int32_t layout, int64_t M, int64_t N, int64_t K, int
     for (int id = 0; id < kNumKernels; ++id) {
         const KernelEntry &e = kKernels[id];
         if (e.layout != layout || (!fast && !e.general)) continue;
+        // the register-streaming kernel re-reads B for every 16 rows of A
+        if (e.stages == 0 && M > kStreamTuneMaxM) continue;
         out.push_back(gemm_f16_tune_entry_t{id, 1, GEMM_F16_OK, -1.0f});
         if (e.general || !e.fn_split || K <= 0) continue;
         const int64_t tiles = cdiv(M, e.block_m) * cdiv(N, e.block_n);

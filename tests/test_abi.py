@@ -91,6 +91,11 @@ def test_config_table(g):
     for cid in range(n):
         info = g.gemm_f16_nt_config_info(cid)
         assert info.config_id == cid
+        if info.stages == 0:
+            # the register-streaming kernel: 16 x 16 tiles, one wave, no LDS
+            assert (info.block_m, info.block_n, info.block_k, info.waves, info.lds_bytes) == \
+                (16, 16, 32, 1, 0) and info.layout == "nt"
+            continue
         assert info.block_k in (32, 64, 128)
         # (the last entry, the general kernel, stages through registers into
         # two LDS buffers with the same layout)
@@ -163,6 +168,25 @@ def test_plain_plan_keeps_the_rule_within_the_model_margin(g, shape, cid):
     # preference for the 256 x 128 tile (8%) lies within its error and the
     # 256 x 256 tile measures faster
     assert g.gemm_f16_nt_plan(*shape, 256).config_id == cid
+
+
+@pytest.mark.parametrize("shape, stream", [
+    ((1, 4096, 4096), True), ((16, 4096, 4096), True), ((8, 4096, 14336), True),
+    ((1, 1, 8), True),
+    ((32, 4096, 4096), False),      # B would be read twice
+    ((1, 16384, 16384), False),     # the tile kernels fill the CUs
+    ((1, 14336, 4096), False),
+])
+def test_plain_plan_streams_b_for_few_rows_of_a(g, shape, stream):
+    # at most 16 rows of A and tiles that would fill at most a quarter of the
+    # CUs: the register-streaming configuration (no LDS ring)
+    p = g.gemm_f16_nt_plan(*shape, 256)
+    assert (g.gemm_f16_nt_config_info(p.config_id).stages == 0) == stream
+    if stream:
+        assert (p.block_m, p.block_n) == (16, 16)
+        assert p.tiles == p.tiles_m * p.tiles_n and p.grid == p.tiles
+    # the other layouts never stream
+    assert g.gemm_f16_nn_plan(*shape, 256).config_id != p.config_id or not stream
 
 
 def _order(g, plan):

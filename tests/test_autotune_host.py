@@ -75,11 +75,14 @@ def test_candidates_well_formed(lay, shape):
 @pytest.mark.parametrize("lay", list(g.LAYOUT_CODES))
 def test_candidates_cover_every_configuration_of_the_layout(lay):
     code = g.LAYOUT_CODES[lay]
-    cand, _ = g.gemm_f16_autotune_candidates(code, 1024, 1024, 4096, CUS, True, 0)
-    ids = {e.config_id for e in cand}
-    want = {i for i, c in enumerate(configs()) if c.layout == lay}
-    assert ids == want
-    assert all(e.splits == 1 for e in cand), "no workspace: no split candidates"
+    # the register-streaming kernel (no LDS ring) only for a few rows of A
+    for m, stream in ((1024, False), (64, True), (16, True)):
+        cand, _ = g.gemm_f16_autotune_candidates(code, m, 1024, 4096, CUS, True, 0)
+        ids = {e.config_id for e in cand}
+        want = {i for i, c in enumerate(configs())
+                if c.layout == lay and (stream or c.stages > 0)}
+        assert ids == want
+        assert all(e.splits == 1 for e in cand), "no workspace: no split candidates"
 
 
 def test_workspace_bound_drops_only_the_larger_splits():

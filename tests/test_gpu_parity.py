@@ -111,7 +111,7 @@ def test_parity_every_config(g, oracle_mod, shape):
                 assert_bit_exact(got, first, f"{shape} config {cid} epilogue {epi} vs first")
 
 
-@pytest.mark.parametrize("cid", [0, 1, 2, 3, 4, 5, 9, 11, 17, 18, 19, 20, 21, 22, 23, 42])
+@pytest.mark.parametrize("cid", [0, 1, 2, 3, 4, 5, 9, 11, 17, 18, 19, 20, 21, 22, 23, 42, 43])
 @pytest.mark.parametrize("k", [8, 24, 32, 40, 64, 72, 128, 136, 160, 192, 200, 256, 264, 328])
 def test_short_and_ragged_k(g, oracle_mod, cid, k):
     """K with fewer slices than stages, exactly the stages, one more, and
@@ -121,7 +121,7 @@ def test_short_and_ragged_k(g, oracle_mod, cid, k):
     assert_within_tolerance(got, oracle_mod.gemm(a, b), f"k={k} config {cid}")
 
 
-@pytest.mark.parametrize("cid", [0, 2, 4, 5, 11, 17, 18, 19, 20, 21, 22, 23, 42])
+@pytest.mark.parametrize("cid", [0, 2, 4, 5, 11, 17, 18, 19, 20, 21, 22, 23, 42, 43])
 def test_edge_m_n(g, oracle_mod, cid):
     info = g.gemm_f16_nt_config_info(cid)
     bm, bn = info.block_m, info.block_n
@@ -143,12 +143,29 @@ def test_unaligned_c(g, oracle_mod, c_offset, epi, cid):
     assert_within_tolerance(got, oracle_mod.gemm(a, b), f"c_offset {c_offset} epilogue {epi}")
 
 
-@pytest.mark.parametrize("cid", [None, 11, 42])
+@pytest.mark.parametrize("cid", [None, 11, 42, 43])
 def test_k_zero_writes_positive_zero(g, cid):
     a = np.zeros((70, 0), np.float16)
     b = np.zeros((90, 0), np.float16)
     got = run_gpu(g, a, b, config=cid)
     assert np.all(got.view(np.uint16) == 0)
+
+
+STREAM = 43   # B streamed through registers (no LDS ring)
+
+
+@pytest.mark.parametrize("m", [1, 2, 7, 16, 17, 40])
+@pytest.mark.parametrize("c_offset", [0, 1, 3])
+def test_streaming_configuration_small_m(g, oracle_mod, m, c_offset):
+    """The register-streaming configuration on a few rows of A, with N and K
+    tails (K = 54 steps of 32 and 8 more) and C at 2-, 4- and 8-byte
+    alignment: within tolerance of the oracle and bit-identical to the
+    headline configuration (the same MFMA and K order)."""
+    assert g.gemm_f16_nt_config_info(STREAM).stages == 0
+    a, b = workloads.make_inputs(m, 1000, 1736, "normal", 0.05, seed=500 + m)
+    got = run_gpu(g, a, b, config=STREAM, c_offset=c_offset)
+    assert_within_tolerance(got, oracle_mod.gemm(a, b), f"stream m={m} c_offset={c_offset}")
+    assert_bit_exact(got, run_gpu(g, a, b, config=11), f"stream m={m} vs config 11")
 
 
 def test_m_or_n_zero_is_a_no_op(g):
