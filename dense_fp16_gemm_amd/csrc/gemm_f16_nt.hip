@@ -1634,8 +1634,8 @@ void gemm_f16_nt_pc_kernel(Params p)
 // GEMM is a stream of B from HBM.  The LDS ring then limits it: what a CU
 // keeps in flight is what its stages hold, and for M = 1 most of each stage
 // is zero rows of the A tile.  Here one wave owns a 16 x 16 output tile (16
-// rows of A, zero past M, and 16 rows of B) and loads both fragments of every
-// K step straight from global memory in the MFMA's operand layout: lane l
+// rows of A and 16 rows of B) and loads both fragments of every K step
+// straight from global memory in the MFMA's operand layout: lane l
 // reads 16 bytes of row l % 16 at k = 32 s + 8 (l / 16), so one load covers
 // 64 bytes of each of 16 rows.  Blocks of D steps are double-buffered: the
 // next block's loads fly while this block's MFMAs run.
@@ -2110,7 +2110,7 @@ static const KernelEntry kKernels[] = {
     // (split_rate: 2's scaled by the unsplit gain at 2048 x 4096 x 8192, 1.11)
     entry_pc<Cfg<256, 128, 64, 2, 2, 3, 16, 0, 0, 1>>(8, 0.87f, 0.754f),
     // 43: B streamed through registers for a few rows of A (planned for M <=
-    // 16: see choose_config)
+    // 16: see choose_config_planned)
     entry_stream<12>(0.0f),
     // 44-46: the general kernel for NN, TT and TN (loads along the operand's
     // contiguous dimension), for arguments the direct-to-LDS kernels of those
