@@ -2273,6 +2273,7 @@ static int choose_config_search(int64_t M, int64_t N, int64_t K, int32_t num_cus
 // 8192 at K = 8192: within -7..+1%; N = 14336 at K = 4096 they are faster),
 // and from M = 32 on streaming loses (B is read again for every 16 rows of A).
 constexpr int64_t kStreamMaxM = 16;
+constexpr int64_t kStreamSplitMaxK = 2048;   // K up to which no split beats it
 
 static int stream_config()
 {
@@ -2459,6 +2460,16 @@ static void choose_split_search(int64_t M, int64_t N, int64_t K, int32_t cus, in
                                 int32_t splits, int *id_out, int32_t *splits_out, int32_t layout)
 {
     const int plain = config_id >= 0 ? config_id : choose_config(M, N, K, cus, layout);
+    // The cost model has no rate for the register-streaming plan.  Measured
+    // against the split the model picks (one box, captured graphs, M in {1,
+    // 2, 8, 16}, N from 256 to 4096): at K = 2048 it ran 0.66-0.84 of the
+    // split's time on all 24 shapes, at K = 8192 it won 2 of 24 and at
+    // K = 32768 none (one wave per 16 rows of B is too few for a long K).
+    if (splits <= 0 && config_id < 0 && plain == stream_config() && K <= kStreamSplitMaxK) {
+        *id_out = plain;
+        *splits_out = 1;
+        return;
+    }
     double best = 0.0;
     int best_id = -1;
     int64_t best_eff = 1;

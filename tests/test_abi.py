@@ -189,6 +189,18 @@ def test_plain_plan_streams_b_for_few_rows_of_a(g, shape, stream):
     assert g.gemm_f16_nn_plan(*shape, 256).config_id != p.config_id or not stream
 
 
+@pytest.mark.parametrize("shape, split", [((1, 4096, 2048), False), ((16, 2048, 2048), False),
+                                          ((1, 4096, 8192), True), ((8, 4096, 32768), True)])
+def test_split_planner_keeps_the_streaming_plan_for_short_k(g, shape, split):
+    # short K: the streaming plan unsplit; long K: a split over K
+    p = g.gemm_f16_nt_plan(*shape, 256)
+    assert g.gemm_f16_nt_config_info(p.config_id).stages == 0
+    sp, eff, ws = g.gemm_f16_nt_splitk_plan(*shape, 256, 0)
+    assert (eff > 1) == split
+    if not split:
+        assert sp.config_id == p.config_id and ws == 0
+
+
 def _order(g, plan):
     return [g.gemm_f16_nt_tile_of_slot(plan, s) for s in range(plan.tiles)]
 
