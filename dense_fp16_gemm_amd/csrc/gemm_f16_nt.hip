@@ -614,7 +614,7 @@ struct Step {
             int dw = -1;
 #pragma unroll
             for (int w = 0; w < NLD; ++w)
-                if ((w * NM) / NLD == t) dw = w;
+                if ((w * NM) / (NLD > 0 ? NLD : 1) == t) dw = w;   // no DMA: no trip
             static_assert(!ZERO || (!FUSED && CF::MI == 16), "zero start: hand-issued MFMAs, no fused DMA");
             if constexpr (FUSED) {
                 static_assert(CF::MI == 16 && NLD <= NM, "fused DMA: hand-issued MFMAs, one DMA per slot");
@@ -1687,16 +1687,24 @@ __global__ __launch_bounds__(64) void gemm_f16_nt_stream_kernel(Params p)
         };
         // Every load inside is unconditional, so the compiler's waits on a
         // buffer's loads leave the other buffer's in flight (a load that
-        // might be skipped would make them wait for everything).  The last
-        // trip's prefetch repeats the last block where there is no next one.
+        // might be skipped would make them wait for everything).  The
+        // scheduling barriers keep each block's loads together ahead of the
+        // other block's MFMAs: left to itself the compiler spreads them
+        // through the MFMA chain, and waits inside the chain then drain the
+        // queue to a few loads.  The last trip's prefetch repeats the last
+        // block where there is no next one.
         if (blocks > 0) {
             load(0, 0);
             int j = 0;
             for (; j + 2 <= blocks; j += 2) {
                 load(1, j + 1);
+                __builtin_amdgcn_sched_barrier(0);
                 mma(0);
+                __builtin_amdgcn_sched_barrier(0);
                 load(0, j + 2 < blocks ? j + 2 : blocks - 1);
+                __builtin_amdgcn_sched_barrier(0);
                 mma(1);
+                __builtin_amdgcn_sched_barrier(0);
             }
             if (j < blocks) mma(0);
         }
