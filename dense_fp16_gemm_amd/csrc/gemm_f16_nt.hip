@@ -1647,23 +1647,37 @@ void gemm_f16_nt_pc_kernel(Params p)
 // read row 0, whose products land only in outputs that are not stored.  A
 // persistent loop walks the tiles row-major (t = blockIdx.x + i gridDim.x)
 // for any grid; any M is computed, though only a few rows of A use it well.
-template <int D>
+//
+// SPLIT: unit t is tile t mod (tiles_m tiles_n) over K range [s k_split,
+// min((s + 1) k_split, K)), s = t / (tiles_m tiles_n), and its fp32 sums go
+// to partial s of W (an M x N row-major matrix) for the reduction kernel.
+// k_split is a multiple of 32, so every range starts on a step and each
+// unit's steps are those of a GEMM of K = its range length.
+template <int D, bool SPLIT>
 __global__ __launch_bounds__(64) void gemm_f16_nt_stream_kernel(Params p)
 {
     const int lane = threadIdx.x;
     const int r = lane & 15;    // operand row: B row n0 + r, A row m0 + r
     const int kq = lane >> 4;   // which 8-element chunk of the 32-wide K step
-    const int32_t M = p.M, N = p.N, K = p.K;
-    const int steps = (K + 31) / 32;
-    const int blocks = (K / 32) / D;   // blocks of D steps whose chunks all lie inside K
+    const int32_t M = p.M, N = p.N, K = p.K;   // K: the operands' row length
+    const int32_t tiles_mn = p.tiles_m * p.tiles_n;
     const half8_t zero = {};
     for (int32_t t = blockIdx.x; t < p.tiles; t += gridDim.x) {
-        const int32_t tm = t / p.tiles_n;
-        const int32_t tn = t - tm * p.tiles_n;
+        int32_t u = t, sp = 0, k0 = 0, klen = K;
+        if constexpr (SPLIT) {
+            sp = t / tiles_mn;
+            u = t - sp * tiles_mn;
+            k0 = sp * p.k_split;
+            klen = min(p.k_split, K - k0);
+        }
+        const int steps = (klen + 31) / 32;
+        const int blocks = (klen / 32) / D;   // blocks of D steps whose chunks all lie in range
+        const int32_t tm = u / p.tiles_n;
+        const int32_t tn = u - tm * p.tiles_n;
         const int32_t m = tm * 16 + r, n = tn * 16 + r;
         const bool a_ok = m < M, b_ok = n < N;
-        const uint16_t *arow = p.A + static_cast<int64_t>(a_ok ? m : 0) * K + kq * 8;
-        const uint16_t *brow = p.B + static_cast<int64_t>(b_ok ? n : 0) * K + kq * 8;
+        const uint16_t *arow = p.A + static_cast<int64_t>(a_ok ? m : 0) * K + k0 + kq * 8;
+        const uint16_t *brow = p.B + static_cast<int64_t>(b_ok ? n : 0) * K + k0 + kq * 8;
         f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
         // whole blocks, double-buffered: block j + 1's loads are in flight
         // while block j's MFMAs (one accumulator, so a dependent chain) run
@@ -1713,7 +1727,7 @@ __global__ __launch_bounds__(64) void gemm_f16_nt_stream_kernel(Params p)
 #pragma unroll
             for (int d = 0; d < D; ++d) {
                 const int s = s0 + d;
-                const bool in = s < steps && s * 32 + kq * 8 < K;
+                const bool in = s < steps && s * 32 + kq * 8 < klen;
                 bf[0][d] = in ? *reinterpret_cast<const half8_t *>(brow + s * 32) : zero;
                 af[0][d] = in ? *reinterpret_cast<const half8_t *>(arow + s * 32) : zero;
             }
@@ -1723,7 +1737,13 @@ __global__ __launch_bounds__(64) void gemm_f16_nt_stream_kernel(Params p)
                     acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(bf[0][d], af[0][d], acc, 0, 0, 0);
         }
         // lane l holds C[m0 + l % 16][n0 + 4 (l / 16) + 0..3]
-        if (a_ok) {
+        if (SPLIT && a_ok) {
+            const int32_t c0 = tn * 16 + kq * 4;
+            float *wrow = p.W + sp * p.split_stride + static_cast<int64_t>(m) * N;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (c0 + e < N) wrow[c0 + e] = acc[e];
+        } else if (a_ok) {
             const int32_t c0 = tn * 16 + kq * 4;
             uint16_t *crow = p.C + static_cast<int64_t>(m) * N;
             const half4_t h = __builtin_convertvector(acc, half4_t);
@@ -2024,11 +2044,12 @@ KernelEntry entry_pc(int swizzle, float rate, float split_rate)
 }
 
 // The register-streaming kernel: 16 x 16 tiles, K 32 per MFMA step, no LDS
-// ring (stages and LDS 0), one wave per workgroup, never split.
+// ring (stages and LDS 0), one wave per workgroup.
 template <int D>
 KernelEntry entry_stream(float rate)
 {
-    return KernelEntry{reinterpret_cast<const void *>(&gemm_f16_nt_stream_kernel<D>), nullptr,
+    return KernelEntry{reinterpret_cast<const void *>(&gemm_f16_nt_stream_kernel<D, false>),
+                       reinterpret_cast<const void *>(&gemm_f16_nt_stream_kernel<D, true>),
                        16, 16, 32, 1, 0, 0, 64, 1, rate, 0.0f, 0, 0, 8, 0};
 }
 
@@ -2281,7 +2302,6 @@ static int choose_config_search(int64_t M, int64_t N, int64_t K, int32_t num_cus
 // 8192 at K = 8192: within -7..+1%; N = 14336 at K = 4096 they are faster),
 // and from M = 32 on streaming loses (B is read again for every 16 rows of A).
 constexpr int64_t kStreamMaxM = 16;
-constexpr int64_t kStreamSplitMaxK = 2048;   // K up to which no split beats it
 
 static int stream_config()
 {
@@ -2458,6 +2478,38 @@ static bool split_candidate(int id)
     return flags[id];
 }
 
+// The split planner's choice for a register-streaming plan, which its cost
+// model has no rate for.  One CU keeps only so many loads in flight, so
+// where the 16 x 16 tiles occupy few CUs only a split over K adds bandwidth:
+// S ranges of K per tile, S the largest power of two with tiles S <= CUs,
+// S <= kStreamMaxSplits and K / S >= kStreamMinSplitK.  Kept where it beat
+// the model's split of a tile configuration: grids of at most a quarter of
+// the CUs, or K <= kStreamKeepK, or at most kStreamFewM rows of A and
+// K <= kStreamFewMK; elsewhere (more tiles and a long K) false, and the
+// model's split stands.  Timed on one MI355X in captured graphs over M in
+// {1, 4, 8, 16}, N from 256 to 4096 and K from 2048 to 32768 (80 shapes):
+// 0.85 of the model's split's time (geometric mean; 1 x 256 x 32768 9.6
+// against 20.8 us, 1 x 4096 x 4096 7.5 against 9.8), none more than 3%
+// slower.
+constexpr int32_t kStreamMaxSplits = 16;
+constexpr int64_t kStreamMinSplitK = 2048;
+constexpr int64_t kStreamKeepK = 2048;
+constexpr int64_t kStreamFewM = 4;
+constexpr int64_t kStreamFewMK = 8192;
+
+static bool stream_split(int64_t M, int64_t N, int64_t K, int32_t cus, int32_t *splits_out)
+{
+    const int64_t tiles = cdiv(M, 16) * cdiv(N, 16);
+    const int64_t c = cus > 0 ? cus : 1;
+    if (!(tiles * 4 <= c || K <= kStreamKeepK || (M <= kStreamFewM && K <= kStreamFewMK)))
+        return false;
+    int32_t s = 1;
+    while (s * 2 <= kStreamMaxSplits && tiles * s * 2 <= c && K / (s * 2) >= kStreamMinSplitK)
+        s *= 2;
+    *splits_out = s > 1 ? static_cast<int32_t>(cdiv(K, split_k_len(stream_config(), K, s))) : 1;
+    return true;
+}
+
 // Configuration and effective split count for the split-K entry points
 // (K > 0, direct-to-LDS arguments).  config_id >= 0 fixes the configuration;
 // splits > 0 fixes the requested count, and splits == 1 (or no split chosen)
@@ -2468,14 +2520,9 @@ static void choose_split_search(int64_t M, int64_t N, int64_t K, int32_t cus, in
                                 int32_t splits, int *id_out, int32_t *splits_out, int32_t layout)
 {
     const int plain = config_id >= 0 ? config_id : choose_config(M, N, K, cus, layout);
-    // The cost model has no rate for the register-streaming plan.  Measured
-    // against the split the model picks (one box, captured graphs, M in {1,
-    // 2, 8, 16}, N from 256 to 4096): at K = 2048 it ran 0.66-0.84 of the
-    // split's time on all 24 shapes, at K = 8192 it won 2 of 24 and at
-    // K = 32768 none (one wave per 16 rows of B is too few for a long K).
-    if (splits <= 0 && config_id < 0 && plain == stream_config() && K <= kStreamSplitMaxK) {
+    if (splits <= 0 && config_id < 0 && plain == stream_config() &&
+        stream_split(M, N, K, cus, splits_out)) {
         *id_out = plain;
-        *splits_out = 1;
         return;
     }
     double best = 0.0;

@@ -189,16 +189,30 @@ def test_plain_plan_streams_b_for_few_rows_of_a(g, shape, stream):
     assert g.gemm_f16_nn_plan(*shape, 256).config_id != p.config_id or not stream
 
 
-@pytest.mark.parametrize("shape, split", [((1, 4096, 2048), False), ((16, 2048, 2048), False),
-                                          ((1, 4096, 8192), True), ((8, 4096, 32768), True)])
-def test_split_planner_keeps_the_streaming_plan_for_short_k(g, shape, split):
-    # short K: the streaming plan unsplit; long K: a split over K
-    p = g.gemm_f16_nt_plan(*shape, 256)
-    assert g.gemm_f16_nt_config_info(p.config_id).stages == 0
-    sp, eff, ws = g.gemm_f16_nt_splitk_plan(*shape, 256, 0)
-    assert (eff > 1) == split
-    if not split:
-        assert sp.config_id == p.config_id and ws == 0
+# (M, N, K) -> the split planner's (streaming?, effective splits) on 256 CUs:
+# a grid of 16 x 16 tiles on at most a quarter of the CUs splits K into the
+# largest power of two of ranges (at most 16) that keeps tiles x splits <= 256
+# and every range >= 2048; more tiles keep the streaming plan unsplit only
+# for K <= 2048 or M <= 4 with K <= 8192, and otherwise take the model's split
+# of a tile configuration
+@pytest.mark.parametrize("shape, stream, splits", [
+    ((1, 4096, 2048), True, 1), ((16, 2048, 2048), True, 1), ((1, 4096, 4096), True, 1),
+    ((1, 4096, 8192), True, 1), ((1, 2048, 8192), True, 2), ((1, 1024, 16384), True, 4),
+    ((16, 512, 8192), True, 4), ((1, 256, 32768), True, 16), ((1, 256, 4096), True, 2),
+    ((16, 1000, 8200), True, 4), ((8, 4096, 32768), False, None), ((16, 2048, 16384), False, None),
+    ((5, 4000, 16384), False, None)])
+def test_split_planner_streams_few_rows_of_a(g, shape, stream, splits):
+    m, n, k = shape
+    p = g.gemm_f16_nt_plan(m, n, k, 256)
+    assert g.gemm_f16_nt_config_info(p.config_id).stages == 0   # the plain plan streams
+    sp, eff, ws = g.gemm_f16_nt_splitk_plan(m, n, k, 256, 0)
+    assert (sp.config_id == p.config_id) == stream
+    if stream:
+        assert eff == splits
+        assert ws == (0 if splits == 1 else splits * -(-(m * n) // 64) * 64 * 4)
+        assert splits == 1 or -(-k // splits) >= 2048
+    else:
+        assert eff > 1 and g.gemm_f16_nt_config_info(sp.config_id).stages > 0
 
 
 def _order(g, plan):

@@ -44,6 +44,9 @@ def run_splitk(g, a, b, splits=0, config=None, ws_offset=0, ws_bytes=None, poiso
     tb = torch.from_numpy(np.ascontiguousarray(b)).to(dev)
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     _, eff, need = g.gemm_f16_nt_splitk_plan(m, n, k, cus, splits)
+    if config is not None and splits > 1:
+        # a forced configuration may cut K into more ranges than the planner's
+        need = max(need, g.gemm_f16_splitk_workspace_bytes(m, n, splits))
     flat = torch.full((m * n + 8,), float("nan"), dtype=torch.float16, device=dev)
     out = flat[:m * n].view(m, n)
     ws = torch.full((need + ws_offset + 16,), poison, dtype=torch.uint8, device=dev)
@@ -76,12 +79,50 @@ def test_splitk_parity(g, oracle_mod, shape, splits, dist, seed):
     assert_within_tolerance(got, oracle_mod.gemm(a, b), f"splitk {shape} splits {splits}")
 
 
-@pytest.mark.parametrize("config", [None, 2, 4, 9, 11, 18, 21, 22, 23, 42])
+@pytest.mark.parametrize("config", [None, 2, 4, 9, 11, 18, 21, 22, 23, 42, 43])
 def test_splitk_integer_bit_exact(g, oracle_mod, config):
     a, b = workloads.make_inputs(200, 300, 6152, "int2", 1.0, seed=311)
     got, eff = run_splitk(g, a, b, 6, config=config)
     assert eff > 1
     assert_bit_exact(got, oracle_mod.gemm(a, b), f"int2 splitk config {config}")
+
+
+STREAM = 43   # B streamed through registers (no LDS ring)
+
+
+def _ranges(k, splits):
+    """Ranges of K a split count gives the streaming configuration (K steps of 32)."""
+    k_split = -(-(-(-k // splits)) // 32) * 32
+    return -(-k // k_split)
+
+
+@pytest.mark.parametrize("shape,splits,dist,seed", [
+    ((1, 256, 8192), 0, "normal", 321),       # planned: 4 ranges of 2048
+    ((16, 1000, 8200), 0, "uniform", 322),    # planned: 4 ranges, N tail, a shorter last range
+    ((1, 256, 32768), 0, "normal", 326),      # planned: 16 ranges
+    ((7, 33, 4136), 5, "normal", 323),        # ranges end mid-block; K tail of 8
+    ((17, 100, 4096), 8, "uniform", 324),     # two tile rows of A
+    ((3, 4099, 2056), 3, "normal", 325),
+])
+def test_splitk_streaming_parity(g, oracle_mod, shape, splits, dist, seed):
+    """The streaming configuration's split instance: each unit streams one
+    range of K for one 16 x 16 tile into an fp32 partial; as planned for few
+    rows of A and as forced, against the oracle."""
+    m, n, k = shape
+    plan, eff, _ = g.gemm_f16_nt_splitk_plan(m, n, k, 256, splits)
+    if splits == 0:
+        assert plan.config_id == STREAM and eff > 1, "the planner must split the streaming plan"
+    a, b = workloads.make_inputs(m, n, k, dist, 1.0 / np.sqrt(k), seed=seed)
+    got, _ = run_splitk(g, a, b, splits, config=None if splits == 0 else STREAM)
+    assert splits == 0 or _ranges(k, splits) > 1
+    assert_within_tolerance(got, oracle_mod.gemm(a, b), f"stream splitk {shape} splits {splits}")
+
+
+@pytest.mark.parametrize("splits", [2, 3, 16])
+def test_splitk_streaming_integer_bit_exact(g, oracle_mod, splits):
+    a, b = workloads.make_inputs(9, 777, 5000, "int2", 1.0, seed=327)
+    got, _ = run_splitk(g, a, b, splits, config=STREAM)
+    assert_bit_exact(got, oracle_mod.gemm(a, b), f"int2 stream splitk {splits}")
 
 
 def test_splitk_one_split_is_the_plain_path(g):
