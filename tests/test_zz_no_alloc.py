@@ -85,6 +85,23 @@ def test_two_calls_in_a_row_match_the_workspace_entry_point(g, oracle_mod):
     assert_within_tolerance(c_na, oracle_mod.gemm(a, b), "noalloc vs oracle, 200x136x9000")
 
 
+def test_streaming_split_plan(g, oracle_mod):
+    # a few rows of A over a short N: the planner splits the register-streaming
+    # plan over K (16 x 16 tiles, one fp32 partial per range); then a smaller
+    # call with ragged N and K over what the first left in the array
+    for (m, n, k, dist, seed) in [(1, 256, 32768, "int2", 75), (5, 200, 8200, "uniform", 76)]:
+        a, b = workloads.make_inputs(m, n, k, dist, 1.0, seed=seed)
+        plan, _, _ = g.gemm_f16_nt_splitk_plan(m, n, k, 256, 0)
+        assert g.gemm_f16_nt_config_info(plan.config_id).stages == 0
+        c_na, c_ws, eff, need = _both(g, a, b, 0)
+        assert eff > 1 and need > 0
+        assert_bit_exact(c_na, c_ws, f"noalloc vs workspace entry point, {m}x{n}x{k} streaming")
+        if dist == "int2":
+            assert_bit_exact(c_na, oracle_mod.gemm(a, b), f"noalloc vs oracle, {m}x{n}x{k}")
+        else:
+            assert_within_tolerance(c_na, oracle_mod.gemm(a, b), f"noalloc vs oracle, {m}x{n}x{k}")
+
+
 def test_repeated_calls_are_bit_identical(g):
     a, b = workloads.make_inputs(300, 260, 12000, "normal", 1.0 / np.sqrt(12000), seed=73)
     first, _, eff, _ = _both(g, a, b, 6)
