@@ -306,12 +306,15 @@ def test_page_mae_statistic(g):
 # ---------------------------------------------------------------------------
 # full-size workloads, in the launch configuration the benchmark times
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("name", list(workloads.WORKLOADS))
+@pytest.mark.parametrize("name", list(workloads.WORKLOADS) + list(workloads.FEW_ROWS_WORKLOADS))
 def test_full_size_workload(g, oracle_mod, name):
     """Each workload at full size, in the plan the benchmark times, against
     the whole oracle matrix (8192^3 takes the oracle about 20 s on 16 host
-    cores)."""
-    w = workloads.WORKLOADS[name]
+    cores).  The one-row workload runs the register-streaming plan."""
+    w = workloads.ALL_WORKLOADS[name]
+    if name in workloads.FEW_ROWS_WORKLOADS:
+        plan = g.gemm_f16_nt_plan(w.M, w.N, w.K, 256)
+        assert g.gemm_f16_nt_config_info(plan.config_id).stages == 0
     _say(f"  workload {name}: {w.M}x{w.N}x{w.K} {w.dist} seed={w.seed}")
     a, b = workloads.workload_inputs(name)
     got = run_gpu(g, a, b)

@@ -216,6 +216,15 @@ def test_full_size_underfilled_workload(g, oracle_mod, name):
     assert_within_tolerance(got[r, c], oracle_mod.gemm_sampled(a, b, r, c), name)
 
 
+@pytest.mark.parametrize("name", list(workloads.FEW_ROWS_WORKLOADS))
+def test_full_size_few_rows_workload_split(g, oracle_mod, name):
+    """The one-row workload through the split entry point as planned, against
+    the whole oracle row."""
+    a, b = workloads.workload_inputs(name)
+    got, _ = run_splitk(g, a, b, 0)
+    assert_within_tolerance(got, oracle_mod.gemm(a, b), name)
+
+
 # ---------------------------------------------------------------------------
 # the split over K for the other operand layouts
 # ---------------------------------------------------------------------------

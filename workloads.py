@@ -76,7 +76,18 @@ EXTRA_WORKLOADS = {
     )
 }
 
-ALL_WORKLOADS = {**WORKLOADS, **EXTRA_WORKLOADS}
+#: One row of A against a B of 4096 x 14336 (a matrix-vector product, 117 MB
+#: of B streamed once): the few-rows-of-A case, where the GEMM is bound by
+#: HBM and the plan streams B through registers.  Not a workload of the pages.
+FEW_ROWS_WORKLOADS = {
+    w.name: w
+    for w in (
+        Workload("gemv1x4096x14336", 1, 4096, 14336, "uniform", _inv_sqrt(14336), 107,
+                 "entries uniform in [-1, 1]/sqrt(K): one row of A, B streamed from HBM"),
+    )
+}
+
+ALL_WORKLOADS = {**WORKLOADS, **EXTRA_WORKLOADS, **FEW_ROWS_WORKLOADS}
 
 #: The workload the benchmark times.
 HEADLINE = "square8192"
