@@ -2295,13 +2295,19 @@ static int choose_config_search(int64_t M, int64_t N, int64_t K, int32_t num_cus
 
 // The register-streaming configuration (no LDS ring) and when the plain plan
 // takes it: NT, at most kStreamMaxM rows of A, and a plan whose tiles would
-// fill at most a quarter of the CUs.  Timed on one MI355X in captured graphs
-// against the plan it replaces (M = 1 / 4 / 8 / 16): 4096 x 4096 8.4 / 9.5 /
-// 10.1 / 11.5 us against 15.6-15.7; N = 4096, K = 14336 24.1 / 25.6 / 28.0 /
-// 32.4 us against 45.4-45.7.  With more tiles the tile kernels keep up (N =
-// 8192 at K = 8192: within -7..+1%; N = 14336 at K = 4096 they are faster),
-// and from M = 32 on streaming loses (B is read again for every 16 rows of A).
+// fill at most a quarter of the CUs; or at most kStreamHalfM rows, K up to
+// kStreamHalfK and tiles on at most half the CUs.  Timed on one MI355X in
+// captured graphs against the plan it replaces (M = 1 / 4 / 8 / 16): 4096 x
+// 4096 7.6 / 8.6 / 8.9 / 10.6 us against 15.6-15.8; N = 4096, K = 14336
+// 19.2 / - / 22.9 / - us against 45.4; N = 8192 (M = 1 / 4 / 8), K = 2048
+// 7.1 / 7.8 / 8.4 against 9.7-9.8 and K = 4096 13.4 / 14.2 / 15.4 against
+// 15.8-16.0.  With more tiles, more rows or a longer K the tile kernels keep
+// up (N = 8192, K = 16384, M = 4: 56.9 against 51.8; N = 14336 at K = 4096
+// they are faster), and from M = 32 on streaming loses (B is read again for
+// every 16 rows of A).
 constexpr int64_t kStreamMaxM = 16;
+constexpr int64_t kStreamHalfM = 8;
+constexpr int64_t kStreamHalfK = 8192;
 
 static int stream_config()
 {
@@ -2317,8 +2323,10 @@ static int choose_config_planned(int64_t M, int64_t N, int64_t K, int32_t num_cu
 {
     const int id = choose_config_search(M, N, K, num_cus, layout);
     const int st = stream_config();
-    if (layout == 0 && st >= 0 && id >= 0 && M <= kStreamMaxM && K > 0 &&
-        cdiv(M, kKernels[id].block_m) * cdiv(N, kKernels[id].block_n) * 4 <= num_cus)
+    if (layout != 0 || st < 0 || id < 0 || K <= 0) return id;
+    const int64_t tiles = cdiv(M, kKernels[id].block_m) * cdiv(N, kKernels[id].block_n);
+    if ((M <= kStreamMaxM && tiles * 4 <= num_cus) ||
+        (M <= kStreamHalfM && K <= kStreamHalfK && tiles * 2 <= num_cus))
         return st;
     return id;
 }
@@ -2484,9 +2492,9 @@ static bool split_candidate(int id)
 // S ranges of K per tile, S the largest power of two with tiles S <= CUs,
 // S <= kStreamMaxSplits and K / S >= kStreamMinSplitK.  Kept where it beat
 // the model's split of a tile configuration: grids of at most a quarter of
-// the CUs, or K <= kStreamKeepK, or at most kStreamFewM rows of A and
-// K <= kStreamFewMK; elsewhere (more tiles and a long K) false, and the
-// model's split stands.  Timed on one MI355X in captured graphs over M in
+// the CUs, or K <= kStreamKeepK, or at most kStreamFewM rows of A,
+// K <= kStreamFewMK and one tile per CU at most; elsewhere (more tiles and a
+// long K) false, and the model's split stands.  Timed on one MI355X in captured graphs over M in
 // {1, 4, 8, 16}, N from 256 to 4096 and K from 2048 to 32768 (80 shapes):
 // 0.85 of the model's split's time (geometric mean; 1 x 256 x 32768 9.6
 // against 20.8 us, 1 x 4096 x 4096 7.5 against 9.8), none more than 3%
@@ -2501,7 +2509,7 @@ static bool stream_split(int64_t M, int64_t N, int64_t K, int32_t cus, int32_t *
 {
     const int64_t tiles = cdiv(M, 16) * cdiv(N, 16);
     const int64_t c = cus > 0 ? cus : 1;
-    if (!(tiles * 4 <= c || K <= kStreamKeepK || (M <= kStreamFewM && K <= kStreamFewMK)))
+    if (!(tiles * 4 <= c || K <= kStreamKeepK || (M <= kStreamFewM && K <= kStreamFewMK && tiles <= c)))
         return false;
     int32_t s = 1;
     while (s * 2 <= kStreamMaxSplits && tiles * s * 2 <= c && K / (s * 2) >= kStreamMinSplitK)
