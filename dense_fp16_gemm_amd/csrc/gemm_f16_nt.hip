@@ -2303,11 +2303,18 @@ static int choose_config_search(int64_t M, int64_t N, int64_t K, int32_t num_cus
 // 7.1 / 7.8 / 8.4 against 9.7-9.8 and K = 4096 13.4 / 14.2 / 15.4 against
 // 15.8-16.0.  With more tiles, more rows or a longer K the tile kernels keep
 // up (N = 8192, K = 16384, M = 4: 56.9 against 51.8; N = 14336 at K = 4096
-// they are faster), and from M = 32 on streaming loses (B is read again for
-// every 16 rows of A).
+// they are faster).  Up to kStreamRoundM rows it still wins where its 16 x 16
+// tiles fit in one round of the CUs and the tile plan fills at most a
+// quarter: B is then read once per 16 rows of A, but the reads after the
+// first hit the L2s (the tile rows run together), and the grid has more
+// waves than the tile plan's (M = 17 / 32 / 64 at N = 1024, K = 8192: 16.6 /
+// 16.5 / 16.5 us against 27.4-27.5; M = 32 at N = 2048, K = 4096: 10.2
+// against 15.8).  With more tiles B's reads are too many (M = 48, N = 2048,
+// K = 4096: 17.7 against 15.8).
 constexpr int64_t kStreamMaxM = 16;
 constexpr int64_t kStreamHalfM = 8;
 constexpr int64_t kStreamHalfK = 8192;
+constexpr int64_t kStreamRoundM = 64;
 
 static int stream_config()
 {
@@ -2326,7 +2333,9 @@ static int choose_config_planned(int64_t M, int64_t N, int64_t K, int32_t num_cu
     if (layout != 0 || st < 0 || id < 0 || K <= 0) return id;
     const int64_t tiles = cdiv(M, kKernels[id].block_m) * cdiv(N, kKernels[id].block_n);
     if ((M <= kStreamMaxM && tiles * 4 <= num_cus) ||
-        (M <= kStreamHalfM && K <= kStreamHalfK && tiles * 2 <= num_cus))
+        (M <= kStreamHalfM && K <= kStreamHalfK && tiles * 2 <= num_cus) ||
+        (M <= kStreamRoundM && tiles * 4 <= num_cus &&
+         cdiv(M, kKernels[st].block_m) * cdiv(N, kKernels[st].block_n) <= num_cus))
         return st;
     return id;
 }
@@ -2492,7 +2501,7 @@ static bool split_candidate(int id)
 // S ranges of K per tile, S the largest power of two with tiles S <= CUs,
 // S <= kStreamMaxSplits and K / S >= kStreamMinSplitK.  Kept where it beat
 // the model's split of a tile configuration: grids of at most a quarter of
-// the CUs, or K <= kStreamKeepK, or at most kStreamFewM rows of A,
+// the CUs (at most kStreamMaxM rows of A), or K <= kStreamKeepK, or at most kStreamFewM rows of A,
 // K <= kStreamFewMK and one tile per CU at most; elsewhere (more tiles and a
 // long K) false, and the model's split stands.  Timed on one MI355X in captured graphs over M in
 // {1, 4, 8, 16}, N from 256 to 4096 and K from 2048 to 32768 (80 shapes):
@@ -2509,7 +2518,8 @@ static bool stream_split(int64_t M, int64_t N, int64_t K, int32_t cus, int32_t *
 {
     const int64_t tiles = cdiv(M, 16) * cdiv(N, 16);
     const int64_t c = cus > 0 ? cus : 1;
-    if (!(tiles * 4 <= c || K <= kStreamKeepK || (M <= kStreamFewM && K <= kStreamFewMK && tiles <= c)))
+    if (!((M <= kStreamMaxM && tiles * 4 <= c) || K <= kStreamKeepK ||
+          (M <= kStreamFewM && K <= kStreamFewMK && tiles <= c)))
         return false;
     int32_t s = 1;
     while (s * 2 <= kStreamMaxSplits && tiles * s * 2 <= c && K / (s * 2) >= kStreamMinSplitK)
