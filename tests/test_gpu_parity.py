@@ -168,6 +168,18 @@ def test_streaming_configuration_small_m(g, oracle_mod, m, c_offset):
     assert_bit_exact(got, run_gpu(g, a, b, config=11), f"stream m={m} vs config 11")
 
 
+@pytest.mark.parametrize("shape", [(64, 1024, 2056), (40, 640, 3080), (8, 6000, 1032), (3, 8192, 1000)])
+def test_planned_streaming_shapes(g, oracle_mod, shape):
+    """Shapes the plain planner streams beyond M <= 16 with a quarter of the
+    CUs (up to 64 rows in one round of 16 x 16 tiles, or up to 8 rows with
+    half the CUs), as planned, on integer inputs: bit-exact with the oracle."""
+    m, n, k = shape
+    plan = g.gemm_f16_nt_plan(m, n, k, 256)
+    assert g.gemm_f16_nt_config_info(plan.config_id).stages == 0
+    a, b = workloads.make_inputs(m, n, k, "int2", 1.0, seed=510 + m)
+    assert_bit_exact(run_gpu(g, a, b), oracle_mod.gemm(a, b), f"planned stream {shape}")
+
+
 def test_m_or_n_zero_is_a_no_op(g):
     import torch
 
