@@ -2331,10 +2331,13 @@ static int choose_config_planned(int64_t M, int64_t N, int64_t K, int32_t num_cu
     const int id = choose_config_search(M, N, K, num_cus, layout);
     const int st = stream_config();
     if (layout != 0 || st < 0 || id < 0 || K <= 0) return id;
+    // the kernel's loads and tiles treat A and B alike, so a few columns of
+    // B (A streamed) count as a few rows of A
+    const int64_t few = M < N ? M : N;
     const int64_t tiles = cdiv(M, kKernels[id].block_m) * cdiv(N, kKernels[id].block_n);
-    if ((M <= kStreamMaxM && tiles * 4 <= num_cus) ||
-        (M <= kStreamHalfM && K <= kStreamHalfK && tiles * 2 <= num_cus) ||
-        (M <= kStreamRoundM && tiles * 4 <= num_cus &&
+    if ((few <= kStreamMaxM && tiles * 4 <= num_cus) ||
+        (few <= kStreamHalfM && K <= kStreamHalfK && tiles * 2 <= num_cus) ||
+        (few <= kStreamRoundM && tiles * 4 <= num_cus &&
          cdiv(M, kKernels[st].block_m) * cdiv(N, kKernels[st].block_n) <= num_cus))
         return st;
     return id;
@@ -2518,8 +2521,9 @@ static bool stream_split(int64_t M, int64_t N, int64_t K, int32_t cus, int32_t *
 {
     const int64_t tiles = cdiv(M, 16) * cdiv(N, 16);
     const int64_t c = cus > 0 ? cus : 1;
-    if (!((M <= kStreamMaxM && tiles * 4 <= c) || K <= kStreamKeepK ||
-          (M <= kStreamFewM && K <= kStreamFewMK && tiles <= c)))
+    const int64_t few = M < N ? M : N;   // rows of A or columns of B
+    if (!((few <= kStreamMaxM && tiles * 4 <= c) || K <= kStreamKeepK ||
+          (few <= kStreamFewM && K <= kStreamFewMK && tiles <= c)))
         return false;
     int32_t s = 1;
     while (s * 2 <= kStreamMaxSplits && tiles * s * 2 <= c && K / (s * 2) >= kStreamMinSplitK)

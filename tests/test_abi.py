@@ -182,6 +182,9 @@ def test_plain_plan_keeps_the_rule_within_the_model_margin(g, shape, cid):
     # up to 64 rows where the 16 x 16 tiles fit in one round of the CUs
     ((32, 2048, 4096), True), ((64, 1024, 8192), True), ((17, 1000, 16384), True),
     ((48, 2048, 4096), False), ((17, 4096, 4096), False), ((65, 1024, 4096), False),
+    # the same rules with the roles swapped: a few columns of B, A streamed
+    ((4096, 1, 4096), True), ((4096, 16, 14336), True), ((8192, 4, 4096), True),
+    ((1024, 64, 8192), True), ((16384, 1, 16384), False), ((4096, 32, 4096), False),
 ])
 def test_plain_plan_streams_b_for_few_rows_of_a(g, shape, stream):
     # at most 16 rows of A and tiles that would fill at most a quarter of the
@@ -208,7 +211,8 @@ def test_plain_plan_streams_b_for_few_rows_of_a(g, shape, stream):
     ((16, 512, 8192), True, 4), ((1, 256, 32768), True, 16), ((1, 256, 4096), True, 2),
     ((16, 1000, 8200), True, 4), ((8, 4096, 32768), False, None), ((16, 2048, 16384), False, None),
     ((5, 4000, 16384), False, None), ((1, 8192, 2048), True, 1), ((1, 8192, 8192), False, None),
-    ((32, 1024, 2048), True, 1), ((32, 1024, 4096), False, None), ((64, 512, 16384), False, None)])
+    ((32, 1024, 2048), True, 1), ((32, 1024, 4096), False, None), ((64, 512, 16384), False, None),
+    ((256, 1, 32768), True, 16), ((2048, 4, 4096), True, 2), ((4096, 16, 16384), False, None)])
 def test_split_planner_streams_few_rows_of_a(g, shape, stream, splits):
     m, n, k = shape
     p = g.gemm_f16_nt_plan(m, n, k, 256)

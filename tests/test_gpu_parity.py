@@ -168,11 +168,13 @@ def test_streaming_configuration_small_m(g, oracle_mod, m, c_offset):
     assert_bit_exact(got, run_gpu(g, a, b, config=11), f"stream m={m} vs config 11")
 
 
-@pytest.mark.parametrize("shape", [(64, 1024, 2056), (40, 640, 3080), (8, 6000, 1032), (3, 8192, 1000)])
+@pytest.mark.parametrize("shape", [(64, 1024, 2056), (40, 640, 3080), (8, 6000, 1032), (3, 8192, 1000),
+                                   (4099, 1, 4104), (1000, 13, 2056), (1000, 40, 1032)])
 def test_planned_streaming_shapes(g, oracle_mod, shape):
     """Shapes the plain planner streams beyond M <= 16 with a quarter of the
     CUs (up to 64 rows in one round of 16 x 16 tiles, or up to 8 rows with
-    half the CUs), as planned, on integer inputs: bit-exact with the oracle."""
+    half the CUs), and with the roles swapped (a few columns of B, A
+    streamed), as planned, on integer inputs: bit-exact with the oracle."""
     m, n, k = shape
     plan = g.gemm_f16_nt_plan(m, n, k, 256)
     assert g.gemm_f16_nt_config_info(plan.config_id).stages == 0
