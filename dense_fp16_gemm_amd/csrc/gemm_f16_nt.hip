@@ -2499,34 +2499,42 @@ static bool split_candidate(int id)
 }
 
 // The split planner's choice for a register-streaming plan, which its cost
-// model has no rate for.  One CU keeps only so many loads in flight, so
-// where the 16 x 16 tiles occupy few CUs only a split over K adds bandwidth:
-// S ranges of K per tile, S the largest power of two with tiles S <= CUs,
-// S <= kStreamMaxSplits and K / S >= kStreamMinSplitK.  Kept where it beat
-// the model's split of a tile configuration: grids of at most a quarter of
-// the CUs (at most kStreamMaxM rows of A), or K <= kStreamKeepK, or at most kStreamFewM rows of A,
-// K <= kStreamFewMK and one tile per CU at most; elsewhere (more tiles and a
-// long K) false, and the model's split stands.  Timed on one MI355X in captured graphs over M in
-// {1, 4, 8, 16}, N from 256 to 4096 and K from 2048 to 32768 (80 shapes):
-// 0.85 of the model's split's time (geometric mean; 1 x 256 x 32768 9.6
-// against 20.8 us, 1 x 4096 x 4096 7.5 against 9.8), none more than 3%
-// slower.
+// model has no rate for ("few" is the smaller of M and N: the kernel treats
+// A and B alike).  One CU keeps only so many loads in flight, so where the
+// 16 x 16 tiles occupy few CUs only a split over K adds bandwidth: S ranges
+// of K per tile, S the largest power of two with tiles S <= CUs, S <=
+// kStreamMaxSplits and K / S >= kStreamMinSplitK (only for few <=
+// kStreamMaxM).  The plan is kept where it beat the model's split of a tile
+// configuration: grids of at most a quarter of the CUs with few <=
+// kStreamMaxM; K <= kStreamKeepK; few <= kStreamFewM with K <= kStreamFewMK
+// and at most one tile per CU; or K <= kStreamShortK with few <=
+// kStreamHalfM or at most a quarter of the CUs.  Elsewhere (more tiles and a
+// long K) the model's split stands.  Timed on one MI355X in captured graphs
+// over M in {1, 4, 8, 16}, N from 256 to 4096 and K from 2048 to 32768 (80
+// shapes): 0.85 of the model's split's time (geometric mean; 1 x 256 x 32768
+// 9.6 against 20.8 us, 1 x 4096 x 4096 7.5 against 9.8), none more than 3%
+// slower; the short-K clause, over 70 random shapes with few <= 64 and K
+// from 2056 to 4096, changed 20 plans, to 0.72 of the time (3467 x 5 x 3856
+// 6.5 against 13.2 us), none slower.
 constexpr int32_t kStreamMaxSplits = 16;
 constexpr int64_t kStreamMinSplitK = 2048;
 constexpr int64_t kStreamKeepK = 2048;
 constexpr int64_t kStreamFewM = 4;
 constexpr int64_t kStreamFewMK = 8192;
+constexpr int64_t kStreamShortK = 4096;
 
 static bool stream_split(int64_t M, int64_t N, int64_t K, int32_t cus, int32_t *splits_out)
 {
     const int64_t tiles = cdiv(M, 16) * cdiv(N, 16);
     const int64_t c = cus > 0 ? cus : 1;
     const int64_t few = M < N ? M : N;   // rows of A or columns of B
+    const bool short_k = K <= kStreamShortK && (few <= kStreamHalfM || tiles * 4 <= c);
     if (!((few <= kStreamMaxM && tiles * 4 <= c) || K <= kStreamKeepK ||
-          (few <= kStreamFewM && K <= kStreamFewMK && tiles <= c)))
+          (few <= kStreamFewM && K <= kStreamFewMK && tiles <= c) || short_k))
         return false;
     int32_t s = 1;
-    while (s * 2 <= kStreamMaxSplits && tiles * s * 2 <= c && K / (s * 2) >= kStreamMinSplitK)
+    while (few <= kStreamMaxM && s * 2 <= kStreamMaxSplits && tiles * s * 2 <= c &&
+           K / (s * 2) >= kStreamMinSplitK)
         s *= 2;
     *splits_out = s > 1 ? static_cast<int32_t>(cdiv(K, split_k_len(stream_config(), K, s))) : 1;
     return true;

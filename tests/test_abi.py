@@ -212,7 +212,10 @@ def test_plain_plan_streams_b_for_few_rows_of_a(g, shape, stream):
     ((16, 1000, 8200), True, 4), ((8, 4096, 32768), False, None), ((16, 2048, 16384), False, None),
     ((5, 4000, 16384), False, None), ((1, 8192, 2048), True, 1), ((1, 8192, 8192), False, None),
     ((32, 1024, 2048), True, 1), ((32, 1024, 4096), False, None), ((64, 512, 16384), False, None),
-    ((256, 1, 32768), True, 16), ((2048, 4, 4096), True, 2), ((4096, 16, 16384), False, None)])
+    ((256, 1, 32768), True, 16), ((2048, 4, 4096), True, 2), ((4096, 16, 16384), False, None),
+    # K <= 4096 with few <= 8, or tiles on a quarter of the CUs: unsplit
+    ((4902, 1, 3560), True, 1), ((37, 59, 2824), True, 1), ((7, 4411, 4056), True, 1),
+    ((16, 2048, 4096), False, None)])
 def test_split_planner_streams_few_rows_of_a(g, shape, stream, splits):
     m, n, k = shape
     p = g.gemm_f16_nt_plan(m, n, k, 256)
