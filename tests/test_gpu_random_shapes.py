@@ -62,6 +62,44 @@ def test_random_shapes_bit_exact(g, oracle_mod, lay, split):
                          f"{lay} split={split} {m}x{n}x{k}")
 
 
+def _few_shapes(seed, count):
+    """NT shapes with a few rows of A or a few columns of B (1..64), the other
+    side up to a few thousand, K a multiple of 8 and sometimes long: the
+    register-streaming plans and their splits over K."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(count):
+        few, many = int(rng.integers(1, 65)), int(rng.integers(16, 4000))
+        k = int(rng.integers(1, 600)) * 8 * (4 if i % 3 == 0 else 1)
+        many = max(16, min(many, int(1.5e8 // (few * k))))   # keeps the oracle quick
+        out.append((few, many, k) if i % 2 == 0 else (many, few, k))
+    return out
+
+
+@pytest.mark.parametrize("split", [False, True])
+def test_random_few_rows_or_columns_bit_exact(g, oracle_mod, split):
+    import torch
+
+    streamed = 0
+    for idx, (m, n, k) in enumerate(_few_shapes(450 + int(split), 16)):
+        plan = (g.gemm_f16_nt_splitk_plan(m, n, k, g.gemm_f16_device_cus(), 0)[0] if split
+                else g.gemm_f16_nt_plan(m, n, k, g.gemm_f16_device_cus()))
+        streamed += g.gemm_f16_nt_config_info(plan.config_id).stages == 0
+        a, b = workloads.make_inputs(m, n, k, "int2", 1.0, seed=460 + idx)
+        print(f"  gpu few rows/columns split={split} {m}x{n}x{k} config {plan.config_id}",
+              file=sys.stderr, flush=True)
+        ta, tb = torch.from_numpy(a).cuda(), torch.from_numpy(b).cuda()
+        out = torch.full((m, n), float("nan"), dtype=torch.float16, device="cuda")
+        if split:
+            g.gemm_splitk(ta, tb, "nt", out=out)
+        else:
+            g.gemm(ta, tb, "nt", out=out)
+        torch.cuda.synchronize()
+        assert_bit_exact(out.cpu().numpy(), oracle_mod.gemm(a, b),
+                         f"few rows/columns split={split} {m}x{n}x{k}")
+    assert streamed >= 4, "the sample must exercise the streaming plans"
+
+
 @pytest.mark.parametrize("lay, shape, tile", [
     ("nt", (2000, 3000, 776), (256, 128)),
     ("nn", (2000, 3000, 776), (256, 128)),
