@@ -2506,8 +2506,9 @@ static bool split_candidate(int id)
 // kStreamMaxSplits and K / S >= kStreamMinSplitK (only for few <=
 // kStreamMaxM).  The plan is kept where it beat the model's split of a tile
 // configuration: grids of at most a quarter of the CUs with few <=
-// kStreamMaxM; K <= kStreamKeepK; few <= kStreamFewM with K <= kStreamFewMK
-// and at most one tile per CU; or K <= kStreamShortK with few <=
+// kStreamMaxM; K <= kStreamKeepK; few <= kStreamFewM with K <=
+// kStreamFewAnyK, or K <= kStreamFewMK and at most one tile per CU; or K <=
+// kStreamShortK with few <=
 // kStreamHalfM or at most a quarter of the CUs.  Elsewhere (more tiles and a
 // long K) the model's split stands.  Timed on one MI355X in captured graphs
 // over M in {1, 4, 8, 16}, N from 256 to 4096 and K from 2048 to 32768 (80
@@ -2515,12 +2516,16 @@ static bool split_candidate(int id)
 // 9.6 against 20.8 us, 1 x 4096 x 4096 7.5 against 9.8), none more than 3%
 // slower; the short-K clause, over 70 random shapes with few <= 64 and K
 // from 2056 to 4096, changed 20 plans, to 0.72 of the time (3467 x 5 x 3856
-// 6.5 against 13.2 us), none slower.
+// 6.5 against 13.2 us), none slower; the few <= kStreamFewM clause up to K =
+// kStreamFewAnyK, over 36 shapes with 1, 3 or 4 rows or columns, the other
+// side 4500-10000 and K = 4200 or 5000, to 0.72 (7500 x 1 x 4200 12.1
+// against 22.4 us), none slower (at K = 6144 it lost up to 1.26 times).
 constexpr int32_t kStreamMaxSplits = 16;
 constexpr int64_t kStreamMinSplitK = 2048;
 constexpr int64_t kStreamKeepK = 2048;
 constexpr int64_t kStreamFewM = 4;
 constexpr int64_t kStreamFewMK = 8192;
+constexpr int64_t kStreamFewAnyK = 5120;
 constexpr int64_t kStreamShortK = 4096;
 
 static bool stream_split(int64_t M, int64_t N, int64_t K, int32_t cus, int32_t *splits_out)
@@ -2529,8 +2534,9 @@ static bool stream_split(int64_t M, int64_t N, int64_t K, int32_t cus, int32_t *
     const int64_t c = cus > 0 ? cus : 1;
     const int64_t few = M < N ? M : N;   // rows of A or columns of B
     const bool short_k = K <= kStreamShortK && (few <= kStreamHalfM || tiles * 4 <= c);
-    if (!((few <= kStreamMaxM && tiles * 4 <= c) || K <= kStreamKeepK ||
-          (few <= kStreamFewM && K <= kStreamFewMK && tiles <= c) || short_k))
+    const bool few_k =
+        few <= kStreamFewM && (K <= kStreamFewAnyK || (K <= kStreamFewMK && tiles <= c));
+    if (!((few <= kStreamMaxM && tiles * 4 <= c) || K <= kStreamKeepK || few_k || short_k))
         return false;
     int32_t s = 1;
     while (few <= kStreamMaxM && s * 2 <= kStreamMaxSplits && tiles * s * 2 <= c &&

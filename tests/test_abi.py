@@ -215,7 +215,9 @@ def test_plain_plan_streams_b_for_few_rows_of_a(g, shape, stream):
     ((256, 1, 32768), True, 16), ((2048, 4, 4096), True, 2), ((4096, 16, 16384), False, None),
     # K <= 4096 with few <= 8, or tiles on a quarter of the CUs: unsplit
     ((4902, 1, 3560), True, 1), ((37, 59, 2824), True, 1), ((7, 4411, 4056), True, 1),
-    ((16, 2048, 4096), False, None)])
+    ((16, 2048, 4096), False, None),
+    # up to 4 rows or columns and K <= 5120: unsplit, whatever the tile count
+    ((3, 7246, 5000), True, 1), ((7500, 1, 4200), True, 1), ((4, 4500, 6144), False, None)])
 def test_split_planner_streams_few_rows_of_a(g, shape, stream, splits):
     m, n, k = shape
     p = g.gemm_f16_nt_plan(m, n, k, 256)
