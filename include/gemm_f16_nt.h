@@ -228,7 +228,10 @@ int gemm_f16_tt_plan(int64_t M, int64_t N, int64_t K, int32_t num_cus,
  * count (*splits_out, at most `splits`: ranges are whole K slices) and the
  * workspace size in bytes (*workspace_bytes, 0 when there is no split).
  * splits <= 0 lets the library choose (it weighs the rounds of MFMA work
- * against the partial-sum traffic); splits = 1 is gemm_f16_nt's plan.
+ * against the partial-sum traffic; where gemm_f16_nt's plan streams B, or A,
+ * through registers for a few rows of A or columns of B, it splits that plan
+ * by a rule of its own or keeps it unsplit); splits = 1 is gemm_f16_nt's
+ * plan.
  * GEMM_F16_INVALID_ARG for NULL outputs, negative sizes, num_cus <= 0 or
  * splits > 64.
  *
